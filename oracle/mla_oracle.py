@@ -1,0 +1,226 @@
+"""fp64 reference for absorbed MLA decode with round-robin KV sharding.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Slow and plain on
+purpose: exact two-pass softmax over an explicitly enumerated set of global
+positions, read from the *contiguous global* KV of each request (no block
+tables, no online softmax, no splitting).
+
+Sources (three vLLM PR digest pages):
+  * PR #52188 page ("support Kimi-K3 DSpark speculative decoding with DCP"),
+    key source snippets: the per-query causal prefix of a multi-token query
+    (row j of a q_len block sees the global prefix tot - (q_len - 1 - j),
+    clamped at 0); the round-robin rank-local length; the non-causal draft
+    block where every row sees the same context; and the `cp_local_slot`
+    kernel (ownership of a position by rank, rank-local offset, pad slot).
+  * PR #54012 page ("MLA decode with DCP uses FlashInfer's native CP mask"),
+    implementation breakdown and key source snippets: the kernel takes the
+    rank-local seq_lens plus the *global* causal lengths, cp_world and cp_rank
+    and masks per row itself; interleave must be 1; the returned LSE is a
+    natural log; partial results of all ranks are merged across ranks.
+  * PR #48180 page ("TokenSpeed MLA with DCP and Eagle"), implementation
+    breakdown: the same kernel contract with a base-2 LSE, and review
+    highlights: an end-aligned local causal mask is wrong under DCP when
+    q_len > 1.
+
+Readings where the pages are silent (each is also listed in the design notes):
+  * LSE is the log-normaliser of the softmax over *scaled* scores; base 2 is
+    the base-e value divided by ln 2.
+  * The query at row j of a causal block is the token at global position
+    tot - q_len + j and sees every global position p <= itself.
+  * Rank r holds local rows t < seq_lens[b] that are the global positions
+    p = t*W + r (interleave 1).  A row sees the positions it holds that its
+    causal bound admits; a non-causal row sees every position it holds.
+  * A row with nothing visible yields out = 0 and lse = -inf.
+  * The merge weights each partial by base**(lse_r - max lse); partials with
+    lse = -inf get weight 0; if every partial is -inf the result is (0, -inf).
+  * The pad slot id is -1; a position whose index in its request is at or
+    past num_valid[b] (the rejected suffix), a negative position and a
+    virtual block past the table width all map to the pad slot.
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+D_QK = 576   # absorbed query / latent KV width: 512 latent + 64 rope
+D_V = 512    # value width: the latent part of the KV row
+PAD_SLOT_ID = -1
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) exactly to float64."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def held_positions(seq_len: int, W: int, r: int) -> np.ndarray:
+    """Global positions of the local rows a rank holds: t*W + r for t < seq_len.
+
+    Round-robin placement with interleave 1 (PR #52188 page, key source
+    snippets, cp_local_slot: segment index modulo the CP size picks the rank).
+    """
+    return np.arange(int(seq_len), dtype=np.int64) * W + r
+
+
+def local_count(g: int, W: int, r: int) -> int:
+    """How many of the global positions 0..g-1 rank r holds, by enumeration."""
+    if g <= 0:
+        return 0
+    p = np.arange(int(g), dtype=np.int64)
+    return int(np.count_nonzero(p % W == r))
+
+
+def visible_positions(seq_len: int, tot: Optional[int], q_len: int, j: int,
+                      W: int, r: int, causal: bool) -> np.ndarray:
+    """Global positions row j of a request attends to on rank r.
+
+    Causal: the row is the token at global position tot - q_len + j, so it
+    sees the global prefix of length tot - (q_len - 1 - j) (PR #52188 page,
+    key source snippets, flattened decode metadata: offsets q_len-1 .. 0
+    subtracted from the global length, clamped at 0).  Of those, the rank
+    sees the ones it holds.  Non-causal: every held position (the draft block
+    repeats the same context length for each row).
+    """
+    held = held_positions(seq_len, W, r)
+    if not causal:
+        return held
+    g = max(int(tot) - (q_len - 1 - j), 0)
+    return held[held < g]
+
+
+def attend(q_rows: np.ndarray, kv_rows: np.ndarray, scale: float, base: str = "e"
+           ) -> Tuple[np.ndarray, np.ndarray]:
+    """Exact softmax attention of query rows [n, 576] over KV rows [m, 576], in float64.
+
+    Scores use all 576 columns (latent and rope parts); values are the first
+    512 columns of the same rows (absorbed MLA: the latent is also the value).
+    Returns out [n, 512] and lse [n] in the requested base.
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    n = q_rows.shape[0]
+    if kv_rows.shape[0] == 0:
+        return np.zeros((n, D_V)), np.full((n,), -np.inf)
+    kv_rows = np.asarray(kv_rows, dtype=np.float64)
+    s = scale * (q_rows @ kv_rows.T)                  # [n, m]
+    m = s.max(axis=1, keepdims=True)                  # pass 1: row max
+    e = np.exp(s - m)
+    z = e.sum(axis=1, keepdims=True)                  # pass 2: normaliser
+    out = (e @ kv_rows[:, :D_V]) / z
+    lse = (m + np.log(z))[:, 0]
+    if base == "2":
+        lse = lse / math.log(2.0)
+    return out, lse
+
+
+def mla_decode(q_bits: np.ndarray, kv_rows: Callable[[int, np.ndarray], np.ndarray],
+               seq_lens: Sequence[int], tot: Optional[Sequence[int]], W: int, r: int,
+               causal: bool, scale: float, base: str = "e",
+               rows: Optional[Sequence[Tuple[int, int, int]]] = None):
+    """Oracle for one rank's decode call.
+
+    q_bits:   [B, Q, H, 576] bf16 bits.
+    kv_rows:  kv_rows(b, positions) -> bf16 bits [len(positions), 576] from the
+              contiguous global KV of request b.
+    seq_lens: rank-local lengths; tot: global causal lengths (None: equal to
+              seq_lens, the single-rank case).
+    rows:     optional list of (b, j, h) to compute; default all.
+    Returns (out [B*Q, H, 512], lse [B*Q, H]) as float64; rows not asked for
+    are NaN.
+    """
+    B, Q, H, D = q_bits.shape
+    assert D == D_QK
+    out = np.full((B * Q, H, D_V), np.nan)
+    lse = np.full((B * Q, H), np.nan)
+    want = {}
+    if rows is None:
+        for b in range(B):
+            for j in range(Q):
+                want[(b, j)] = list(range(H))
+    else:
+        for (b, j, h) in rows:
+            want.setdefault((b, j), []).append(h)
+    cache = {}
+    for (b, j), heads in sorted(want.items()):
+        t = None if tot is None else int(tot[b])
+        if t is None:
+            t = int(seq_lens[b])
+        pos = visible_positions(int(seq_lens[b]), t, Q, j, W, r, causal)
+        key = (b, pos.size, int(pos[-1]) if pos.size else -1)
+        if key not in cache:
+            cache.clear()
+            cache[key] = bf16_bits_to_f64(kv_rows(b, pos))
+        kv = cache[key]
+        qr = bf16_bits_to_f64(q_bits[b, j, heads, :])
+        o, l = attend(qr, kv, scale, base)
+        out[b * Q + j, heads] = o
+        lse[b * Q + j, heads] = l
+    return out, lse
+
+
+def merge_lse(outs: List[np.ndarray], lses: List[np.ndarray], base: str = "e"
+              ) -> Tuple[np.ndarray, np.ndarray]:
+    """Combine partial (out, lse) pairs of disjoint key sets into the full result.
+
+    The pages name the cross-rank merge of partial outputs by their LSE
+    (PR #54012 page, implementation breakdown: the LSE base must agree across
+    ranks before merging) without printing it; this is the standard
+    log-sum-exp combine: weights base**(lse_r - M) with M = max_r lse_r.
+    """
+    beta = math.e if base == "e" else 2.0
+    o = np.stack([np.asarray(x, dtype=np.float64) for x in outs])     # [n, rows, H, 512]
+    lam = np.stack([np.asarray(x, dtype=np.float64) for x in lses])   # [n, rows, H]
+    M = lam.max(axis=0)
+    empty = ~np.isfinite(M)
+    Msafe = np.where(empty, 0.0, M)
+    w = np.where(np.isfinite(lam), np.power(beta, lam - Msafe[None]), 0.0)
+    wsum = w.sum(axis=0)
+    num = (w[..., None] * o).sum(axis=0)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        out = np.where(empty[..., None], 0.0, num / np.where(empty, 1.0, wsum)[..., None])
+        lse = np.where(empty, -np.inf, Msafe + np.log(np.where(empty, 1.0, wsum)) / math.log(beta))
+    return out, lse
+
+
+def cp_local_slot(positions: np.ndarray, block_table: np.ndarray, block_size: int,
+                  W: int, r: int, interleave: int = 1,
+                  num_valid: Optional[np.ndarray] = None) -> np.ndarray:
+    """Rank-local KV slot of each position, or PAD_SLOT_ID, with plain Python ints.
+
+    PR #52188 page, key source snippets (cp_local_slot): a block-table entry
+    covers block_size * W consecutive global positions (the virtual block,
+    index pos // (block_size * W), as the DFlash input preparation computes
+    it); inside it, segments of `interleave` positions go to ranks in turn;
+    a rank's local offset counts its whole rounds of segments and then the
+    offset inside the current segment; positions the rank does not own get
+    the pad slot.  With W == 1 the slot is the plain paged slot.
+    The rejected context suffix (index >= num_valid[b]), negative positions
+    and virtual blocks past the table width also get the pad slot.
+    """
+    positions = np.asarray(positions)
+    B, n = positions.shape
+    out = np.empty((B, n), dtype=np.int64)
+    nb = block_table.shape[1]
+    for b in range(B):
+        for i in range(n):
+            pos = int(positions[b, i])
+            if (num_valid is not None and i >= int(num_valid[b])) or pos < 0:
+                out[b, i] = PAD_SLOT_ID
+                continue
+            span = block_size * W
+            v = pos // span
+            off = pos % span
+            if v >= nb:
+                out[b, i] = PAD_SLOT_ID
+                continue
+            blk = int(block_table[b, v])
+            if W == 1:
+                out[b, i] = blk * block_size + off
+                continue
+            if (off // interleave) % W != r:
+                out[b, i] = PAD_SLOT_ID
+                continue
+            local = (off // (interleave * W)) * interleave + off % interleave
+            out[b, i] = blk * block_size + local
+    return out

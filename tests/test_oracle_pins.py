@@ -1,0 +1,375 @@
+"""Pins of the CPU oracle against facts it does not compute itself.
+
+Each test fixes a part of the oracle by something other than its own code:
+the pages' printed integer formulas, closed forms of softmax attention,
+torch's float64 scaled-dot-product attention with an explicit mask, a pure
+Python brute force, algebraic identities of the LSE merge, and hand-worked
+slot examples.  A plausible slip in the oracle (a dropped rope term, a wrong
+causal offset or rank, a transposed operand, a wrong LSE base, an off-by-one
+slot) breaks at least one of them; test_mutations_are_caught checks that.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import mla_oracle as O
+import workloads as WL
+from tests import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def tiny(B=2, H=3, Q=3, W=2, causal=True, lengths=(9, 14), seed=11, ranks=None, **kw):
+    spec = WL.Spec(name="tiny", B=B, H=H, Q=Q, causal=causal, seed=seed, lengths=list(lengths), W=W,
+                   ranks=tuple(range(W)) if ranks is None else ranks, block_size=4, **kw)
+    return WL.build(spec)
+
+
+def oracle_rank(wl, r, base="e", causal=None):
+    s = wl.spec
+    causal = s.causal if causal is None else causal
+    return oracle.mla_decode(wl.q_bits, wl.global_rows, wl.seq_lens[r], wl.tot, s.W, r, causal, s.scale, base)
+
+
+# ---------------------------------------------------------------- lengths
+
+def page_local_len(G, W, r, I):
+    """Rank-local length as printed on the PR #52188 page (key source snippets)."""
+    span = W * I
+    rem = min(max(G % span - r * I, 0), I)
+    return G // span * I + rem
+
+
+def test_local_count_matches_page_formula_and_ceil():
+    for W in range(1, 17):
+        for r in range(W):
+            for G in range(0, 2000):
+                n = oracle.local_count(G, W, r)
+                assert n == page_local_len(G, W, r, 1), (G, W, r)
+                assert n == -(-max(G - r, 0) // W), (G, W, r)
+
+
+def test_page_formula_with_interleave_matches_enumeration():
+    # ownership with interleave I: segment index (p // I) mod W picks the rank
+    for I in (1, 2, 4):
+        for W in (1, 2, 3, 8):
+            for r in range(W):
+                for G in range(0, 300):
+                    enum = sum(1 for p in range(G) if (p // I) % W == r)
+                    assert enum == page_local_len(G, W, r, I)
+
+
+def test_visible_count_textbook_causal_w1():
+    # the token at global position tot-Q+j sees positions 0..tot-Q+j
+    for tot in range(0, 40):
+        for Q in range(1, 6):
+            for j in range(Q):
+                pos = oracle.visible_positions(tot, tot, Q, j, 1, 0, True)
+                expect = max(tot - Q + j + 1, 0)
+                assert pos.tolist() == list(range(expect))
+
+
+def test_visible_positions_match_bruteforce_predicate():
+    for W in (1, 2, 3, 8):
+        for r in range(W):
+            for tot in range(0, 45, 3):
+                seq = oracle.local_count(tot, W, r)
+                for Q in (1, 3, 4):
+                    for j in range(Q):
+                        for causal in (True, False):
+                            got = oracle.visible_positions(seq, tot, Q, j, W, r, causal).tolist()
+                            exp = [p for p in range(tot + W) if brute.is_visible(p, j, Q, tot, seq, W, r, causal)]
+                            assert got == exp
+
+
+def test_end_aligned_local_mask_differs_under_dcp():
+    # PR #48180 page, review highlights: a local end-aligned causal mask is
+    # wrong under DCP when q_len > 1.  W=8, r=0, tot=32, Q=4.
+    W, r, tot, Q = 8, 0, 32, 4
+    n_local = oracle.local_count(tot, W, r)
+    correct = [oracle.visible_positions(n_local, tot, Q, j, W, r, True).size for j in range(Q)]
+    end_aligned = [n_local - (Q - 1 - j) for j in range(Q)]
+    assert correct == [4, 4, 4, 4]
+    assert end_aligned == [1, 2, 3, 4]
+    assert correct != end_aligned
+
+
+# ---------------------------------------------------------------- attention values
+
+def sdpa_reference(wl, r, base="e"):
+    """torch float64 SDPA over the *full global* KV with a visibility mask."""
+    s = wl.spec
+    B, Q, H = s.B, s.Q, s.H
+    outs = np.zeros((B * Q, H, 512))
+    lses = np.zeros((B * Q, H))
+    for b in range(B):
+        kv = O.bf16_bits_to_f64(wl.global_kv(b))
+        L = kv.shape[0]
+        q = O.bf16_bits_to_f64(wl.q_bits[b])            # [Q, H, 576]
+        mask = np.zeros((Q, L), dtype=bool)
+        for j in range(Q):
+            for p in range(L):
+                mask[j, p] = brute.is_visible(p, j, Q, int(wl.tot[b]), int(wl.seq_lens[r][b]), s.W, r, s.causal)
+        qt = torch.from_numpy(q).permute(1, 0, 2).unsqueeze(0)          # [1, H, Q, 576]
+        kt = torch.from_numpy(kv).unsqueeze(0).unsqueeze(0).expand(1, H, L, 576)
+        vt = torch.from_numpy(np.ascontiguousarray(kv[:, :512])).unsqueeze(0).unsqueeze(0).expand(1, H, L, 512)
+        mt = torch.from_numpy(mask)
+        for j in range(Q):
+            if not mask[j].any():
+                outs[b * Q + j] = 0.0
+                lses[b * Q + j] = -np.inf
+                continue
+            o = torch.nn.functional.scaled_dot_product_attention(
+                qt[:, :, j:j + 1], kt, vt, attn_mask=mt[j:j + 1], scale=s.scale)
+            outs[b * Q + j] = o[0, :, 0].numpy()
+            sc = s.scale * (qt[0, :, j].unsqueeze(1) @ kt[0].transpose(-1, -2)).squeeze(1)   # [H, L]
+            sc = sc.masked_fill(~mt[j], -math.inf)
+            l = torch.logsumexp(sc, dim=-1).numpy()
+            lses[b * Q + j] = l / math.log(2.0) if base == "2" else l
+    return outs, lses
+
+
+@pytest.mark.parametrize("W,causal", [(1, True), (2, True), (3, True), (2, False), (4, False)])
+def test_oracle_matches_torch_sdpa(W, causal):
+    wl = tiny(B=2, H=3, Q=3, W=W, causal=causal, lengths=(9, 23), seed=100 + W)
+    for r in range(W):
+        o, l = oracle_rank(wl, r)
+        ro, rl = sdpa_reference(wl, r)
+        np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l, rl, rtol=0, atol=1e-12)
+
+
+def test_oracle_matches_pure_python_bruteforce():
+    wl = tiny(B=2, H=2, Q=3, W=3, causal=True, lengths=(7, 11), seed=5)
+    s = wl.spec
+    for r in range(3):
+        for base in ("e", "2"):
+            o, l = oracle_rank(wl, r, base)
+            for b in range(2):
+                kv = [[brute.bf16_to_float(x) for x in row] for row in wl.global_kv(b)]
+                for j in range(s.Q):
+                    for h in range(s.H):
+                        q = [brute.bf16_to_float(x) for x in wl.q_bits[b, j, h]]
+                        bo, bl = brute.attend_row(q, kv, j, s.Q, int(wl.tot[b]), int(wl.seq_lens[r][b]),
+                                                  s.W, r, True, s.scale, base)
+                        assert abs(l[b * s.Q + j, h] - bl) <= 1e-12 or (bl == -math.inf and l[b * s.Q + j, h] == -math.inf)
+                        np.testing.assert_allclose(o[b * s.Q + j, h], bo, rtol=0, atol=1e-12)
+
+
+def test_zero_query_gives_uniform_mean_and_log_count():
+    # q = 0: every visible score is 0, softmax is uniform: lse = ln(count), out = mean of V
+    wl = tiny(B=2, H=2, Q=4, W=3, causal=True, lengths=(17, 30), seed=9, q_zero=True)
+    s = wl.spec
+    for r in range(3):
+        o, l = oracle_rank(wl, r)
+        for b in range(2):
+            kv = O.bf16_bits_to_f64(wl.global_kv(b))
+            for j in range(s.Q):
+                vis = [p for p in range(kv.shape[0]) if brute.is_visible(p, j, s.Q, int(wl.tot[b]),
+                                                                        int(wl.seq_lens[r][b]), 3, r, True)]
+                if not vis:
+                    assert np.all(l[b * s.Q + j] == -np.inf) and np.all(o[b * s.Q + j] == 0)
+                    continue
+                np.testing.assert_allclose(l[b * s.Q + j], math.log(len(vis)), atol=1e-14)
+                np.testing.assert_allclose(o[b * s.Q + j], np.broadcast_to(kv[vis, :512].mean(0), (s.H, 512)), atol=1e-13)
+
+
+def test_single_visible_key_and_identical_keys_closed_forms():
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((4, 576))
+    k = rng.standard_normal((1, 576))
+    out, lse = oracle.attend(q, k, 0.37)
+    np.testing.assert_allclose(out, np.broadcast_to(k[0, :512], (4, 512)), atol=1e-15)
+    np.testing.assert_allclose(lse, 0.37 * (q @ k[0]), atol=1e-13)
+    kk = np.repeat(k, 7, axis=0)
+    out, lse = oracle.attend(q, kk, 0.37)
+    np.testing.assert_allclose(out, np.broadcast_to(k[0, :512], (4, 512)), atol=1e-14)
+    np.testing.assert_allclose(lse, 0.37 * (q @ k[0]) + math.log(7), atol=1e-13)
+    # nothing visible
+    out, lse = oracle.attend(q, np.zeros((0, 576)), 0.37)
+    assert np.all(out == 0) and np.all(lse == -np.inf)
+
+
+def test_lse_base_two_is_base_e_over_ln2():
+    wl = tiny(B=2, H=3, Q=2, W=2, causal=True, lengths=(10, 13), seed=21)
+    for r in range(2):
+        oe, le = oracle_rank(wl, r, "e")
+        o2, l2 = oracle_rank(wl, r, "2")
+        np.testing.assert_array_equal(oe, o2)
+        fin = np.isfinite(le)
+        np.testing.assert_allclose(le[fin], math.log(2.0) * l2[fin], rtol=1e-14)
+
+
+def test_single_rank_equals_non_dcp():
+    wl = tiny(B=2, H=3, Q=3, W=1, causal=True, lengths=(12, 19), seed=31)
+    o1, l1 = oracle.mla_decode(wl.q_bits, wl.global_rows, wl.seq_lens[0], wl.tot, 1, 0, True, wl.spec.scale)
+    o0, l0 = oracle.mla_decode(wl.q_bits, wl.global_rows, wl.seq_lens[0], None, 1, 0, True, wl.spec.scale)
+    np.testing.assert_array_equal(o1, o0)
+    np.testing.assert_array_equal(l1, l0)
+
+
+@pytest.mark.parametrize("W,causal,base", [(2, True, "e"), (8, True, "e"), (3, False, "2"), (8, True, "2")])
+def test_sharded_then_merged_equals_unsharded(W, causal, base):
+    wl = tiny(B=3, H=2, Q=4, W=W, causal=causal, lengths=(5, 29, 40), seed=41 + W)
+    parts = [oracle_rank(wl, r, base) for r in range(W)]
+    mo, ml = oracle.merge_lse([p[0] for p in parts], [p[1] for p in parts], base)
+    un = WL.unsharded(wl)
+    uo, ul = oracle.mla_decode(un.q_bits, un.global_rows, un.seq_lens[0], un.tot, 1, 0, causal, wl.spec.scale, base)
+    np.testing.assert_allclose(mo, uo, atol=1e-12)
+    np.testing.assert_allclose(ml, ul, atol=1e-12)
+
+
+def test_merge_special_cases():
+    rng = np.random.default_rng(0)
+    o = rng.standard_normal((3, 2, 512))
+    l = rng.standard_normal((3, 2))
+    mo, ml = oracle.merge_lse([o], [l])
+    np.testing.assert_allclose(mo, o, atol=1e-15)
+    np.testing.assert_allclose(ml, l, atol=1e-15)
+    # a -inf partial has weight 0
+    mo, ml = oracle.merge_lse([o, np.zeros_like(o)], [l, np.full_like(l, -np.inf)])
+    np.testing.assert_allclose(mo, o, atol=1e-15)
+    np.testing.assert_allclose(ml, l, atol=1e-15)
+    # every partial empty
+    mo, ml = oracle.merge_lse([np.zeros_like(o)] * 3, [np.full_like(l, -np.inf)] * 3)
+    assert np.all(mo == 0) and np.all(ml == -np.inf)
+    # two equal partials: same out, lse + ln 2 (base e) / + 1 (base 2)
+    mo, ml = oracle.merge_lse([o, o], [l, l], "e")
+    np.testing.assert_allclose(mo, o, atol=1e-15)
+    np.testing.assert_allclose(ml, l + math.log(2), atol=1e-14)
+    mo, ml = oracle.merge_lse([o, o], [l, l], "2")
+    np.testing.assert_allclose(ml, l + 1.0, atol=1e-14)
+
+
+# ---------------------------------------------------------------- slots
+
+@pytest.mark.parametrize("fname", ["cp_local_slot_hand_example.json", "cp_local_slot_interleave2_hand_example.json"])
+def test_slot_hand_examples(fname):
+    g = json.load(open(os.path.join(GOLDEN, fname)))
+    bt = np.array(g["block_table"], dtype=np.int32)
+    pos = np.array(g["positions"], dtype=np.int64)
+    for r, exp in g["expected"].items():
+        got = oracle.cp_local_slot(pos, bt, g["block_size"], g["cp_world"], int(r), g["interleave"])
+        assert got.tolist() == exp
+
+
+def test_slot_single_rank_is_textbook_paging():
+    rng = np.random.default_rng(1)
+    bt = rng.permutation(50).astype(np.int32)[:40].reshape(4, 10)
+    pos = rng.integers(0, 10 * 16, size=(4, 33))
+    got = oracle.cp_local_slot(pos, bt, 16, 1, 0)
+    exp = np.array([[bt[b, p // 16] * 16 + p % 16 for p in pos[b]] for b in range(4)])
+    np.testing.assert_array_equal(got, exp)
+
+
+@pytest.mark.parametrize("W,I,bs", [(2, 1, 4), (4, 1, 16), (8, 1, 64), (3, 2, 4), (4, 4, 16)])
+def test_slot_ownership_and_local_layout(W, I, bs):
+    # exactly one rank owns each position; rank r's slots are its local rows
+    # t = 0, 1, ... laid out by plain paging inside the shared table
+    rng = np.random.default_rng(W * 10 + I)
+    nb = 6
+    bt = rng.permutation(3 * nb).astype(np.int32)[:nb].reshape(1, nb)
+    L = nb * bs * W
+    pos = np.arange(L, dtype=np.int64).reshape(1, L)
+    slots = np.stack([oracle.cp_local_slot(pos, bt, bs, W, r, I)[0] for r in range(W)])
+    owners = (slots != oracle.PAD_SLOT_ID).sum(0)
+    assert np.all(owners == 1)
+    for r in range(W):
+        mine = slots[r][slots[r] != oracle.PAD_SLOT_ID]
+        n = mine.size
+        exp = [bt[0, t // bs] * bs + t % bs for t in range(n)]
+        assert mine.tolist() == exp
+
+
+def test_slot_pad_cases():
+    bt = np.array([[2, 5], [1, 0]], dtype=np.int32)
+    pos = np.array([[0, 1, 2, -3, 40, 9], [3, 4, 5, 6, 7, 8]], dtype=np.int64)
+    nv = np.array([4, 2], dtype=np.int32)
+    got = oracle.cp_local_slot(pos, bt, 4, 2, 0, 1, nv)
+    # request 0: index >= 4 is the rejected suffix; -3 is negative
+    assert got[0].tolist() == [8, -1, 9, -1, -1, -1]
+    # request 1: only the first 2 entries are valid
+    assert got[1].tolist() == [-1, 6, -1, -1, -1, -1]
+    # virtual block past the table width
+    got = oracle.cp_local_slot(np.array([[16, 15]]), np.array([[3, 4]], dtype=np.int32), 4, 2, 1)
+    assert got.tolist() == [[-1, 19]]
+
+
+def test_draft_rejected_suffix_maps_to_pad():
+    # PR #52188 page: at cp_rank=1, cp_size=2 the rejected context suffix maps to the pad slot
+    spec = WL.Spec(name="draft", B=4, H=2, Q=16, causal=False, seed=77, lengths=[300, 517, 1000, 1601],
+                   W=2, ranks=(1,), block_size=8)
+    wl = WL.build(spec)
+    si = WL.draft_slot_inputs(wl)
+    got = oracle.cp_local_slot(si["ctx_positions"], wl.block_table, 8, 2, 1, 1, si["ctx_num_valid"])
+    for b in range(4):
+        nv = int(si["ctx_num_valid"][b])
+        assert np.all(got[b, nv:] == oracle.PAD_SLOT_ID)
+        for i in range(nv):
+            p = int(si["ctx_positions"][b, i])
+            if p % 2 == 1:
+                t = p // 2
+                assert got[b, i] == wl.block_table[b, t // 8] * 8 + t % 8
+            else:
+                assert got[b, i] == oracle.PAD_SLOT_ID
+
+
+# ---------------------------------------------------------------- generator consistency
+
+def test_paged_pool_holds_the_shards():
+    wl = tiny(B=3, H=2, Q=2, W=3, causal=True, lengths=(1, 30, 47), seed=61)
+    bs = wl.spec.block_size
+    for r in range(3):
+        for b in range(3):
+            n = int(wl.seq_lens[r][b])
+            for t in range(n):
+                np.testing.assert_array_equal(wl.pools[r][wl.block_table[b, t // bs], t % bs], wl.shards[r][b][t])
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def test_mutations_are_caught(monkeypatch):
+    """Plant plausible slips in the oracle (CPU only) and check a pin catches each."""
+    wl = tiny(B=2, H=2, Q=3, W=2, causal=True, lengths=(9, 16), seed=7)
+
+    def pins_pass():
+        try:
+            for r in range(2):
+                o, l = oracle_rank(wl, r)
+                ro, rl = sdpa_reference(wl, r)
+                np.testing.assert_allclose(o, ro, atol=1e-9)
+                np.testing.assert_allclose(l, rl, atol=1e-9)
+            return True
+        except AssertionError:
+            return False
+
+    assert pins_pass()
+    real_attend = O.attend
+    real_vis = O.visible_positions
+
+    muts = {
+        "drop rope part of the score": lambda q, kv, sc, base="e": real_attend(
+            np.concatenate([q[:, :512], 0 * q[:, 512:]], 1), kv, sc, base),
+        "wrong scale": lambda q, kv, sc, base="e": real_attend(q, kv, sc * 1.01, base),
+        "lse in base 2": lambda q, kv, sc, base="e": real_attend(q, kv, sc, "2"),
+    }
+    for name, fn in muts.items():
+        monkeypatch.setattr(O, "attend", fn)
+        assert not pins_pass(), name
+        monkeypatch.setattr(O, "attend", real_attend)
+
+    vis_muts = {
+        "causal offset off by one": lambda s, t, Q, j, W, r, c: real_vis(s, t + 1, Q, j, W, r, c),
+        "wrong rank": lambda s, t, Q, j, W, r, c: real_vis(s, t, Q, j, W, (r + 1) % W, c),
+        "end-aligned local mask": lambda s, t, Q, j, W, r, c: real_vis(s, t, Q, j, W, r, False)[: max(s - (Q - 1 - j), 0)],
+    }
+    for name, fn in vis_muts.items():
+        monkeypatch.setattr(O, "visible_positions", fn)
+        assert not pins_pass(), name
+        monkeypatch.setattr(O, "visible_positions", real_vis)
+    assert pins_pass()
