@@ -1,0 +1,232 @@
+"""Python binding of libmla_decode.so: paged absorbed-MLA decode on MI355X (gfx950).
+
+Argument marshalling only.  Every step runs in the library's HIP kernels;
+torch provides device memory and the current stream.  There is no fallback:
+if the library is missing or a tensor is not on the GPU, calls raise.
+
+Entry points (same names as the C ABI in include/mla_decode.h):
+  mla_decode(q, kv_cache, block_table, seq_lens, causal_seqlens_global,
+             cp_world, cp_rank, q_len, causal, scale, lse_base) -> (out, lse)
+  mla_merge_lse(partials, lses, lse_base) -> (out, lse)
+  cp_local_slot(positions, block_table, block_size, cp_world, cp_rank,
+                num_valid=None, cp_interleave=1) -> slots
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+__all__ = [
+    "D_QK", "D_V", "PAD_SLOT_ID", "LSE_BASE_E", "LSE_BASE_2", "MLAError",
+    "library_path", "load_library", "exported_symbols",
+    "mla_decode", "mla_decode_workspace_size", "mla_merge_lse", "cp_local_slot",
+]
+
+D_QK = 576
+D_V = 512
+PAD_SLOT_ID = -1
+LSE_BASE_E = 0
+LSE_BASE_2 = 1
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libmla_decode.so"
+_lib = None
+
+# (name, restype, argtypes) for every function include/mla_decode.h declares
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SIGNATURES = [
+    ("mla_status_string", ctypes.c_char_p, [_I]),
+    ("mla_decode_workspace_size", ctypes.c_size_t, [_I, _I, _I, _I]),
+    ("mla_decode", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                        ctypes.c_float, _I, _P, _P, _P, ctypes.c_size_t, _P]),
+    ("mla_merge_lse", _I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
+    ("cp_local_slot", _I, [_P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, _P]),
+]
+
+
+class MLAError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return os.environ.get("MLA_DECODE_LIB", os.path.join(_PKG, _LIB_NAME))
+
+
+def load_library():
+    """Load the HIP library (built by decode_attention_11_amd.build); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m decode_attention_11_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, res, args in _SIGNATURES:
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def exported_symbols() -> Sequence[str]:
+    return [s[0] for s in _SIGNATURES]
+
+
+def _check(status: int) -> None:
+    if status == 0:
+        return
+    msg = load_library().mla_status_string(status).decode()
+    if status in (1, 2):
+        raise ValueError(f"libmla_decode: {msg} (status {status})")
+    raise MLAError(f"libmla_decode: {msg} (status {status})")
+
+
+def _need(t: torch.Tensor, name: str, dtype, dim: Optional[int] = None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims, got shape {tuple(t.shape)}")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def mla_decode_workspace_size(B: int, q_len: int, H: int, max_seq_len: int) -> int:
+    return int(load_library().mla_decode_workspace_size(B, q_len, H, max_seq_len))
+
+
+def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+               causal_seqlens_global: Optional[torch.Tensor] = None, cp_world: int = 1, cp_rank: int = 0,
+               q_len: Optional[int] = None, causal: bool = True, scale: Optional[float] = None,
+               lse_base: str = "e", *, max_seq_len: Optional[int] = None,
+               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None, return_lse: bool = True
+               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """One rank's paged MLA decode.  q: [B, q_len, H, 576] (or [B*q_len, H, 576]
+    with q_len given) bf16; kv_cache: [num_blocks, block_size, 576] bf16.
+    Returns out [B*q_len, H, 512] bf16 and lse [B*q_len, H] float32."""
+    lib = load_library()
+    if q.dim() == 3:
+        if q_len is None:
+            raise ValueError("q_len is required for a [tokens, H, 576] query")
+        if q.shape[0] % q_len:
+            raise ValueError("uneven query lengths are not supported: tokens must be B*q_len")
+        q = q.view(q.shape[0] // q_len, q_len, q.shape[1], q.shape[2])
+    _need(q, "q", torch.bfloat16, 4)
+    B, Q, H, Dq = q.shape
+    if q_len is not None and q_len != Q:
+        raise ValueError(f"q_len={q_len} does not match q.shape[1]={Q}")
+    if Dq != D_QK:
+        raise ValueError(f"q last dim must be {D_QK}")
+    _need(kv_cache, "kv_cache", torch.bfloat16, 3)
+    if kv_cache.shape[2] != D_QK:
+        raise ValueError(f"kv_cache last dim must be {D_QK}")
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    if block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_table and seq_lens must have B rows")
+    if causal_seqlens_global is not None:
+        _need(causal_seqlens_global, "causal_seqlens_global", torch.int32, 1)
+        if causal_seqlens_global.shape[0] != B:
+            raise ValueError("causal_seqlens_global must have B entries")
+    num_blocks, bs = int(kv_cache.shape[0]), int(kv_cache.shape[1])
+    max_blocks = int(block_table.shape[1])
+    if max_seq_len is None:
+        max_seq_len = max_blocks * bs  # the table's capacity bounds every local length
+    if scale is None:
+        scale = 1.0 / math.sqrt(192.0)
+    base = {"e": LSE_BASE_E, "2": LSE_BASE_2}.get(str(lse_base))
+    if base is None:
+        raise ValueError("lse_base must be 'e' or '2'")
+    dev = q.device
+    if out is None:
+        out = torch.empty((B * Q, H, D_V), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", torch.bfloat16, 3)
+        if tuple(out.shape) != (B * Q, H, D_V):
+            raise ValueError("out must be [B*q_len, H, 512]")
+    if return_lse:
+        if lse is None:
+            lse = torch.empty((B * Q, H), dtype=torch.float32, device=dev)
+        else:
+            _need(lse, "lse", torch.float32, 2)
+            if tuple(lse.shape) != (B * Q, H):
+                raise ValueError("lse must be [B*q_len, H]")
+    ws_bytes = int(lib.mla_decode_workspace_size(B, Q, H, int(max_seq_len)))
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+    _check(lib.mla_decode(
+        q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(),
+        causal_seqlens_global.data_ptr() if causal_seqlens_global is not None else None,
+        B, Q, H, num_blocks, bs, max_blocks, int(max_seq_len), int(cp_world), int(cp_rank),
+        1 if causal else 0, float(scale), base, out.data_ptr(),
+        lse.data_ptr() if (return_lse and lse is not None) else None,
+        workspace.data_ptr(), int(workspace.numel()), _stream(dev)))
+    return out, (lse if return_lse else None)
+
+
+def mla_merge_lse(partials: Sequence[torch.Tensor], lses: Sequence[torch.Tensor], lse_base: str = "e",
+                  *, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+                  ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """LSE-weighted merge of partial outputs [rows, H, 512] bf16 with their lse [rows, H] f32."""
+    lib = load_library()
+    n = len(partials)
+    if n != len(lses) or n < 1 or n > 64:
+        raise ValueError("need 1..64 partials with one lse each")
+    for i, (p, l) in enumerate(zip(partials, lses)):
+        _need(p, f"partials[{i}]", torch.bfloat16, 3)
+        _need(l, f"lses[{i}]", torch.float32, 2)
+        if p.shape != partials[0].shape or tuple(l.shape) != tuple(partials[0].shape[:2]):
+            raise ValueError("partials and lses must share shapes [rows, H, 512] / [rows, H]")
+    rows, H, dv = partials[0].shape
+    if dv != D_V:
+        raise ValueError("partials must be [rows, H, 512]")
+    base = {"e": LSE_BASE_E, "2": LSE_BASE_2}.get(str(lse_base))
+    if base is None:
+        raise ValueError("lse_base must be 'e' or '2'")
+    dev = partials[0].device
+    out = torch.empty((rows, H, D_V), dtype=torch.bfloat16, device=dev) if out is None else out
+    lse = torch.empty((rows, H), dtype=torch.float32, device=dev) if lse is None else lse
+    _need(out, "out", torch.bfloat16, 3)
+    _need(lse, "lse", torch.float32, 2)
+    parr = (ctypes.c_void_p * n)(*[p.data_ptr() for p in partials])
+    larr = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lses])
+    _check(lib.mla_merge_lse(ctypes.cast(parr, ctypes.c_void_p), ctypes.cast(larr, ctypes.c_void_p), n,
+                             int(rows), int(H), base, out.data_ptr(), lse.data_ptr(), _stream(dev)))
+    return out, lse
+
+
+def cp_local_slot(positions: torch.Tensor, block_table: torch.Tensor, block_size: int, cp_world: int,
+                  cp_rank: int, num_valid: Optional[torch.Tensor] = None, cp_interleave: int = 1,
+                  *, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Rank-local slots [B, n] int64 of positions [B, n] int64, PAD_SLOT_ID where not owned."""
+    lib = load_library()
+    _need(positions, "positions", torch.int64, 2)
+    _need(block_table, "block_table", torch.int32, 2)
+    B, n = positions.shape
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must have B rows")
+    if num_valid is not None:
+        _need(num_valid, "num_valid", torch.int32, 1)
+        if num_valid.shape[0] != B:
+            raise ValueError("num_valid must have B entries")
+    out = torch.empty((B, n), dtype=torch.int64, device=positions.device) if out is None else out
+    _need(out, "out", torch.int64, 2)
+    _check(lib.cp_local_slot(positions.data_ptr(), num_valid.data_ptr() if num_valid is not None else None,
+                             int(B), int(n), block_table.data_ptr(), int(block_table.shape[1]),
+                             int(block_size), int(cp_world), int(cp_rank), int(cp_interleave),
+                             out.data_ptr(), _stream(positions.device)))
+    return out

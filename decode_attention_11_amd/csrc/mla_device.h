@@ -1,0 +1,67 @@
+// Device-side helpers shared by the gfx950 kernels of libmla_decode.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int D_QK = 576;
+constexpr int D_V = 512;
+constexpr int ROW_BYTES = D_QK * 2;  // one latent KV row / one query head: 1152 bytes
+constexpr float NEG_INF = -__builtin_inff();
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Two floats to packed bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x2 to_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_convertvector(v, bf16x2);
+}
+
+__device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) {
+  f32x4 v = {a, b, c, d};
+  return __builtin_convertvector(v, bf16x4);
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint8_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  bf16x8 z;
+  for (int i = 0; i < 8; ++i) z[i] = (__bf16)0.0f;
+  return z;
+}
+
+// Rank-local visible key count of query row j of a request (interleave 1):
+// causal rows see the global prefix tot - (q_len-1-j) of which rank r holds
+// ceil(max(prefix - r, 0) / W) positions, capped by the rank's local length;
+// non-causal rows see the whole local length.
+__device__ __forceinline__ int row_bound(int seq, int tot, int q_len, int j, int W, int r, int causal) {
+  if (seq < 0) seq = 0;
+  if (!causal) return seq;
+  int64_t g = (int64_t)tot - (q_len - 1 - j);
+  int64_t x = g - r;
+  if (x < 0) x = 0;
+  int64_t n = (x + W - 1) / W;
+  return n < seq ? (int)n : seq;
+}
+
+// Index of the balanced work range that holds unit u when T units are cut
+// into G ranges [floor(w*T/G), floor((w+1)*T/G)).
+__device__ __forceinline__ int range_owner(int64_t u, int64_t T, int G) {
+  return (int)(((u + 1) * (int64_t)G - 1) / T);
+}
+
+}  // namespace mla

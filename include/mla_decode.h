@@ -1,0 +1,169 @@
+/*
+ * Paged absorbed-MLA decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libmla_decode.so.  Every entry point takes plain device pointers
+ * and sizes, enqueues its work on the given HIP stream and returns a status
+ * code; nothing synchronises with the host, and nothing is allocated: the
+ * caller owns every buffer, including the decode workspace.  All argument
+ * checks happen on the host before any launch, so a non-zero status means
+ * nothing was enqueued.  Calls on different streams may overlap; a workspace
+ * must not be shared by two calls in flight at the same time.
+ *
+ * Sources: three vLLM pull-request digest pages (prhub.com.cn):
+ *   PR #52188 "support Kimi-K3 DSpark speculative decoding with DCP",
+ *   PR #54012 "MLA decode with DCP switches to FlashInfer's native CP mask",
+ *   PR #48180 "TokenSpeed MLA backend gains DCP and Eagle support".
+ * Section names below are those pages' sections (summary, motivation,
+ * implementation breakdown, key files, key source snippets, review
+ * highlights, risks and impact).
+ */
+#ifndef MLA_DECODE_H_
+#define MLA_DECODE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Widths of absorbed MLA: 512 latent + 64 rope per query head and per KV row
+ * (PR #54012 page, key source snippets: kv_lora_rank 512, rope dim 64,
+ * query [.., heads, 576], output [.., heads, 512]). */
+#define MLA_D_QK 576
+#define MLA_D_V 512
+
+/* Slot value for positions a rank must not write (PR #52188 page, key source
+ * snippets, cp_local_slot).  The pages do not print its value; -1 cannot
+ * collide with a real slot. */
+#define MLA_PAD_SLOT_ID (-1LL)
+
+/* LSE bases.  Base e is the contract of the CuTeDSL DCP path (PR #54012
+ * page, implementation breakdown: lse_base_on_e becomes true); base 2 is
+ * TokenSpeed's (PR #48180 page, implementation breakdown). */
+#define MLA_LSE_BASE_E 0
+#define MLA_LSE_BASE_2 1
+
+/* Status codes. */
+#define MLA_OK 0
+#define MLA_ERR_INVALID_ARG 1  /* a null pointer, a size or index out of range, a workspace too small */
+#define MLA_ERR_UNSUPPORTED 2  /* a valid request this library does not implement (interleave != 1 in attention) */
+#define MLA_ERR_HIP 3          /* the HIP runtime refused a launch */
+
+/* Short static description of a status code; never NULL. */
+const char* mla_status_string(int status);
+
+/*
+ * Bytes of device workspace mla_decode needs for these sizes on the current
+ * device (0 when none).  max_seq_len only sizes the work split; any upper
+ * bound works.  Returns 0 for invalid sizes.
+ */
+size_t mla_decode_workspace_size(int B, int q_len, int H, int max_seq_len);
+
+/*
+ * One rank's absorbed MLA decode over its paged latent KV cache.
+ *
+ * What is computed (PR #54012 page, implementation breakdown and key source
+ * snippets: the native-DCP kernel receives rank-local seq_lens together with
+ * the global causal lengths, cp_world and cp_rank and masks every query row
+ * itself; PR #52188 page, key source snippets: the per-row prefix and its
+ * round-robin rank-local length; PR #48180 page, key source snippets: the
+ * same contract for TokenSpeed with causal_seqs):
+ *   For request b, query row j < q_len, head h, the scores are
+ *     s_t = scale * sum_{d<576} q[b,j,h,d] * kv[row(b,t), d]
+ *   over the rank-local keys t < n(b,j), where
+ *     causal:     G = max(tot_b - (q_len-1-j), 0),
+ *                 n(b,j) = min(seq_lens[b], ceil(max(G - cp_rank, 0) / cp_world)),
+ *                 tot_b = causal_seqlens_global[b] (or seq_lens[b] when that
+ *                 pointer is NULL, allowed only for cp_world == 1);
+ *     non-causal: n(b,j) = seq_lens[b] for every row (a draft block).
+ *   out[b*q_len+j, h, :] = softmax(s) @ kv[row(b,t), 0:512]   (bf16, RNE)
+ *   lse[b*q_len+j, h]    = log of sum_t exp(s_t), natural log for
+ *                          MLA_LSE_BASE_E, log2 for MLA_LSE_BASE_2.
+ *   A row with n(b,j) == 0 gets out = 0 and lse = -inf.
+ *   Local key t lives at physical row
+ *     block_table[b*max_blocks + t/block_size]*block_size + t%block_size.
+ *   The rank's keys are the global positions t*cp_world + cp_rank
+ *   (round-robin, interleave 1: the native CP mask requires it, PR #54012
+ *   page, implementation breakdown).
+ *
+ * Layouts (all contiguous, row-major, device memory):
+ *   q                     [B, q_len, H, 576] bf16
+ *   kv_cache              [num_blocks, block_size, 576] bf16 (512 latent, then 64 rope)
+ *   block_table           [B, max_blocks] int32
+ *   seq_lens              [B] int32, rank-local lengths
+ *   causal_seqlens_global [B] int32 or NULL, global lengths including the
+ *                         request's own q_len query tokens
+ *   out                   [B*q_len, H, 512] bf16
+ *   lse                   [B*q_len, H] float32, or NULL to skip it
+ *   workspace             >= mla_decode_workspace_size(B, q_len, H, max_seq_len) bytes
+ * Arguments: causal is 0 or 1; lse_base is MLA_LSE_BASE_E or MLA_LSE_BASE_2;
+ * 0 <= cp_rank < cp_world.  B == 0 is a no-op.
+ * Device-side preconditions (not checked on the host, which cannot read
+ * device memory without a sync): seq_lens[b] <= max_blocks*block_size.
+ * Out-of-range block ids are guarded in the kernel: such keys read as zero
+ * rows instead of faulting, and the result for that request is undefined.
+ * Errors: MLA_ERR_INVALID_ARG for null pointers, sizes < 1 (B < 0),
+ * cp_rank outside [0, cp_world), causal with cp_world > 1 and a NULL global
+ * pointer, an unknown lse_base, a non-finite scale, or a workspace smaller
+ * than required; MLA_ERR_HIP if a launch fails.
+ */
+int mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
+               const int32_t* seq_lens, const int32_t* causal_seqlens_global,
+               int B, int q_len, int H, int num_blocks, int block_size, int max_blocks,
+               int max_seq_len, int cp_world, int cp_rank, int causal, float scale,
+               int lse_base, void* out, float* lse, void* workspace, size_t workspace_bytes,
+               hipStream_t stream);
+
+/*
+ * Merge partial attention results of disjoint key sets (the ranks' shards)
+ * by their LSE (PR #54012 page, implementation breakdown: the CP path returns
+ * a natural-log LSE and the bases must agree before the cross-rank merge;
+ * PR #48180 page, implementation breakdown: the DCP decode output is merged
+ * after the kernel).  With M = max_i lse_i and beta the base:
+ *   w_i = beta^(lse_i - M),  out = sum_i w_i out_i / sum_i w_i,
+ *   lse = M + log_beta(sum_i w_i);
+ * partials with lse = -inf get weight 0; if all are -inf the result is
+ * out = 0, lse = -inf.
+ * partials: host array of n_parts device pointers, each [rows, H, 512] bf16.
+ * lses:     host array of n_parts device pointers, each [rows, H] float32.
+ * out: [rows, H, 512] bf16; lse: [rows, H] float32 or NULL.
+ * 1 <= n_parts <= 64.  The host arrays are read during the call only.
+ * Errors: MLA_ERR_INVALID_ARG for null pointers, n_parts outside [1, 64],
+ * rows < 0, H < 1, or an unknown lse_base; MLA_ERR_HIP if the launch fails.
+ */
+int mla_merge_lse(const void* const* partials, const float* const* lses, int n_parts,
+                  int rows, int H, int lse_base, void* out, float* lse, hipStream_t stream);
+
+/*
+ * Rank-local KV slot of each position, or MLA_PAD_SLOT_ID (PR #52188 page,
+ * key source snippets, cp_local_slot; implementation breakdown: the DFlash
+ * input preparation takes the virtual block index pos // (block_size*cp_world)
+ * and applies the slot mapping to context and query positions).  For
+ * position pos = positions[b*n + i]:
+ *   span = block_size*cp_world, v = pos / span, off = pos % span;
+ *   pad if i >= num_valid[b] (the rejected suffix), pos < 0, or v >= max_blocks;
+ *   blk = block_table[b*max_blocks + v];
+ *   cp_world == 1: slot = blk*block_size + off;
+ *   else pad unless (off / cp_interleave) % cp_world == cp_rank, and then
+ *     slot = blk*block_size + (off / (cp_interleave*cp_world))*cp_interleave
+ *            + off % cp_interleave.
+ * positions: [B, n] int64; num_valid: [B] int32 or NULL (all valid);
+ * block_table: [B, max_blocks] int32; slots: [B, n] int64.  Bit-exact integer
+ * arithmetic in 64 bits.
+ * Errors: MLA_ERR_INVALID_ARG for null pointers (when B*n > 0), B or n < 0,
+ * max_blocks < 1, block_size < 1, cp_world < 1, cp_rank outside
+ * [0, cp_world), cp_interleave < 1 or block_size not a multiple of
+ * cp_interleave; MLA_ERR_HIP if the launch fails.
+ */
+int cp_local_slot(const int64_t* positions, const int32_t* num_valid, int B, int n,
+                  const int32_t* block_table, int max_blocks, int block_size,
+                  int cp_world, int cp_rank, int cp_interleave, int64_t* slots,
+                  hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H_ */
