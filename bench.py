@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged MLA decode hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N] [--no-cpu-baseline]
+
+A step is one pass of the hot path over one batch of synthetic input:
+  * slot mapping of the step's new tokens (cp_local_slot),
+  * each rank's decode (mla_decode: row bounds, paged gather, QK^T, online
+    softmax, PV, split combine, finalise),
+  * and, for a sharded workload, the LSE merge of the ranks' partials.
+The default workload is the memory-bound single-token decode (batch 64,
+16 heads, lengths uniform in [1024, 8192]); --config 1..5 picks another.
+Inputs are resident in HBM before timing starts.  Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode TFLOP/s + KV GB/s and % of binding roofline, 1×MI355X"
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2516.6    # 256 CU x 4096 flop/clk x 2.4 GHz, dense bf16
+FLOP_PER_KEY_ROW = 2 * 576 + 2 * 512   # QK^T (576-wide) + PV (512-wide) per (row, key)
+KV_ROW_BYTES = 576 * 2
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ HIP events
+class Hip:
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def record(self, e, stream):
+        assert self.lib.hipEventRecord(e, stream) == 0
+
+    def elapsed_ms(self, a, b):
+        assert self.lib.hipEventSynchronize(b) == 0
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
+
+
+# ------------------------------------------------------------------ algorithmic work
+def row_keys(seq, tot, Q, j, W, r, causal):
+    """Rank-local visible keys of row j (the same bound the kernel applies)."""
+    if not causal:
+        return seq
+    g = tot - (Q - 1 - j)
+    return min(seq, -(-max(g - r, 0) // W))
+
+
+def rank_work(wl, r):
+    s = wl.spec
+    flops = 0
+    kv = 0
+    bt = 0
+    for b in range(s.B):
+        seq = int(wl.seq_lens[r][b])
+        tot = int(wl.tot[b]) if not s.global_is_null else seq
+        nmax = row_keys(seq, tot, s.Q, s.Q - 1, s.W, r, s.causal)
+        kv += nmax * KV_ROW_BYTES
+        bt += -(-nmax // s.block_size) * 4
+        for j in range(s.Q):
+            flops += row_keys(seq, tot, s.Q, j, s.W, r, s.causal) * s.H * FLOP_PER_KEY_ROW
+    rows = s.B * s.Q * s.H
+    return dict(flops=flops, kv_bytes=kv, q_bytes=rows * KV_ROW_BYTES, bt_bytes=bt,
+                out_bytes=rows * 512 * 2, lse_bytes=rows * 4)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "decode_attention_11_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------ CPU baseline (oracle)
+def cpu_baseline(wl, ranks, unit, budget_s=20.0):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = 1
+    s = wl.spec
+    done_b, flops, kv = 0, 0, 0
+    t0 = time.perf_counter()
+    for b in range(s.B):
+        for r in ranks:
+            seq = wl.seq_lens[r]
+            tot = None if (s.global_is_null and s.W == 1) else wl.tot
+            rows = [(b, j, h) for j in range(s.Q) for h in range(s.H)]
+            oracle.mla_decode(wl.q_bits, wl.global_rows, seq, tot, s.W, r, s.causal, s.scale, s.lse_base, rows=rows)
+            sq = int(seq[b])
+            tt = int(wl.tot[b]) if tot is not None else sq
+            kv += row_keys(sq, tt, s.Q, s.Q - 1, s.W, r, s.causal) * KV_ROW_BYTES
+            flops += sum(row_keys(sq, tt, s.Q, j, s.W, r, s.causal) for j in range(s.Q)) * s.H * FLOP_PER_KEY_ROW
+        done_b += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    value = kv / dt / 1e9 if unit == "GB/s" else flops / dt / 1e12
+    return {"value": round(value, 6), "unit": unit, "cores": int(cores), "kind": "oracle",
+            "sample": f"{done_b} of {s.B} requests, all {s.Q}x{s.H} rows, ranks {list(ranks)}, "
+                      f"float64 numpy oracle, {dt:.1f} s wall"}
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--replicas", type=int, default=0, help="KV replicas rotated per step (0: auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--out", default=None, help="also append the JSON line to this file")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        msg = ("this benchmark runs on one GPU only: decode-context-parallel shards are computed one after "
+               "another on a single MI355X and merged locally; run with --gpus 1")
+        print(msg, file=sys.stderr)
+        if int(os.environ.get("RANK", "0")) == 0:
+            print(json.dumps({"metric": METRIC, "error": msg, "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import decode_attention_11_amd as mla
+    import workloads as WL
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(3)
+    mla.load_library()
+    dev = torch.device("cuda:0")
+    hip = Hip()
+
+    spec = WL.config(args.config)
+    log(f"workload {spec.name}: generating inputs")
+    t0 = time.perf_counter()
+    wl = WL.build(spec)
+    log(f"generated in {time.perf_counter() - t0:.1f} s")
+    ranks = sorted(wl.pools)
+    s = spec
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    replicas = args.replicas or (3 if args.config in (1, 2) else 1)
+    q = bf16(wl.q_bits)
+    bt = torch.from_numpy(wl.block_table).to(dev)
+    tot = torch.from_numpy(wl.tot.astype(np.int32)).to(dev)
+    pools = {r: [bf16(wl.pools[r])] for r in ranks}
+    for r in ranks:
+        for _ in range(replicas - 1):
+            pools[r].append(pools[r][0].clone())
+    seq = {r: torch.from_numpy(wl.seq_lens[r]).to(dev) for r in ranks}
+    glob_arg = None if s.global_is_null else tot
+    if s.W > 1 and not s.causal:
+        si = WL.draft_slot_inputs(wl)
+        slot_jobs = [(torch.from_numpy(si["ctx_positions"]).to(dev), torch.from_numpy(si["ctx_num_valid"]).to(dev)),
+                     (torch.from_numpy(si["query_positions"]).to(dev), None)]
+    else:
+        newpos = (wl.tot[:, None] - s.Q + np.arange(s.Q)[None, :]).astype(np.int64)
+        slot_jobs = [(torch.from_numpy(newpos).to(dev), None)]
+    max_seq = {r: int(wl.seq_lens[r].max()) for r in ranks}
+    outs = {r: torch.empty((s.B * s.Q, s.H, 512), dtype=torch.bfloat16, device=dev) for r in ranks}
+    lses = {r: torch.empty((s.B * s.Q, s.H), dtype=torch.float32, device=dev) for r in ranks}
+    ws = {r: torch.empty((max(mla.mla_decode_workspace_size(s.B, s.Q, s.H, max_seq[r]), 1),),
+                         dtype=torch.uint8, device=dev) for r in ranks}
+    merged = (torch.empty((s.B * s.Q, s.H, 512), dtype=torch.bfloat16, device=dev),
+              torch.empty((s.B * s.Q, s.H), dtype=torch.float32, device=dev))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def step(i, evs=None):
+        rep = i % replicas
+        for r in ranks:
+            for pos, nv in slot_jobs:
+                mla.cp_local_slot(pos, bt, s.block_size, s.W, r, nv)
+            if evs is not None:
+                a, b_ = evs.pop()
+                mla.profile_attention_events(a, b_)
+            mla.mla_decode(q, pools[r][rep], bt, seq[r], glob_arg, s.W, r, None, s.causal, s.scale, s.lse_base,
+                           max_seq_len=max_seq[r], out=outs[r], lse=lses[r], workspace=ws[r])
+        if evs is not None:
+            mla.profile_attention_events(None, None)
+        if s.W > 1 and len(ranks) == s.W:
+            mla.mla_merge_lse([outs[r] for r in ranks], [lses[r] for r in ranks], s.lse_base,
+                              out=merged[0], lse=merged[1])
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    n_launch = args.steps * len(ranks)
+    pairs = [(hip.event(), hip.event()) for _ in range(n_launch)]
+    todo = list(reversed(pairs))
+    t_start, t_stop = hip.event(), hip.event()
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    hip.record(t_start, stream)
+    for i in range(args.steps):
+        step(i, todo)
+    hip.record(t_stop, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = hip.elapsed_ms(t_start, t_stop)
+    attn_ms = [hip.elapsed_ms(a, b_) for a, b_ in pairs]
+    for a, b_ in pairs:
+        hip.destroy(a)
+        hip.destroy(b_)
+    ms_per_step = total_ms / args.steps
+    avg_attn_ms = sum(attn_ms) / len(attn_ms)
+    log(f"{ms_per_step:.4f} ms/step (wall {wall / args.steps * 1e3:.4f}), attention kernel avg {avg_attn_ms:.4f} ms")
+
+    work = [rank_work(wl, r) for r in ranks]
+    step_flops = sum(w["flops"] for w in work)
+    step_kv = sum(w["kv_bytes"] for w in work)
+    step_alg_bytes = sum(w["kv_bytes"] + w["q_bytes"] + w["bt_bytes"] + w["out_bytes"] + w["lse_bytes"] for w in work)
+    tflops = step_flops / (ms_per_step * 1e-3) / 1e12
+    kv_gbps = step_kv / (ms_per_step * 1e-3) / 1e9
+    # per launch of the attention kernel: it reads KV, Q and the block table
+    launch_bytes = sum(w["kv_bytes"] + w["q_bytes"] + w["bt_bytes"] for w in work) / len(ranks)
+    launch_flops = step_flops / len(ranks)
+    mem_bound = args.config in (1, 2)
+    if mem_bound:
+        achieved = launch_bytes / (avg_attn_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
+        unit, value = "GB/s", kv_gbps
+    else:
+        achieved = launch_flops / (avg_attn_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        unit, value = "TFLOP/s", tflops
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"traffic_config{args.config}.json")
+    if os.path.exists(tfile):
+        t = json.load(open(tfile))
+        if t.get("source_hash") == source_hash():
+            traffic = t.get("bytes_per_launch")
+    roof["traffic"] = traffic
+
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": spec.name, "batch": s.B, "heads": s.H, "q_len": s.Q, "causal": s.causal,
+                   "cp_world": s.W, "ranks": ranks, "block_size": s.block_size, "kv_replicas": replicas},
+        "tflops": round(tflops, 3), "kv_gbps": round(kv_gbps, 1),
+        "alg_bytes_per_step": int(step_alg_bytes), "flops_per_step": int(step_flops),
+        "attention_kernel_ms": round(avg_attn_ms, 5), "source_hash": source_hash(),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on a bounded sample")
+        line["cpu_baseline"] = cpu_baseline(wl, ranks, unit)
+    else:
+        line["cpu_baseline"] = None
+    txt = json.dumps(line)
+    print(txt, flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(txt + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -24,6 +24,7 @@ __all__ = [
     "D_QK", "D_V", "PAD_SLOT_ID", "LSE_BASE_E", "LSE_BASE_2", "MLAError",
     "library_path", "load_library", "exported_symbols",
     "mla_decode", "mla_decode_workspace_size", "mla_merge_lse", "cp_local_slot",
+    "profile_attention_events",
 ]
 
 D_QK = 576
@@ -46,6 +47,7 @@ _SIGNATURES = [
                         ctypes.c_float, _I, _P, _P, _P, ctypes.c_size_t, _P]),
     ("mla_merge_lse", _I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
     ("cp_local_slot", _I, [_P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, _P]),
+    ("mla_profile_attention_events", _I, [_P, _P]),
 ]
 
 
@@ -102,6 +104,12 @@ def _need(t: torch.Tensor, name: str, dtype, dim: Optional[int] = None) -> None:
 
 def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def profile_attention_events(start: Optional[int], stop: Optional[int]) -> None:
+    """Record raw hipEvent_t handles around the attention kernel of following
+    mla_decode calls of this thread (None, None to stop)."""
+    _check(load_library().mla_profile_attention_events(start, stop))
 
 
 def mla_decode_workspace_size(B: int, q_len: int, H: int, max_seq_len: int) -> int:

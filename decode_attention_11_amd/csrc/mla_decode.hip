@@ -396,7 +396,17 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus) {
   return p;
 }
 
+thread_local hipEvent_t tl_prof_start = nullptr;
+thread_local hipEvent_t tl_prof_stop = nullptr;
+
 }  // namespace
+
+extern "C" int mla_profile_attention_events(hipEvent_t start, hipEvent_t stop) {
+  if ((start == nullptr) != (stop == nullptr)) return MLA_ERR_INVALID_ARG;
+  tl_prof_start = start;
+  tl_prof_stop = stop;
+  return MLA_OK;
+}
 
 extern "C" size_t mla_decode_workspace_size(int B, int q_len, int H, int max_seq_len) {
   if (B <= 0 || q_len < 1 || H < 1 || max_seq_len < 0) return 0;
@@ -440,7 +450,9 @@ extern "C" int mla_decode(const void* q, const void* kv_cache, const int32_t* bl
   a.lse = lse;
 
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, a);
+  if (tl_prof_start) (void)hipEventRecord(tl_prof_start, stream);
   hipLaunchKernelGGL(attn_r16_kernel, dim3(p.G), dim3(256), 0, stream, a);
+  if (tl_prof_stop) (void)hipEventRecord(tl_prof_stop, stream);
   hipLaunchKernelGGL(combine_kernel<R16_ROWS>, dim3(B * p.n_rt), dim3(256), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;

@@ -117,6 +117,16 @@ int mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
                hipStream_t stream);
 
 /*
+ * Profiling aid (not part of the computation): for the calling host thread,
+ * record `start` just before and `stop` just after the split-KV attention
+ * kernel of each following mla_decode call, on that call's stream.  Pass two
+ * NULLs to stop.  The events are created and owned by the caller; each call
+ * re-records them, so a caller timing several calls sets a fresh pair before
+ * each.  Returns MLA_ERR_INVALID_ARG if exactly one of them is NULL.
+ */
+int mla_profile_attention_events(hipEvent_t start, hipEvent_t stop);
+
+/*
  * Merge partial attention results of disjoint key sets (the ranks' shards)
  * by their LSE (PR #54012 page, implementation breakdown: the CP path returns
  * a natural-log LSE and the bases must agree before the cross-rank merge;

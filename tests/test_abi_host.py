@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["mla_status_string", "mla_decode_workspace_size", "mla_decode",
-                                           "mla_merge_lse", "cp_local_slot"])
+                                           "mla_merge_lse", "cp_local_slot", "mla_profile_attention_events"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -109,3 +109,10 @@ def test_slot_rejects_bad_arguments(bad):
 
 def test_slot_empty_is_a_noop():
     assert _slot(B=0, pos=None, bt=None, slots=None) == 0
+
+
+def test_profile_events_need_both_or_neither():
+    lib = mla.load_library()
+    assert lib.mla_profile_attention_events(1, None) == 1
+    assert lib.mla_profile_attention_events(None, 1) == 1
+    assert lib.mla_profile_attention_events(None, None) == 0
