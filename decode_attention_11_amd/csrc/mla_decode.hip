@@ -18,15 +18,17 @@
 // (PR #54012 page, implementation breakdown: the non-DCP call keeps its
 // multi-CTA KV counter buffer); the balanced range split is this library's.
 //
-// Kernel family R16 (this file): 16 rows per tile; four waves of a
-// workgroup take turns over 16-key subtiles of the piece, each keeping its
-// own online-softmax state for the 16 rows, and the four states are merged
-// in LDS at the end of the piece.  Scores are S^T = K * Q^T on
-// v_mfma_f32_16x16x32_bf16 (K rows as the A operand straight from HBM into
-// registers, Q^T resident in registers), so each lane holds 4 keys of one
-// row; P*V is O^T += V^T * P^T on v_mfma_f32_16x16x16_bf16 with V^T read
+// Kernel family M16 (this file): 16 rows per tile, for single-token decode
+// with up to 16 heads, the HBM-bound case.  Eight waves of a workgroup take
+// turns over 16-key subtiles of a piece, each keeping its own online-softmax
+// state for the 16 rows, merged in LDS at the end of the piece.  Scores are
+// S^T = K * Q^T on v_mfma_f32_16x16x32_bf16 (K rows as the A operand straight
+// from HBM into registers, Q^T read from LDS), so each lane holds 4 keys of
+// one row; P*V is O^T += V^T * P^T on v_mfma_f32_16x16x16_bf16 with V^T read
 // from LDS by ds_read_b64_tr_b16, so P never leaves registers and each lane
-// owns one row of O^T.
+// owns one row of O^T.  The running max is a reference that only moves when
+// a row's max grows by more than 2^8, so the accumulators are rarely
+// rescaled (the exponentials stay <= 256, exact in fp32 and bf16 range).
 #include <hip/hip_runtime.h>
 #include <cmath>
 #include <cstdint>
@@ -48,6 +50,7 @@ struct DecodeArgs {
   const int32_t* glob;     // [B] or null
   int B, Q, H, R;          // R = Q*H rows per request
   int num_blocks, bs, max_blocks;
+  int bs_shift;            // log2(bs) when bs is a power of two, else -1
   int W, rank, causal;
   float scale_log2;        // softmax scale times log2(e)
   int lse_base;
@@ -69,233 +72,327 @@ __device__ __forceinline__ int request_keys(const DecodeArgs& a, int b) {
   return row_bound(seq, request_tot(a, b, seq), a.Q, a.Q - 1, a.W, a.rank, a.causal);
 }
 
-// ---------------------------------------------------------------- plan
-// prefix[b] = sum over earlier requests of n_rt * keys: one block-wide scan.
-__global__ __launch_bounds__(256) void plan_kernel(DecodeArgs a) {
-  __shared__ int64_t wsum[4];
-  __shared__ int64_t carry;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) { carry = 0; a.prefix[0] = 0; }
+// ---------------------------------------------------------------- in-kernel plan
+// Every partial workgroup recomputes the request offsets itself (a block
+// scan over seq_lens), so no separate planning launch is needed; workgroup 0
+// also stores them for the combine kernel.
+template <int NT>
+__device__ __forceinline__ int64_t block_sum_i64(int64_t v, int64_t* s_red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
   __syncthreads();
-  for (int base = 0; base < a.B; base += 256) {
-    const int b = base + tid;
-    int64_t v = (b < a.B) ? (int64_t)a.n_rt * request_keys(a, b) : 0;
-    for (int off = 1; off < 64; off <<= 1) {
-      int64_t y = __shfl_up(v, off, 64);
-      if (lane >= off) v += y;
-    }
-    if (lane == 63) wsum[wave] = v;
-    __syncthreads();
-    int64_t add = carry;
-    for (int w = 0; w < wave; ++w) add += wsum[w];
-    if (b < a.B) a.prefix[b + 1] = add + v;
-    __syncthreads();
-    if (tid == 255) carry = add + v;
-    __syncthreads();
-  }
+  if (lane == 0) s_red[wave] = v;
+  __syncthreads();
+  int64_t t = 0;
+  for (int w = 0; w < NT / 64; ++w) t += s_red[w];
+  return t;
 }
 
-// ---------------------------------------------------------------- R16 partial
-constexpr int R16_ROWS = 16;
-constexpr int R16_SUB = 16;          // keys per subtile
-constexpr int R16_VROW = 1056;       // LDS bytes per key row of a V stage (1024 + 32 pad)
-constexpr int R16_VSTAGE = R16_SUB * R16_VROW;
-constexpr int R16_MRG_LD = 17;       // padded row stride of the LDS merge buffer [dv][row]
-constexpr int R16_SLOT = R16_ROWS * D_V + 2 * R16_ROWS;  // floats per partial slot
-constexpr int R16_SMEM = 4 * R16_VSTAGE;                 // V stages; the merge buffer aliases them
+template <int NT>
+__device__ __forceinline__ int64_t block_incl_scan_i64(int64_t v, int64_t* s_red, int64_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t y = __shfl_up(v, off, 64);
+    if (lane >= off) v += y;
+  }
+  __syncthreads();
+  if (lane == 63) s_red[wave] = v;
+  __syncthreads();
+  int64_t before = 0;
+  total = 0;
+  for (int w = 0; w < NT / 64; ++w) {
+    const int64_t x = s_red[w];
+    if (w < wave) before += x;
+    total += x;
+  }
+  return before + v;
+}
 
-static_assert(D_V * R16_MRG_LD * 4 <= R16_SMEM, "merge buffer must fit in the V stages");
+// ---------------------------------------------------------------- M16 partial
+// Memory-bound family: up to 16 rows per request (single-token decode with
+// up to 16 heads and similar).  256 threads = 4 waves per workgroup (one per
+// SIMD), one workgroup per CU; the waves take turns over 16-key subtiles of a
+// piece.  Each wave keeps Q^T (72 VGPRs) and two key subtiles (2 x 72 VGPRs)
+// in registers and the 16 x 512 fp32 O^T accumulator in MFMA registers; the
+// block-table entry of a subtile is read two subtiles ahead and the key rows
+// one subtile ahead, so no wait ever drains the prefetch.
+constexpr int M16_THREADS = 256;
+constexpr int M16_WAVES = 4;
+constexpr int M16_ROWS = 16;
+constexpr int M16_SUB = 16;          // keys per subtile
+constexpr int M16_VROW = 1056;       // LDS bytes per key row of a V stage (1024 + 32 pad: conflict-free tr reads)
+constexpr int M16_VSTAGE = M16_SUB * M16_VROW;
+constexpr int M16_QBYTES = 18 * 64 * 16;                   // Q^T fragments of the 16 rows
+constexpr int M16_MRG_LD = 17;       // padded row stride of the merge buffer [dv][row]
+constexpr int M16_SMEM = M16_WAVES * M16_VSTAGE;           // V stages; the merge buffer aliases them
+constexpr float M16_RESCALE_LOG2 = 8.f;                    // keep exponentials <= 2^8 between rescales
 
-struct R16Piece {
-  int b, rt, k0, k1;
+static_assert(D_V * M16_MRG_LD * 4 <= M16_SMEM, "merge buffer must fit in the V stages");
+
+// A zero latent row: lanes whose key is outside the piece (or has an invalid
+// block id) read it instead, so every lane issues the same loads and the V
+// rows of masked keys are exact zeros (0 * NaN garbage would poison P*V).
+__device__ __attribute__((aligned(64))) const uint4 kZeroRow[ROW_BYTES / 16] = {};
+
+__device__ __forceinline__ int block_of(const DecodeArgs& a, int t) {
+  return a.bs_shift >= 0 ? (t >> a.bs_shift) : t / a.bs;
+}
+
+// Raw block-table entry covering local key t.  The read is unconditional
+// (index clamped into the row) and its value is only inspected by key_row,
+// a loop iteration later: a load inside a branch, or a select right after
+// it, would make the compiler wait for every load in flight.
+__device__ __forceinline__ int key_block(const DecodeArgs& a, const int32_t* btr, int t) {
+  const int vb = block_of(a, t);
+  return gload_i32(btr + (vb < a.max_blocks ? vb : a.max_blocks - 1));
+}
+
+// Row address of local key t given its block-table entry; the zero row when
+// t is outside the piece, past the table width, or the block id is invalid.
+__device__ __forceinline__ const uint8_t* key_row(const DecodeArgs& a, int blk, int t, int k1) {
+  const int vb = block_of(a, t);
+  if (t >= k1 || vb >= a.max_blocks || (unsigned)blk >= (unsigned)a.num_blocks)
+    return reinterpret_cast<const uint8_t*>(kZeroRow);
+  return a.kv + ((int64_t)blk * a.bs + (t - vb * a.bs)) * ROW_BYTES;
+}
+
+// Loads one subtile's 16 keys as MFMA A-operand fragments: lane (li, g)
+// holds 16-byte chunks 4*kk + g of its key's row.
+__device__ __forceinline__ void m16_load(bf16x8 (&kb)[18], const uint8_t* rowp, int g) {
+  rowp += g * 16;
+#pragma unroll
+  for (int kk = 0; kk < 18; ++kk) kb[kk] = gload_bf16x8(rowp + kk * 64);
+}
+
+struct M16State {
+  f32x4 o[32];
+  float m_ref, l_part;
 };
 
-// Loads the 16 keys of one subtile as MFMA A-operand fragments: lane (li, g)
-// gets key k0 + 16*s + li, 16-byte chunks 4*kk + g of its 576-wide row.
-__device__ __forceinline__ void r16_load(bf16x8 (&kb)[18], const DecodeArgs& a, const int32_t* btr,
-                                         int k0, int k1, int nsub, int s, int li, int g) {
-  const int t = k0 + R16_SUB * s + li;
-  bool valid = (s < nsub) && (t < k1);
-  const uint8_t* rowp = nullptr;
-  if (valid) {
-    const int vb = t / a.bs;
-    const int blk = (vb < a.max_blocks) ? btr[vb] : -1;
-    valid = (unsigned)blk < (unsigned)a.num_blocks;
-    rowp = a.kv + ((int64_t)blk * a.bs + (t - vb * a.bs)) * ROW_BYTES;
-  }
-  if (valid) {
-#pragma unroll
-    for (int kk = 0; kk < 18; ++kk) kb[kk] = load_bf16x8(rowp + (4 * kk + g) * 16);
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < 18; ++kk) kb[kk] = zero_bf16x8();
-  }
-}
-
-__device__ __forceinline__ void r16_compute(const bf16x8 (&kb)[18], const bf16x8 (&qf)[18], f32x4 (&o)[32],
-                                            float& m, float& l, uint8_t* vs, float scale_log2,
-                                            int kbase, int k1, int nrow, int li, int g) {
-  // S^T[t][row] for the 16 keys of the subtile: lane holds t = 4g+i, row = li.
+// One 16-key subtile: S^T = K Q^T, online softmax with a lazily moved
+// reference max, O^T += V^T P^T.
+__device__ __forceinline__ void m16_compute(M16State& st, const bf16x8 (&kb)[18], const uint8_t* q_lds,
+                                            uint8_t* vs, float scale_log2, int kbase, int k1, int nrow,
+                                            int lane, int li, int g) {
+  // S^T[t][row]: lane holds keys t = kbase + 4g + i of row li.  Q^T comes
+  // from LDS every subtile (the compiler barrier keeps the reads here
+  // instead of hoisting them into 72 registers that would then spill).
+  asm volatile("" ::: "memory");
   f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < 18; kk += 2) {
-    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qf[kk], sa, 0, 0, 0);
-    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk + 1], qf[kk + 1], sb, 0, 0, 0);
+    const bf16x8 qa = *reinterpret_cast<const bf16x8*>(q_lds + (kk * 64 + lane) * 16);
+    const bf16x8 qb = *reinterpret_cast<const bf16x8*>(q_lds + ((kk + 1) * 64 + lane) * 16);
+    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qa, sa, 0, 0, 0);
+    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk + 1], qb, sb, 0, 0, 0);
   }
-  // the V part (first 512 columns) of this subtile goes to LDS for the transposed read
+  // the V part (first 512 columns) goes to this wave's LDS stage for the transposed read
 #pragma unroll
   for (int kk = 0; kk < 16; ++kk)
-    *reinterpret_cast<bf16x8*>(vs + li * R16_VROW + (4 * kk + g) * 16) = kb[kk];
+    *reinterpret_cast<bf16x8*>(vs + li * M16_VROW + (4 * kk + g) * 16) = kb[kk];
 
   float p[4];
   float mx = NEG_INF;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int t = kbase + 4 * g + i;
-    float v = (sa[i] + sb[i]) * scale_log2;
-    v = (t < k1 && t < nrow) ? v : NEG_INF;
+    const float v = (t < k1 && t < nrow) ? (sa[i] + sb[i]) * scale_log2 : NEG_INF;
     p[i] = v;
     mx = fmaxf(mx, v);
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  const float mnew = fmaxf(m, mx);
-  float alpha = 1.f;
-  if (mnew != NEG_INF) {
-    alpha = fast_exp2(m - mnew);
+  // move the reference only when some row's max grew by more than 2^8 over it
+  if (__ballot(mx > st.m_ref + M16_RESCALE_LOG2) != 0) {
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (mx > st.m_ref + M16_RESCALE_LOG2) {
+      const float alpha = fast_exp2(st.m_ref - mx);
+      st.l_part *= alpha;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(p[i] - mnew);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = 0.f;
+      for (int mt = 0; mt < 32; ++mt) st.o[mt] *= alpha;
+      st.m_ref = mx;
+    }
   }
-  float rs = (p[0] + p[1]) + (p[2] + p[3]);
-  rs += __shfl_xor(rs, 16, 64);
-  rs += __shfl_xor(rs, 32, 64);
-  l = l * alpha + rs;
-  m = mnew;
-  const bf16x4 pf = to_bf16x4(p[0], p[1], p[2], p[3]);
-  // O^T[dv][row] += V^T[dv][t] * P^T[t][row]; the tr read gives lane (li, g)
-  // V[4g+e][16*mt+li] for e = 0..3 when lane (q, g) points at row 4g+q/4,
-  // columns 16*mt + 4*(q%4).
-  const uint8_t* vread = vs + (4 * g + (li >> 2)) * R16_VROW + (li & 3) * 8;
 #pragma unroll
-  for (int mt = 0; mt < 32; ++mt) {
-    o[mt] *= alpha;
-    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4*)(vread + mt * 32));
-    o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, v), pf, o[mt], 0, 0, 0);
+  for (int i = 0; i < 4; ++i) {
+    p[i] = (p[i] == NEG_INF) ? 0.f : fast_exp2(p[i] - st.m_ref);
+    st.l_part += p[i];
+  }
+  const bf16x4 pf = to_bf16x4(p[0], p[1], p[2], p[3]);
+  // O^T[dv][row] += V^T[dv][t] P^T[t][row]; the transposed read gives lane
+  // (li, g) V[4g+e][16*mt+li] when lane (q, g) points at row 4g+q/4,
+  // columns 16*mt + 4*(q%4)
+  const uint8_t* vread = vs + (4 * g + (li >> 2)) * M16_VROW + (li & 3) * 8;
+#pragma unroll
+  for (int mt0 = 0; mt0 < 32; mt0 += 8) {
+    i16x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vread + (mt0 + j) * 32));
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      st.o[mt0 + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, v[j]), pf,
+                                                               st.o[mt0 + j], 0, 0, 0);
   }
 }
 
-__global__ __launch_bounds__(256, 1) void attn_r16_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[R16_SMEM];
-  __shared__ float mrg_m[4][R16_ROWS];
-  __shared__ float mrg_l[R16_ROWS];
+__global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[M16_SMEM];
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[M16_QBYTES];
+  __shared__ int64_t s_red[M16_WAVES];
+  __shared__ int64_t s_excl[M16_THREADS];
+  __shared__ int s_first, s_last;
+  __shared__ float mrg_m[M16_WAVES][M16_ROWS];
+  __shared__ float mrg_l[M16_ROWS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
-  const int64_t T = a.prefix[a.B];
   const int w = blockIdx.x;
-  int64_t u = (int64_t)w * T / a.G;
-  const int64_t uend = (int64_t)(w + 1) * T / a.G;
-  if (u >= uend) return;
-
-  // request holding unit u: the largest b with prefix[b] <= u
-  int lo = 0, hi = a.B;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.prefix[mid] <= u) lo = mid; else hi = mid;
-  }
-  int b = lo;
-  uint8_t* vs = smem + wave * R16_VSTAGE;
   float* mrg_o = reinterpret_cast<float*>(smem);
+  uint8_t* vs = smem + wave * M16_VSTAGE;
 
-  while (u < uend) {
-    const int64_t pb = a.prefix[b], pb1 = a.prefix[b + 1];
-    if (pb1 <= u) { ++b; continue; }
-    const int nb = (int)((pb1 - pb) / a.n_rt);
-    const int rt = (int)((u - pb) / nb);
-    const int k0 = (int)((u - pb) - (int64_t)rt * nb);
-    const int64_t left = uend - u;
-    const int k1 = (int)((int64_t)(nb - k0) < left ? nb : k0 + left);
+  // total units
+  int64_t T = 0;
+  for (int base = 0; base < a.B; base += M16_THREADS) {
+    const int b = base + tid;
+    T += block_sum_i64<M16_THREADS>(b < a.B ? (int64_t)a.n_rt * request_keys(a, b) : 0, s_red);
+  }
+  const int64_t u0 = (int64_t)w * T / a.G, u1 = (int64_t)(w + 1) * T / a.G;
 
-    // this lane's row (as the S^T / O^T column)
-    const int my_row = rt * R16_ROWS + li;
-    const bool row_ok = my_row < a.R;
-    const int seq = a.seq_lens[b];
-    const int nrow = row_ok ? row_bound(seq, request_tot(a, b, seq), a.Q, my_row / a.H, a.W, a.rank, a.causal) : 0;
-
-    bf16x8 qf[18];
-    {
-      const uint8_t* qrow = a.q + ((int64_t)b * a.R + (row_ok ? my_row : 0)) * ROW_BYTES;
-#pragma unroll
-      for (int kk = 0; kk < 18; ++kk) qf[kk] = row_ok ? load_bf16x8(qrow + (4 * kk + g) * 16) : zero_bf16x8();
+  int64_t carry = 0;
+  for (int base = 0; base < a.B; base += M16_THREADS) {
+    const int b = base + tid;
+    const int64_t x = b < a.B ? (int64_t)a.n_rt * request_keys(a, b) : 0;
+    int64_t chunk_total;
+    const int64_t incl = block_incl_scan_i64<M16_THREADS>(x, s_red, chunk_total) + carry;
+    const int64_t excl = incl - x;
+    if (w == 0 && b < a.B) {
+      a.prefix[b + 1] = incl;
+      if (b == 0) a.prefix[0] = 0;
     }
-    f32x4 o[32];
-#pragma unroll
-    for (int mt = 0; mt < 32; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = NEG_INF, l = 0.f;
-
-    const int32_t* btr = a.bt + (int64_t)b * a.max_blocks;
-    const int nsub = (k1 - k0 + R16_SUB - 1) / R16_SUB;
-    bf16x8 kb0[18], kb1[18];
-    r16_load(kb0, a, btr, k0, k1, nsub, wave, li, g);
-    r16_load(kb1, a, btr, k0, k1, nsub, wave + 4, li, g);
-    for (int s = wave; s < nsub; s += 8) {
-      r16_compute(kb0, qf, o, m, l, vs, a.scale_log2, k0 + R16_SUB * s, k1, nrow, li, g);
-      r16_load(kb0, a, btr, k0, k1, nsub, s + 8, li, g);
-      if (s + 4 < nsub) {
-        r16_compute(kb1, qf, o, m, l, vs, a.scale_log2, k0 + R16_SUB * (s + 4), k1, nrow, li, g);
-        r16_load(kb1, a, btr, k0, k1, nsub, s + 12, li, g);
-      }
+    s_excl[tid] = excl;
+    if (tid == 0) { s_first = 0x7fffffff; s_last = -1; }
+    __syncthreads();
+    if (x > 0 && excl < u1 && incl > u0) {
+      atomicMin(&s_first, tid);
+      atomicMax(&s_last, tid);
     }
+    __syncthreads();
+    const int first = s_first, last = s_last;
+    carry += chunk_total;
 
-    // merge the four waves' states of the 16 rows in LDS, in a fixed wave
-    // order so that the result does not depend on timing
-    __syncthreads();
-    if (g == 0) mrg_m[wave][li] = m;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(mrg_m[0][li], mrg_m[1][li]), fmaxf(mrg_m[2][li], mrg_m[3][li]));
-    const float f = (m == NEG_INF) ? 0.f : fast_exp2(m - M);
-    for (int wv = 0; wv < 4; ++wv) {
-      if (wave == wv) {
+    for (int i = first; i <= last; ++i) {
+      const int bb = __builtin_amdgcn_readfirstlane(base + i);
+      const int64_t pb = s_excl[i];
+      const int nb = __builtin_amdgcn_readfirstlane(request_keys(a, bb));
+      const int seq = __builtin_amdgcn_readfirstlane(a.seq_lens[bb]);
+      const int tot = __builtin_amdgcn_readfirstlane(request_tot(a, bb, seq));
+      const int32_t* btr = a.bt + (int64_t)bb * a.max_blocks;
+      const int64_t lo = u0 > pb ? u0 - pb : 0;                       // first unit of the request in range
+      const int64_t hi = (u1 - pb) < (int64_t)a.n_rt * nb ? u1 - pb : (int64_t)a.n_rt * nb;
+      for (int rt = (int)(lo / nb); (int64_t)rt * nb < hi; ++rt) {
+        const int k0 = __builtin_amdgcn_readfirstlane((int)((int64_t)rt * nb < lo ? lo - (int64_t)rt * nb : 0));
+        const int k1 = __builtin_amdgcn_readfirstlane((int)((int64_t)(rt + 1) * nb < hi ? nb : hi - (int64_t)rt * nb));
+        // ---- one piece: rows [16 rt, 16 rt + 16) of request bb, keys [k0, k1)
+        const int my_row = rt * M16_ROWS + li;
+        const bool row_ok = my_row < a.R;
+        const int nrow = row_ok ? row_bound(seq, tot, a.Q, my_row / a.H, a.W, a.rank, a.causal) : 0;
+        // Q^T fragments of the 16 rows into LDS, laid out [kk][g][row] x 16 bytes
+        for (int e = tid; e < 18 * 64; e += M16_THREADS) {
+          const int kk = e >> 6, gg = (e >> 4) & 3, rr = e & 15;
+          const int row = rt * M16_ROWS + rr;
+          bf16x8 v = zero_bf16x8();
+          if (row < a.R) v = gload_bf16x8(a.q + ((int64_t)bb * a.R + row) * ROW_BYTES + (4 * kk + gg) * 16);
+          *reinterpret_cast<bf16x8*>(q_lds + e * 16) = v;
+        }
+        __syncthreads();
+        M16State st;
 #pragma unroll
-        for (int mt = 0; mt < 32; ++mt)
+        for (int mt = 0; mt < 32; ++mt) st.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st.m_ref = NEG_INF;
+        st.l_part = 0.f;
+        const int nsub = (k1 - k0 + M16_SUB - 1) / M16_SUB;
+        // wave w takes subtiles w, w+4, w+8, ...; lane li loads key k0 + 16*s + li
+        constexpr int STEP = M16_WAVES * M16_SUB;
+        int t0 = k0 + M16_SUB * wave + li;
+        bf16x8 kb0[18], kb1[18];
+        m16_load(kb0, key_row(a, key_block(a, btr, t0), t0, k1), g);
+        m16_load(kb1, key_row(a, key_block(a, btr, t0 + STEP), t0 + STEP, k1), g);
+        int blk2 = key_block(a, btr, t0 + 2 * STEP);
+        int blk3 = key_block(a, btr, t0 + 3 * STEP);
+        // the scheduling barriers pin each prefetch right after the compute
+        // that frees its registers (left alone, the scheduler sinks the loads
+        // under the other buffer's compute and only one subtile is in flight)
+        for (int s = wave; s < nsub; s += 2 * M16_WAVES) {
+          m16_compute(st, kb0, q_lds, vs, a.scale_log2, k0 + M16_SUB * s, k1, nrow, lane, li, g);
+          __builtin_amdgcn_sched_barrier(0);
+          m16_load(kb0, key_row(a, blk2, t0 + 2 * STEP, k1), g);
+          blk2 = key_block(a, btr, t0 + 4 * STEP);
+          __builtin_amdgcn_sched_barrier(0);
+          // unconditional even past the last subtile (its keys are all masked):
+          // a conditional half would make every wait count conservative
+          m16_compute(st, kb1, q_lds, vs, a.scale_log2, k0 + M16_SUB * (s + M16_WAVES), k1, nrow, lane, li, g);
+          __builtin_amdgcn_sched_barrier(0);
+          m16_load(kb1, key_row(a, blk3, t0 + 3 * STEP, k1), g);
+          blk3 = key_block(a, btr, t0 + 5 * STEP);
+          __builtin_amdgcn_sched_barrier(0);
+          t0 += 2 * STEP;
+        }
+        float l_row = st.l_part;
+        l_row += __shfl_xor(l_row, 16, 64);
+        l_row += __shfl_xor(l_row, 32, 64);
+
+        // merge the waves' states of the 16 rows in LDS, in a fixed wave order
+        __syncthreads();
+        if (g == 0) mrg_m[wave][li] = st.m_ref;
+        __syncthreads();
+        float M = NEG_INF;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float* dst = &mrg_o[(16 * mt + 4 * g + i) * R16_MRG_LD + li];
-            *dst = (wv == 0 ? 0.f : *dst) + o[mt][i] * f;
+        for (int wv = 0; wv < M16_WAVES; ++wv) M = fmaxf(M, mrg_m[wv][li]);
+        const float f = (st.m_ref == NEG_INF) ? 0.f : fast_exp2(st.m_ref - M);
+        for (int wv = 0; wv < M16_WAVES; ++wv) {
+          if (wave == wv) {
+#pragma unroll
+            for (int mt = 0; mt < 32; ++mt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                float* dst = &mrg_o[(16 * mt + 4 * g + i) * M16_MRG_LD + li];
+                *dst = (wv == 0 ? 0.f : *dst) + st.o[mt][i] * f;
+              }
+            if (g == 0) mrg_l[li] = (wv == 0 ? 0.f : mrg_l[li]) + l_row * f;
           }
-        if (g == 0) mrg_l[li] = (wv == 0 ? 0.f : mrg_l[li]) + l * f;
+          __syncthreads();
+        }
+        const int slot = w + bb * a.n_rt + rt;
+        float* ps = a.partials + (int64_t)slot * (M16_ROWS * D_V + 2 * M16_ROWS);
+        for (int e = tid; e < D_V * M16_ROWS; e += M16_THREADS)
+          ps[e] = mrg_o[(e >> 4) * M16_MRG_LD + (e & 15)];
+        if (tid < M16_ROWS) {
+          float Mt = NEG_INF;
+          for (int wv = 0; wv < M16_WAVES; ++wv) Mt = fmaxf(Mt, mrg_m[wv][tid]);
+          ps[D_V * M16_ROWS + tid] = Mt;
+          ps[D_V * M16_ROWS + M16_ROWS + tid] = mrg_l[tid];
+        }
+        __syncthreads();
       }
-      __syncthreads();
-    }
-    const int slot = w + b * a.n_rt + rt;
-    float* ps = a.partials + (int64_t)slot * R16_SLOT;
-    for (int e = tid; e < D_V * R16_ROWS; e += 256)
-      ps[e] = mrg_o[(e >> 4) * R16_MRG_LD + (e & 15)];
-    if (tid < R16_ROWS) {
-      const float Mt = fmaxf(fmaxf(mrg_m[0][tid], mrg_m[1][tid]), fmaxf(mrg_m[2][tid], mrg_m[3][tid]));
-      ps[D_V * R16_ROWS + tid] = Mt;
-      ps[D_V * R16_ROWS + R16_ROWS + tid] = mrg_l[tid];
     }
     __syncthreads();
-    u += k1 - k0;
   }
 }
 
 // ---------------------------------------------------------------- combine
-// One workgroup per (request, row tile): merge the partial slots of the
-// workgroups that covered it, write bf16 out and the LSE.
+// Grid: (request, row tile) groups x 8 slices of 64 output columns.  Merges
+// the partial slots of the workgroups that covered the group and writes bf16
+// out and (slice 0) the LSE.  Groups no workgroup covered (no visible keys)
+// get out = 0, lse = -inf.
 template <int ROWS>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
-  constexpr int TPR = 256 / ROWS;          // threads per row
-  constexpr int DV_PER = D_V / TPR;        // output columns per thread
+  constexpr int SLICE = 64;                       // output columns per workgroup
+  constexpr int PER = ROWS * SLICE / 256;         // outputs per thread
   constexpr int SLOT = ROWS * D_V + 2 * ROWS;
-  const int grp = blockIdx.x;
+  const int grp = blockIdx.x >> 3, slice = blockIdx.x & 7;
   const int b = grp / a.n_rt, rt = grp - b * a.n_rt;
-  const int row = threadIdx.x % ROWS, part = threadIdx.x / ROWS;
+  const int row = threadIdx.x % ROWS;
+  const int col0 = slice * SLICE + (threadIdx.x / ROWS) * PER;
   const int row_idx = rt * ROWS + row;
   if (row_idx >= a.R) return;
   const int64_t T = a.prefix[a.B];
@@ -303,52 +400,39 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int nb = (int)((pb1 - pb) / a.n_rt);
   int w0 = 0, w1 = -1;
   if (nb > 0) {
-    const int64_t u0 = pb + (int64_t)rt * nb;
-    w0 = range_owner(u0, T, a.G);
-    w1 = range_owner(u0 + nb - 1, T, a.G);
+    const int64_t ustart = pb + (int64_t)rt * nb;
+    w0 = range_owner(ustart, T, a.G);
+    w1 = range_owner(ustart + nb - 1, T, a.G);
   }
   float M = NEG_INF;
-  for (int w = w0; w <= w1; ++w) {
-    const float* ps = a.partials + (int64_t)(w + grp) * SLOT;
-    M = fmaxf(M, ps[ROWS * D_V + row]);
-  }
+  for (int w = w0; w <= w1; ++w) M = fmaxf(M, a.partials[(int64_t)(w + grp) * SLOT + ROWS * D_V + row]);
   const int64_t orow = (int64_t)b * a.R + row_idx;
-  uint16_t* op = a.out + orow * D_V;
+  uint16_t* op = a.out + orow * D_V + col0;
+  static_assert(PER % 4 == 0, "outputs are stored 4 columns at a time");
   if (M == NEG_INF) {
-    for (int c = 0; c < DV_PER; c += 8) {
-      uint4 z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<uint4*>(op + part * DV_PER + c) = z;
-    }
-    if (a.lse && part == 0) a.lse[orow] = NEG_INF;
+#pragma unroll
+    for (int c = 0; c < PER; c += 4) *reinterpret_cast<uint2*>(op + c) = uint2{0u, 0u};
+    if (a.lse && slice == 0 && threadIdx.x < ROWS) a.lse[orow] = NEG_INF;
     return;
   }
   float L = 0.f;
+  float acc[PER];
+#pragma unroll
+  for (int c = 0; c < PER; ++c) acc[c] = 0.f;
   for (int w = w0; w <= w1; ++w) {
     const float* ps = a.partials + (int64_t)(w + grp) * SLOT;
     const float mw = ps[ROWS * D_V + row];
     const float f = (mw == NEG_INF) ? 0.f : fast_exp2(mw - M);
     L += f * ps[ROWS * D_V + ROWS + row];
+#pragma unroll
+    for (int c = 0; c < PER; ++c) acc[c] += f * ps[(col0 + c) * ROWS + row];
   }
   const float inv = 1.f / L;
-  for (int c0 = 0; c0 < DV_PER; c0 += 8) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int w = w0; w <= w1; ++w) {
-      const float* ps = a.partials + (int64_t)(w + grp) * SLOT;
-      const float mw = ps[ROWS * D_V + row];
-      const float f = (mw == NEG_INF) ? 0.f : fast_exp2(mw - M);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[c] += f * ps[(part * DV_PER + c0 + c) * ROWS + row];
-    }
-    bf16x8 r;
-#pragma unroll
-    for (int c = 0; c < 8; c += 2) {
-      const bf16x2 pr = to_bf16x2(acc[c] * inv, acc[c + 1] * inv);
-      r[c] = pr[0];
-      r[c + 1] = pr[1];
-    }
-    *reinterpret_cast<bf16x8*>(op + part * DV_PER + c0) = r;
-  }
-  if (a.lse && part == 0) {
+  for (int c0 = 0; c0 < PER; c0 += 4)
+    *reinterpret_cast<bf16x4*>(op + c0) = to_bf16x4(acc[c0] * inv, acc[c0 + 1] * inv, acc[c0 + 2] * inv,
+                                                     acc[c0 + 3] * inv);
+  if (a.lse && slice == 0 && threadIdx.x < ROWS) {
     const float l2 = M + __log2f(L);
     a.lse[orow] = (a.lse_base == MLA_LSE_BASE_E) ? l2 * LN2 : l2;
   }
@@ -382,7 +466,7 @@ int device_cu_count() {
 Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus) {
   Plan p{};
   const int64_t R = (int64_t)q_len * H;
-  p.rows_tile = R16_ROWS;
+  p.rows_tile = M16_ROWS;
   p.n_rt = (int)((R + p.rows_tile - 1) / p.rows_tile);
   const int64_t units = (int64_t)B * p.n_rt * (max_seq_len > 0 ? max_seq_len : 1);
   int64_t G = (units + 255) / 256;  // at least 256 keys per workgroup
@@ -439,6 +523,7 @@ extern "C" int mla_decode(const void* q, const void* kv_cache, const int32_t* bl
   a.glob = causal_seqlens_global;
   a.B = B; a.Q = q_len; a.H = H; a.R = q_len * H;
   a.num_blocks = num_blocks; a.bs = block_size; a.max_blocks = max_blocks;
+  a.bs_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
   a.W = cp_world; a.rank = cp_rank; a.causal = causal;
   a.scale_log2 = scale * LOG2E;
   a.lse_base = lse_base;
@@ -449,11 +534,10 @@ extern "C" int mla_decode(const void* q, const void* kv_cache, const int32_t* bl
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
 
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, a);
   if (tl_prof_start) (void)hipEventRecord(tl_prof_start, stream);
-  hipLaunchKernelGGL(attn_r16_kernel, dim3(p.G), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(attn_m16_kernel, dim3(p.G), dim3(M16_THREADS), 0, stream, a);
   if (tl_prof_stop) (void)hipEventRecord(tl_prof_stop, stream);
-  hipLaunchKernelGGL(combine_kernel<R16_ROWS>, dim3(B * p.n_rt), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(combine_kernel<M16_ROWS>, dim3(B * p.n_rt * 8), dim3(256), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }

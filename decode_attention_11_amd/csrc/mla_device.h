@@ -34,8 +34,22 @@ __device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) 
   return __builtin_convertvector(v, bf16x4);
 }
 
+typedef __attribute__((address_space(1))) const bf16x8 global_bf16x8;
+typedef __attribute__((address_space(1))) const int32_t global_i32;
+
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint8_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// 16-byte load through the global address space (global_load_dwordx4; a
+// generic pointer would become a flat load, which also counts against the
+// LDS wait counter).
+__device__ __forceinline__ bf16x8 gload_bf16x8(const uint8_t* p) {
+  return *(global_bf16x8*)(p);
+}
+
+__device__ __forceinline__ int32_t gload_i32(const int32_t* p) {
+  return *(global_i32*)(p);
 }
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
