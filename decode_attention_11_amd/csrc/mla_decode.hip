@@ -379,11 +379,305 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
   }
 }
 
+// ---------------------------------------------------------------- R128 partial
+// Compute-bound family: more than 16 rows per request (multi-token or many
+// heads: 4 x 128 or 16 x 128 rows).  A workgroup owns 128 rows (4 waves x 32
+// rows) of one request and a key range; the 32-key tiles of the latent KV are
+// shared by the four waves through a 3-stage LDS ring filled by direct
+// global->LDS loads.  Scores S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with K
+// from LDS and Q^T in registers (144 VGPRs); each lane then holds 16 keys of
+// one row, so P^T feeds O^T += V^T P^T (V^T by ds_read_b64_tr_b16) without
+// leaving registers; O^T (32 rows x 512) lives in 256 MFMA accumulator
+// registers.  The ring's loads are issued by inline assembly and waited on
+// with explicit counts: the compiler would otherwise drain every in-flight
+// LDS load at each barrier.
+constexpr int R128_THREADS = 256;
+constexpr int R128_ROWS = 128;
+constexpr int R128_TILE = 32;                 // keys per tile
+constexpr int R128_ROWB = 1168;               // LDS bytes per key row (1152 + 16: conflict-free reads)
+constexpr int R128_DMA = 37;                  // 1 KiB load instructions per tile (32 x 1168 B rounded up)
+constexpr int R128_DMA_PER_WAVE = 10;         // ceil(37 / 4); the spare ones write a dummy area
+constexpr int R128_STAGE = R128_DMA * 1024;
+constexpr int R128_NS = 3;                    // ring stages
+constexpr int R128_BT_WIN = 1024;             // block-table entries held in LDS per sub-piece
+constexpr int R128_QREG = 28;                 // Q^T k-steps (of 16 dims) kept in registers; the rest in LDS
+constexpr int R128_QLDS = 36 - R128_QREG;
+constexpr float R128_RESCALE_LOG2 = 8.f;
+
+static_assert(R128_TILE * R128_ROWB <= R128_STAGE, "tile must fit its stage");
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+#define R128_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  // 64 lanes x 16 bytes from per-lane global addresses to lds_base + 16*lane
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(base) : "memory", "m0");
+}
+
+// Issue this wave's share of the loads of tile [ts, ts+32) into a stage.
+// Chunk o = 1024*j + 16*lane of the stage holds key o / 1168, byte o % 1168;
+// padding, keys past k1 and invalid block ids read the zero row.
+__device__ __forceinline__ void r128_issue_tile(const DecodeArgs& a, const int* bt_lds, int e0, int ts, int k1,
+                                                uint32_t stage_lds, uint32_t dummy_lds, int wave, int lane) {
+  // opaque copies: the per-lane address arithmetic below is loop-invariant
+  // and, left visible, gets hoisted out of the tile loop into ~200 registers
+  asm volatile("" : "+v"(lane));
+  const uint8_t* zero_row = reinterpret_cast<const uint8_t*>(kZeroRow);
+  asm volatile("" : "+v"(zero_row));
+#pragma unroll
+  for (int m = 0; m < R128_DMA_PER_WAVE; ++m) {
+    const int j = wave + 4 * m;
+    const int o = 1024 * j + 16 * lane;
+    const int key = o / R128_ROWB;
+    const int byte = o - key * R128_ROWB;
+    const int t = ts + key;
+    const uint8_t* src = zero_row;
+    if (key < R128_TILE && byte < ROW_BYTES && t < k1) {
+      const int vb = block_of(a, t);
+      const int blk = bt_lds[vb - e0];
+      if ((unsigned)blk < (unsigned)a.num_blocks)
+        src = a.kv + ((int64_t)blk * a.bs + (t - vb * a.bs)) * ROW_BYTES + byte;
+    }
+    dma16(src, j < R128_DMA ? stage_lds + 1024 * j : dummy_lds);
+  }
+}
+
+struct R128State {
+  f32x16 o[16];
+  float m_ref, l_part;
+};
+
+__device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R128_QREG], const uint8_t* q_tail,
+                                             const uint8_t* stage, float scale_log2, int ts, int k1, int nrow,
+                                             int lane) {
+  const int r = lane & 31, h = lane >> 5;
+  // S^T[key][row]: lane holds keys 8*(i/4) + 4h + i%4 of row r
+  f32x16 sc = {};
+  const uint8_t* kp = stage + r * R128_ROWB + 16 * h;
+#pragma unroll
+  for (int kk = 0; kk < R128_QREG; kk += 2) {
+    const bf16x8 k0f = *reinterpret_cast<const bf16x8*>(kp + 32 * kk);
+    const bf16x8 k1f = *reinterpret_cast<const bf16x8*>(kp + 32 * (kk + 1));
+    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qf[kk], sc, 0, 0, 0);
+    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f, qf[kk + 1], sc, 0, 0, 0);
+  }
+  // the last dims of Q^T come from this wave's LDS copy, laid out [kk][lane]
+#pragma unroll
+  for (int kk = 0; kk < R128_QLDS; ++kk) {
+    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kp + 32 * (R128_QREG + kk));
+    const bf16x8 qt = *reinterpret_cast<const bf16x8*>(q_tail + (kk * 64 + lane) * 16);
+    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qt, sc, 0, 0, 0);
+  }
+  float mx = NEG_INF;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = ts + 8 * (i >> 2) + 4 * h + (i & 3);
+    sc[i] = (t < k1 && t < nrow) ? sc[i] * scale_log2 : NEG_INF;
+    mx = fmaxf(mx, sc[i]);
+  }
+  if (__ballot(mx > st.m_ref + R128_RESCALE_LOG2) != 0) {
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (mx > st.m_ref + R128_RESCALE_LOG2) {
+      const float alpha = fast_exp2(st.m_ref - mx);
+      st.l_part *= alpha;
+      // one 16-register tile at a time, so the rare rescale never needs 256
+      // temporaries at once
+#pragma unroll
+      for (int m = 0; m < 16; ++m)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          // in place on the accumulator register (a plain multiply makes the
+          // register allocator keep two copies of all 256 accumulators)
+          float tmp;
+          asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                       : "+a"(st.o[m][i]), "=&v"(tmp) : "v"(alpha));
+        }
+      st.m_ref = mx;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    sc[i] = (sc[i] == NEG_INF) ? 0.f : fast_exp2(sc[i] - st.m_ref);
+    st.l_part += sc[i];
+  }
+  bf16x8 pf[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const bf16x4 lo4 = to_bf16x4(sc[8 * ks + 0], sc[8 * ks + 1], sc[8 * ks + 2], sc[8 * ks + 3]);
+    const bf16x4 hi4 = to_bf16x4(sc[8 * ks + 4], sc[8 * ks + 5], sc[8 * ks + 6], sc[8 * ks + 7]);
+    pf[ks] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  // V^T fragments: the MFMA's contraction slot 8h + s pairs with key
+  // 16*ks + 8*(s/4) + 4h + s%4 on the P^T side, so lane (q = lane/16, i)
+  // reads rows 16*ks + 4h (+8) of columns 32*m + 16*(q%2) + i.
+  const int q = lane >> 4, i16 = lane & 15;
+  const uint8_t* vp = stage + (4 * h + (i16 >> 2)) * R128_ROWB + 2 * (16 * (q & 1) + 4 * (i16 & 3));
+#pragma unroll
+  for (int m0 = 0; m0 < 16; m0 += 2) {
+    i16x4 v[2][2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          v[m][ks][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vp + (16 * ks + 8 * hh) * R128_ROWB + 64 * (m0 + m)));
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x4 a0 = __builtin_bit_cast(bf16x4, v[m][ks][0]);
+        const bf16x4 a1 = __builtin_bit_cast(bf16x4, v[m][ks][1]);
+        st.o[m0 + m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), pf[ks], st.o[m0 + m], 0, 0, 0);
+      }
+  }
+}
+
+__global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[R128_NS * R128_STAGE + 1024];
+  __shared__ int bt_lds[R128_BT_WIN];
+  __shared__ __attribute__((aligned(16))) uint8_t q_tail_lds[4][R128_QLDS * 64 * 16];
+  __shared__ int64_t s_red[4];
+  __shared__ int64_t s_excl[R128_THREADS];
+  __shared__ int s_first, s_last;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = blockIdx.x;
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
+  const uint32_t dummy_lds = ring_lds + R128_NS * R128_STAGE;
+
+  int64_t T = 0;
+  for (int base = 0; base < a.B; base += R128_THREADS) {
+    const int b = base + tid;
+    T += block_sum_i64<R128_THREADS>(b < a.B ? (int64_t)a.n_rt * request_keys(a, b) : 0, s_red);
+  }
+  const int64_t u0 = (int64_t)w * T / a.G, u1 = (int64_t)(w + 1) * T / a.G;
+
+  int64_t carry = 0;
+  for (int base = 0; base < a.B; base += R128_THREADS) {
+    const int b = base + tid;
+    const int64_t x = b < a.B ? (int64_t)a.n_rt * request_keys(a, b) : 0;
+    int64_t chunk_total;
+    const int64_t incl = block_incl_scan_i64<R128_THREADS>(x, s_red, chunk_total) + carry;
+    const int64_t excl = incl - x;
+    if (w == 0 && b < a.B) {
+      a.prefix[b + 1] = incl;
+      if (b == 0) a.prefix[0] = 0;
+    }
+    s_excl[tid] = excl;
+    if (tid == 0) { s_first = 0x7fffffff; s_last = -1; }
+    __syncthreads();
+    if (x > 0 && excl < u1 && incl > u0) {
+      atomicMin(&s_first, tid);
+      atomicMax(&s_last, tid);
+    }
+    __syncthreads();
+    const int first = s_first, last = s_last;
+    carry += chunk_total;
+
+    for (int ii = first; ii <= last; ++ii) {
+      const int bb = __builtin_amdgcn_readfirstlane(base + ii);
+      const int64_t pb = s_excl[ii];
+      const int nb = __builtin_amdgcn_readfirstlane(request_keys(a, bb));
+      const int seq = __builtin_amdgcn_readfirstlane(a.seq_lens[bb]);
+      const int tot = __builtin_amdgcn_readfirstlane(request_tot(a, bb, seq));
+      const int32_t* btr = a.bt + (int64_t)bb * a.max_blocks;
+      const int64_t lo = u0 > pb ? u0 - pb : 0;
+      const int64_t hi = (u1 - pb) < (int64_t)a.n_rt * nb ? u1 - pb : (int64_t)a.n_rt * nb;
+      for (int rt = (int)(lo / nb); (int64_t)rt * nb < hi; ++rt) {
+        const int k0 = __builtin_amdgcn_readfirstlane((int)((int64_t)rt * nb < lo ? lo - (int64_t)rt * nb : 0));
+        const int k1 = __builtin_amdgcn_readfirstlane((int)((int64_t)(rt + 1) * nb < hi ? nb : hi - (int64_t)rt * nb));
+        // ---- one piece: rows [128 rt, 128 rt + 128) of request bb, keys [k0, k1)
+        const int my_row = rt * R128_ROWS + wave * 32 + (lane & 31);
+        const bool row_ok = my_row < a.R;
+        const int nrow = row_ok ? row_bound(seq, tot, a.Q, my_row / a.H, a.W, a.rank, a.causal) : 0;
+        bf16x8 qf[R128_QREG];
+        uint8_t* q_tail = q_tail_lds[wave];
+        {
+          const uint8_t* qrow = a.q + ((int64_t)bb * a.R + (row_ok ? my_row : 0)) * ROW_BYTES + 16 * (lane >> 5);
+#pragma unroll
+          for (int kk = 0; kk < R128_QREG; ++kk) qf[kk] = row_ok ? gload_bf16x8(qrow + 32 * kk) : zero_bf16x8();
+#pragma unroll
+          for (int kk = 0; kk < R128_QLDS; ++kk)
+            *reinterpret_cast<bf16x8*>(q_tail + (kk * 64 + lane) * 16) =
+                row_ok ? gload_bf16x8(qrow + 32 * (R128_QREG + kk)) : zero_bf16x8();
+        }
+        R128State st;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) st.o[m] = f32x16{};
+        st.m_ref = NEG_INF;
+        st.l_part = 0.f;
+
+        // sub-pieces whose block-table span fits the LDS window
+        const int span_keys = (R128_BT_WIN - 1) * a.bs;
+        for (int ka = k0; ka < k1; ka += span_keys) {
+          const int kb = (k1 - ka) < span_keys ? k1 : ka + span_keys;
+          const int e0 = block_of(a, ka), e1 = block_of(a, kb - 1);
+          __syncthreads();  // previous sub-piece done with the window and the ring
+          for (int e = e0 + tid; e <= e1; e += R128_THREADS)
+            bt_lds[e - e0] = e < a.max_blocks ? btr[e] : -1;
+          __syncthreads();
+          const int nt = (kb - ka + R128_TILE - 1) / R128_TILE;
+          // prologue: tiles 0 and 1
+          r128_issue_tile(a, bt_lds, e0, ka, kb, ring_lds, dummy_lds, wave, lane);
+          r128_issue_tile(a, bt_lds, e0, ka + R128_TILE, kb, ring_lds + R128_STAGE, dummy_lds, wave, lane);
+          for (int it = 0; it < nt; ++it) {
+            // tile it landed (only tile it+1 may still be in flight), then
+            // every wave is also done computing tile it-1 ...
+            R128_WAIT_VMCNT(R128_DMA_PER_WAVE);
+            __syncthreads();
+            // ... so its stage can take tile it+2
+            r128_issue_tile(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb,
+                            ring_lds + ((it + 2) % R128_NS) * R128_STAGE, dummy_lds, wave, lane);
+            r128_compute(st, qf, q_tail, ring + (it % R128_NS) * R128_STAGE, a.scale_log2, ka + it * R128_TILE,
+                         kb, nrow, lane);
+          }
+          R128_WAIT_VMCNT(0);
+        }
+        // partial slot: O^T in the accumulator layout [m][row][h][i] (the 16
+        // values a lane holds per 32x32 tile are contiguous: 4 x 16-byte
+        // stores), then m and l per row
+        float l_row = st.l_part + __shfl_xor(st.l_part, 32, 64);
+        const int slot = w + bb * a.n_rt + rt;
+        float* ps = a.partials + (int64_t)slot * (R128_ROWS * D_V + 2 * R128_ROWS);
+        const int prow = wave * 32 + (lane & 31), h = lane >> 5;
+        float* pl = ps + (prow * 2 + h) * 16;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            *reinterpret_cast<f32x4*>(pl + m * (R128_ROWS * 32) + 4 * c) =
+                f32x4{st.o[m][4 * c], st.o[m][4 * c + 1], st.o[m][4 * c + 2], st.o[m][4 * c + 3]};
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (h == 0) {
+          ps[R128_ROWS * D_V + prow] = st.m_ref;
+          ps[R128_ROWS * D_V + R128_ROWS + prow] = l_row;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------- combine
 // Grid: (request, row tile) groups x 8 slices of 64 output columns.  Merges
 // the partial slots of the workgroups that covered the group and writes bf16
 // out and (slice 0) the LSE.  Groups no workgroup covered (no visible keys)
 // get out = 0, lse = -inf.
+// Partial slot element (row, dv): the M16 kernel stores O^T as [dv][row];
+// the R128 kernel stores its accumulator layout [dv/32][row][h][i] with
+// dv % 32 = 8*(i/4) + 4h + i%4.
+template <int ROWS>
+__device__ __forceinline__ int slot_index(int row, int dv) {
+  if (ROWS == M16_ROWS) return dv * ROWS + row;
+  const int r32 = dv & 31;
+  return ((dv >> 5) * ROWS + row) * 32 + ((r32 >> 2) & 1) * 16 + (r32 >> 3) * 4 + (r32 & 3);
+}
+
 template <int ROWS>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   constexpr int SLICE = 64;                       // output columns per workgroup
@@ -425,7 +719,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     const float f = (mw == NEG_INF) ? 0.f : fast_exp2(mw - M);
     L += f * ps[ROWS * D_V + ROWS + row];
 #pragma unroll
-    for (int c = 0; c < PER; ++c) acc[c] += f * ps[(col0 + c) * ROWS + row];
+    for (int c = 0; c < PER; ++c) acc[c] += f * ps[slot_index<ROWS>(row, col0 + c)];
   }
   const float inv = 1.f / L;
 #pragma unroll
@@ -466,7 +760,7 @@ int device_cu_count() {
 Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus) {
   Plan p{};
   const int64_t R = (int64_t)q_len * H;
-  p.rows_tile = M16_ROWS;
+  p.rows_tile = R <= M16_ROWS ? M16_ROWS : R128_ROWS;
   p.n_rt = (int)((R + p.rows_tile - 1) / p.rows_tile);
   const int64_t units = (int64_t)B * p.n_rt * (max_seq_len > 0 ? max_seq_len : 1);
   int64_t G = (units + 255) / 256;  // at least 256 keys per workgroup
@@ -535,9 +829,15 @@ extern "C" int mla_decode(const void* q, const void* kv_cache, const int32_t* bl
   a.lse = lse;
 
   if (tl_prof_start) (void)hipEventRecord(tl_prof_start, stream);
-  hipLaunchKernelGGL(attn_m16_kernel, dim3(p.G), dim3(M16_THREADS), 0, stream, a);
+  if (p.rows_tile == M16_ROWS)
+    hipLaunchKernelGGL(attn_m16_kernel, dim3(p.G), dim3(M16_THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_r128_kernel, dim3(p.G), dim3(R128_THREADS), 0, stream, a);
   if (tl_prof_stop) (void)hipEventRecord(tl_prof_stop, stream);
-  hipLaunchKernelGGL(combine_kernel<M16_ROWS>, dim3(B * p.n_rt * 8), dim3(256), 0, stream, a);
+  if (p.rows_tile == M16_ROWS)
+    hipLaunchKernelGGL(combine_kernel<M16_ROWS>, dim3(B * p.n_rt * 8), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(combine_kernel<R128_ROWS>, dim3(B * p.n_rt * 8), dim3(256), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }

@@ -129,12 +129,12 @@ def test_flattened_rows_equal_native_multi_token():
         fo, fl = mla.mla_decode(qf, up.pools[r], btf, i32_dev(n), None, cp_world=1, cp_rank=0, causal=False,
                                 scale=sp.scale)
         torch.cuda.synchronize()
-        err = (fo.float() - native_o.float()).abs().max().item()
-        assert err <= 1e-2, err
+        # both are separate bf16 results: each must meet the bar against the oracle
+        ro, rl = oracle_rank(wl, r)
+        compare(native_o, native_l, ro, rl, f"native r{r}")
+        compare(fo, fl, ro, rl, f"flattened r{r}")
         nl, fl_ = native_l.cpu().numpy(), fl.cpu().numpy()
         assert np.array_equal(np.isfinite(nl), np.isfinite(fl_))
-        fin = np.isfinite(nl)
-        assert np.abs(nl[fin] - fl_[fin]).max() <= 1e-4
 
 
 def test_end_aligned_mask_is_not_what_the_kernel_does():
