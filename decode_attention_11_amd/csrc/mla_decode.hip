@@ -72,6 +72,14 @@ __device__ __forceinline__ int request_keys(const DecodeArgs& a, int b) {
   return row_bound(seq, request_tot(a, b, seq), a.Q, a.Q - 1, a.W, a.rank, a.causal);
 }
 
+// Workgroups are dispatched to the 8 XCDs round-robin (blockIdx % 8).  The
+// balanced ranges are numbered so that consecutive ranges (the row tiles of
+// one request read the same keys at the same time) sit on one XCD and share
+// its L2.
+__device__ __forceinline__ int xcd_range_index(int block, int G) {
+  return (G % 8 == 0) ? (block % 8) * (G / 8) + block / 8 : block;
+}
+
 // ---------------------------------------------------------------- in-kernel plan
 // Every partial workgroup recomputes the request offsets itself (a block
 // scan over seq_lens), so no separate planning launch is needed; workgroup 0
@@ -246,7 +254,7 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
-  const int w = blockIdx.x;
+  const int w = xcd_range_index(blockIdx.x, a.G);
   float* mrg_o = reinterpret_cast<float*>(smem);
   uint8_t* vs = smem + wave * M16_VSTAGE;
 
@@ -394,17 +402,16 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
 constexpr int R128_THREADS = 256;
 constexpr int R128_ROWS = 128;
 constexpr int R128_TILE = 32;                 // keys per tile
-constexpr int R128_ROWB = 1168;               // LDS bytes per key row (1152 + 16: conflict-free reads)
-constexpr int R128_DMA = 37;                  // 1 KiB load instructions per tile (32 x 1168 B rounded up)
-constexpr int R128_DMA_PER_WAVE = 10;         // ceil(37 / 4); the spare ones write a dummy area
-constexpr int R128_STAGE = R128_DMA * 1024;
+constexpr int R128_ROWB = ROW_BYTES;          // LDS bytes per key row (unpadded; chunks are swizzled instead)
+constexpr int R128_DMA_PER_WAVE = 9;          // 1 KiB load instructions per wave per tile: its 8 rows
+constexpr int R128_STAGE = R128_TILE * R128_ROWB;   // 36 KiB
 constexpr int R128_NS = 3;                    // ring stages
 constexpr int R128_BT_WIN = 1024;             // block-table entries held in LDS per sub-piece
 constexpr int R128_QREG = 28;                 // Q^T k-steps (of 16 dims) kept in registers; the rest in LDS
 constexpr int R128_QLDS = 36 - R128_QREG;
 constexpr float R128_RESCALE_LOG2 = 8.f;
 
-static_assert(R128_TILE * R128_ROWB <= R128_STAGE, "tile must fit its stage");
+static_assert(R128_STAGE == 4 * R128_DMA_PER_WAVE * 1024, "a stage is exactly the four waves' loads");
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 #define R128_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
@@ -415,31 +422,57 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(base) : "memory", "m0");
 }
 
-// Issue this wave's share of the loads of tile [ts, ts+32) into a stage.
-// Chunk o = 1024*j + 16*lane of the stage holds key o / 1168, byte o % 1168;
-// padding, keys past k1 and invalid block ids read the zero row.
+// Swizzle of the 16-byte chunks of a key row in LDS: logical chunk c of row r
+// sits at (c & ~7) | ((c ^ f(r)) & 7), f(r) = g((r >> 1) & 7) with
+// g(v) = (v >> 1) | ((v & 1) << 2).  Rows are 1152 bytes (72 chunks, 8 mod 16
+// in 16-byte bank groups), so odd rows already land on the other half of the
+// banks; f is a permutation over even (and over odd) rows, which makes the
+// QK^T reads (16 rows, one chunk) conflict-free, and f(4u) ^ f(4u+2) = 4,
+// which does the same for the transposed V reads (4 rows x 2-4 chunks).
+__device__ __forceinline__ int r128_f(int r) {
+  const int v = (r >> 1) & 7;
+  return (v >> 1) | ((v & 1) << 2);
+}
+
+// Issue this wave's loads of tile [ts, ts+32) into a stage: wave w loads keys
+// 8w..8w+7 with 9 instructions; instruction m, lane l fills stage byte
+// 1024*(9w+m) + 16*l, i.e. row 8w + (64m+l)/72, physical chunk (64m+l)%72.
+// dma_sel_off[m] (per lane, fixed) holds the logical byte offset of that chunk
+// and whether its row is the higher of the two rows instruction m touches.
 __device__ __forceinline__ void r128_issue_tile(const DecodeArgs& a, const int* bt_lds, int e0, int ts, int k1,
-                                                uint32_t stage_lds, uint32_t dummy_lds, int wave, int lane) {
-  // opaque copies: the per-lane address arithmetic below is loop-invariant
-  // and, left visible, gets hoisted out of the tile loop into ~200 registers
-  asm volatile("" : "+v"(lane));
-  const uint8_t* zero_row = reinterpret_cast<const uint8_t*>(kZeroRow);
-  asm volatile("" : "+v"(zero_row));
+                                                uint32_t stage_lds, int wave, int lane,
+                                                const int (&dma_sel_off)[R128_DMA_PER_WAVE]) {
+  // lanes 0..7 resolve the row address of key ts + 8*wave + lane (or the zero row)
+  const int k = lane & 7;
+  const int t = ts + 8 * wave + k;
+  const uint8_t* rowp = reinterpret_cast<const uint8_t*>(kZeroRow);
+  asm volatile("" : "+v"(rowp));
+  if (t < k1) {
+    const int vb = t >> a.bs_shift;
+    const int blk = bt_lds[vb - e0];
+    if ((unsigned)blk < (unsigned)a.num_blocks)
+      rowp = a.kv + ((int64_t)blk * a.bs + (t & (a.bs - 1))) * ROW_BYTES;
+  }
+  const uint64_t row64 = reinterpret_cast<uint64_t>(rowp);
+  uint64_t rows[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)row64, j);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(row64 >> 32), j);
+    rows[j] = ((uint64_t)hi << 32) | lo;
+  }
 #pragma unroll
   for (int m = 0; m < R128_DMA_PER_WAVE; ++m) {
-    const int j = wave + 4 * m;
-    const int o = 1024 * j + 16 * lane;
-    const int key = o / R128_ROWB;
-    const int byte = o - key * R128_ROWB;
-    const int t = ts + key;
-    const uint8_t* src = zero_row;
-    if (key < R128_TILE && byte < ROW_BYTES && t < k1) {
-      const int vb = block_of(a, t);
-      const int blk = bt_lds[vb - e0];
-      if ((unsigned)blk < (unsigned)a.num_blocks)
-        src = a.kv + ((int64_t)blk * a.bs + (t - vb * a.bs)) * ROW_BYTES + byte;
-    }
-    dma16(src, j < R128_DMA ? stage_lds + 1024 * j : dummy_lds);
+    const int rlo = (64 * m) / 72;
+    const int rhi = (64 * m + 63) / 72;
+    const int so = dma_sel_off[m];
+    // lanes in the higher row add the (uniform) distance between the two row
+    // addresses; arithmetic rather than a select keeps the compiler from
+    // turning it into a compare chain over all eight rows
+    const uint64_t dist = rows[rhi] - rows[rlo];
+    const uint64_t msk = (uint64_t)0 - (uint64_t)((uint32_t)so >> 15);
+    dma16(reinterpret_cast<const void*>(rows[rlo] + (dist & msk) + (so & 0x7fff)),
+          stage_lds + 1024 * (R128_DMA_PER_WAVE * wave + m));
   }
 }
 
@@ -454,20 +487,26 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R
   const int r = lane & 31, h = lane >> 5;
   // S^T[key][row]: lane holds keys 8*(i/4) + 4h + i%4 of row r
   f32x16 sc = {};
-  const uint8_t* kp = stage + r * R128_ROWB + 16 * h;
+  // k-step kk = 4a + b reads logical chunk 2kk + h of row r: physical byte
+  // 128a + 16*((2b + h) ^ f(r)) of the row
+  const int fk = r128_f(r);
+  const uint8_t* krow = stage + r * R128_ROWB;
+  const uint8_t* kp[4];
 #pragma unroll
-  for (int kk = 0; kk < R128_QREG; kk += 2) {
-    const bf16x8 k0f = *reinterpret_cast<const bf16x8*>(kp + 32 * kk);
-    const bf16x8 k1f = *reinterpret_cast<const bf16x8*>(kp + 32 * (kk + 1));
-    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qf[kk], sc, 0, 0, 0);
-    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f, qf[kk + 1], sc, 0, 0, 0);
-  }
-  // the last dims of Q^T come from this wave's LDS copy, laid out [kk][lane]
+  for (int b = 0; b < 4; ++b) kp[b] = krow + 16 * ((2 * b + h) ^ fk);
+  // K fragments are read two k-steps ahead of their MFMA (LDS latency would
+  // otherwise be exposed at every step); the last dims of Q^T come from this
+  // wave's LDS copy, laid out [kk][lane]
+  bf16x8 kf[3];
+  kf[0] = *reinterpret_cast<const bf16x8*>(kp[0]);
+  kf[1] = *reinterpret_cast<const bf16x8*>(kp[1]);
 #pragma unroll
-  for (int kk = 0; kk < R128_QLDS; ++kk) {
-    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kp + 32 * (R128_QREG + kk));
-    const bf16x8 qt = *reinterpret_cast<const bf16x8*>(q_tail + (kk * 64 + lane) * 16);
-    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qt, sc, 0, 0, 0);
+  for (int kk = 0; kk < 36; ++kk) {
+    if (kk + 2 < 36)
+      kf[(kk + 2) % 3] = *reinterpret_cast<const bf16x8*>(kp[(kk + 2) & 3] + 128 * ((kk + 2) >> 2));
+    const bf16x8 qv = kk < R128_QREG ? qf[kk < R128_QREG ? kk : 0]
+                                     : *reinterpret_cast<const bf16x8*>(q_tail + ((kk - R128_QREG) * 64 + lane) * 16);
+    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % 3], qv, sc, 0, 0, 0);
   }
   float mx = NEG_INF;
 #pragma unroll
@@ -511,8 +550,19 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R
   // V^T fragments: the MFMA's contraction slot 8h + s pairs with key
   // 16*ks + 8*(s/4) + 4h + s%4 on the P^T side, so lane (q = lane/16, i)
   // reads rows 16*ks + 4h (+8) of columns 32*m + 16*(q%2) + i.
+  // Lane (q, i) of a transposed read covers row 16ks + 8hh + 4h + i/4,
+  // logical chunk 4m + 2(q%2) + (i%4)/2, byte 8*(i%2) of it; the swizzle
+  // only depends on hh and on m's parity (per lane).
   const int q = lane >> 4, i16 = lane & 15;
-  const uint8_t* vp = stage + (4 * h + (i16 >> 2)) * R128_ROWB + 2 * (16 * (q & 1) + 4 * (i16 & 3));
+  const uint8_t* vrow = stage + (4 * h + (i16 >> 2)) * R128_ROWB + 8 * (i16 & 1);
+  const uint8_t* vp[2][2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int ft = r128_f(8 * hh + 4 * h + (i16 >> 2));
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      vp[hh][par] = vrow + 8 * hh * R128_ROWB + 16 * ((4 * par + 2 * (q & 1) + ((i16 & 3) >> 1)) ^ ft);
+  }
 #pragma unroll
   for (int m0 = 0; m0 < 16; m0 += 2) {
     i16x4 v[2][2][2];
@@ -523,7 +573,7 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
           v[m][ks][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vp + (16 * ks + 8 * hh) * R128_ROWB + 64 * (m0 + m)));
+              (lds_i16x4*)(vp[hh][(m0 + m) & 1] + 16 * ks * R128_ROWB + 128 * ((m0 + m) >> 1)));
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -537,7 +587,7 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R
 }
 
 __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[R128_NS * R128_STAGE + 1024];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[R128_NS * R128_STAGE];
   __shared__ int bt_lds[R128_BT_WIN];
   __shared__ __attribute__((aligned(16))) uint8_t q_tail_lds[4][R128_QLDS * 64 * 16];
   __shared__ int64_t s_red[4];
@@ -545,9 +595,19 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
   __shared__ int s_first, s_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int w = blockIdx.x;
+  const int w = xcd_range_index(blockIdx.x, a.G);
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
-  const uint32_t dummy_lds = ring_lds + R128_NS * R128_STAGE;
+  // per-lane constants of this wave's ring loads (see r128_issue_tile):
+  // logical byte offset of the chunk, bit 15 set when its row is the higher
+  // of the two rows the instruction touches
+  int dma_sel_off[R128_DMA_PER_WAVE];
+#pragma unroll
+  for (int m = 0; m < R128_DMA_PER_WAVE; ++m) {
+    const int cidx = 64 * m + lane;
+    const int row_rel = cidx / 72, pch = cidx - 72 * (cidx / 72);
+    const int c = (pch & ~7) | ((pch ^ r128_f(8 * wave + row_rel)) & 7);
+    dma_sel_off[m] = 16 * c | ((row_rel != (64 * m) / 72) ? (1 << 15) : 0);
+  }
 
   int64_t T = 0;
   for (int base = 0; base < a.B; base += R128_THREADS) {
@@ -622,16 +682,16 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
           __syncthreads();
           const int nt = (kb - ka + R128_TILE - 1) / R128_TILE;
           // prologue: tiles 0 and 1
-          r128_issue_tile(a, bt_lds, e0, ka, kb, ring_lds, dummy_lds, wave, lane);
-          r128_issue_tile(a, bt_lds, e0, ka + R128_TILE, kb, ring_lds + R128_STAGE, dummy_lds, wave, lane);
+          r128_issue_tile(a, bt_lds, e0, ka, kb, ring_lds, wave, lane, dma_sel_off);
+          r128_issue_tile(a, bt_lds, e0, ka + R128_TILE, kb, ring_lds + R128_STAGE, wave, lane, dma_sel_off);
           for (int it = 0; it < nt; ++it) {
             // tile it landed (only tile it+1 may still be in flight), then
             // every wave is also done computing tile it-1 ...
-            R128_WAIT_VMCNT(R128_DMA_PER_WAVE);
+            R128_WAIT_VMCNT(R128_DMA_PER_WAVE);  // tile it+1's 9 loads may stay in flight
             __syncthreads();
             // ... so its stage can take tile it+2
             r128_issue_tile(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb,
-                            ring_lds + ((it + 2) % R128_NS) * R128_STAGE, dummy_lds, wave, lane);
+                            ring_lds + ((it + 2) % R128_NS) * R128_STAGE, wave, lane, dma_sel_off);
             r128_compute(st, qf, q_tail, ring + (it % R128_NS) * R128_STAGE, a.scale_log2, ka + it * R128_TILE,
                          kb, nrow, lane);
           }
@@ -757,10 +817,12 @@ int device_cu_count() {
   return cache[dev];
 }
 
-Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus) {
+// The 128-row kernel needs a power-of-two block size (its ring loads use
+// shifts and masks); every other case runs the 16-row kernel.
+Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool allow_r128) {
   Plan p{};
   const int64_t R = (int64_t)q_len * H;
-  p.rows_tile = R <= M16_ROWS ? M16_ROWS : R128_ROWS;
+  p.rows_tile = (R <= M16_ROWS || !allow_r128) ? M16_ROWS : R128_ROWS;
   p.n_rt = (int)((R + p.rows_tile - 1) / p.rows_tile);
   const int64_t units = (int64_t)B * p.n_rt * (max_seq_len > 0 ? max_seq_len : 1);
   int64_t G = (units + 255) / 256;  // at least 256 keys per workgroup
@@ -788,7 +850,10 @@ extern "C" int mla_profile_attention_events(hipEvent_t start, hipEvent_t stop) {
 
 extern "C" size_t mla_decode_workspace_size(int B, int q_len, int H, int max_seq_len) {
   if (B <= 0 || q_len < 1 || H < 1 || max_seq_len < 0) return 0;
-  return make_plan(B, q_len, H, max_seq_len, device_cu_count()).bytes;
+  const int cus = device_cu_count();
+  const size_t a = make_plan(B, q_len, H, max_seq_len, cus, true).bytes;
+  const size_t b = make_plan(B, q_len, H, max_seq_len, cus, false).bytes;
+  return a > b ? a : b;
 }
 
 extern "C" int mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
@@ -806,7 +871,8 @@ extern "C" int mla_decode(const void* q, const void* kv_cache, const int32_t* bl
   if (causal && cp_world > 1 && causal_seqlens_global == nullptr) return MLA_ERR_INVALID_ARG;
   if (B == 0) return MLA_OK;
   if (!q || !kv_cache || !block_table || !seq_lens || !out) return MLA_ERR_INVALID_ARG;
-  const Plan p = make_plan(B, q_len, H, max_seq_len, device_cu_count());
+  const bool pow2_bs = (block_size & (block_size - 1)) == 0;
+  const Plan p = make_plan(B, q_len, H, max_seq_len, device_cu_count(), pow2_bs);
   if (workspace_bytes < p.bytes || workspace == nullptr) return MLA_ERR_INVALID_ARG;
 
   DecodeArgs a{};
