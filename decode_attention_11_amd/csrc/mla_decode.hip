@@ -18,17 +18,16 @@
 // (PR #54012 page, implementation breakdown: the non-DCP call keeps its
 // multi-CTA KV counter buffer); the balanced range split is this library's.
 //
-// Kernel family M16 (this file): 16 rows per tile, for single-token decode
-// with up to 16 heads, the HBM-bound case.  Eight waves of a workgroup take
-// turns over 16-key subtiles of a piece, each keeping its own online-softmax
-// state for the 16 rows, merged in LDS at the end of the piece.  Scores are
-// S^T = K * Q^T on v_mfma_f32_16x16x32_bf16 (K rows as the A operand straight
-// from HBM into registers, Q^T read from LDS), so each lane holds 4 keys of
-// one row; P*V is O^T += V^T * P^T on v_mfma_f32_16x16x16_bf16 with V^T read
-// from LDS by ds_read_b64_tr_b16, so P never leaves registers and each lane
-// owns one row of O^T.  The running max is a reference that only moves when
-// a row's max grows by more than 2^8, so the accumulators are rarely
-// rescaled (the exponentials stay <= 256, exact in fp32 and bf16 range).
+// Two kernel families compute the partials.  M16 (16 rows per tile) serves
+// single-token decode with up to 16 heads, the HBM-bound case; R128 (128
+// rows per tile) serves multi-token and many-head requests, where the score
+// and value products dominate.  Both stream key tiles through an LDS ring,
+// compute S^T = K Q^T so that each lane ends up holding keys of one query
+// row, and feed P^T straight from registers into O^T += V^T P^T with V^T
+// read from LDS by the transposing ds_read_b64_tr_b16.  The running max is a
+// reference that only moves when a row's max grows by more than 2^8, so the
+// accumulators are rarely rescaled (the exponentials stay <= 256, exact in
+// fp32 and in bf16 range).
 #include <hip/hip_runtime.h>
 #include <cmath>
 #include <cstdint>
@@ -116,176 +115,43 @@ __device__ __forceinline__ int64_t block_incl_scan_i64(int64_t v, int64_t* s_red
   return before + v;
 }
 
-// ---------------------------------------------------------------- M16 partial
-// Memory-bound family: up to 16 rows per request (single-token decode with
-// up to 16 heads and similar).  256 threads = 4 waves per workgroup (one per
-// SIMD), one workgroup per CU; the waves take turns over 16-key subtiles of a
-// piece.  Each wave keeps Q^T (72 VGPRs) and two key subtiles (2 x 72 VGPRs)
-// in registers and the 16 x 512 fp32 O^T accumulator in MFMA registers; the
-// block-table entry of a subtile is read two subtiles ahead and the key rows
-// one subtile ahead, so no wait ever drains the prefetch.
-constexpr int M16_THREADS = 256;
-constexpr int M16_WAVES = 4;
-constexpr int M16_ROWS = 16;
-constexpr int M16_SUB = 16;          // keys per subtile
-constexpr int M16_VROW = 1056;       // LDS bytes per key row of a V stage (1024 + 32 pad: conflict-free tr reads)
-constexpr int M16_VSTAGE = M16_SUB * M16_VROW;
-constexpr int M16_QBYTES = 18 * 64 * 16;                   // Q^T fragments of the 16 rows
-constexpr int M16_MRG_LD = 17;       // padded row stride of the merge buffer [dv][row]
-constexpr int M16_SMEM = M16_WAVES * M16_VSTAGE;           // V stages; the merge buffer aliases them
-constexpr float M16_RESCALE_LOG2 = 8.f;                    // keep exponentials <= 2^8 between rescales
-
-static_assert(D_V * M16_MRG_LD * 4 <= M16_SMEM, "merge buffer must fit in the V stages");
-
-// A zero latent row: lanes whose key is outside the piece (or has an invalid
-// block id) read it instead, so every lane issues the same loads and the V
-// rows of masked keys are exact zeros (0 * NaN garbage would poison P*V).
-__device__ __attribute__((aligned(64))) const uint4 kZeroRow[ROW_BYTES / 16] = {};
-
-__device__ __forceinline__ int block_of(const DecodeArgs& a, int t) {
-  return a.bs_shift >= 0 ? (t >> a.bs_shift) : t / a.bs;
-}
-
-// Raw block-table entry covering local key t.  The read is unconditional
-// (index clamped into the row) and its value is only inspected by key_row,
-// a loop iteration later: a load inside a branch, or a select right after
-// it, would make the compiler wait for every load in flight.
-__device__ __forceinline__ int key_block(const DecodeArgs& a, const int32_t* btr, int t) {
-  const int vb = block_of(a, t);
-  return gload_i32(btr + (vb < a.max_blocks ? vb : a.max_blocks - 1));
-}
-
-// Row address of local key t given its block-table entry; the zero row when
-// t is outside the piece, past the table width, or the block id is invalid.
-__device__ __forceinline__ const uint8_t* key_row(const DecodeArgs& a, int blk, int t, int k1) {
-  const int vb = block_of(a, t);
-  if (t >= k1 || vb >= a.max_blocks || (unsigned)blk >= (unsigned)a.num_blocks)
-    return reinterpret_cast<const uint8_t*>(kZeroRow);
-  return a.kv + ((int64_t)blk * a.bs + (t - vb * a.bs)) * ROW_BYTES;
-}
-
-// Loads one subtile's 16 keys as MFMA A-operand fragments: lane (li, g)
-// holds 16-byte chunks 4*kk + g of its key's row.
-__device__ __forceinline__ void m16_load(bf16x8 (&kb)[18], const uint8_t* rowp, int g) {
-  rowp += g * 16;
-#pragma unroll
-  for (int kk = 0; kk < 18; ++kk) kb[kk] = gload_bf16x8(rowp + kk * 64);
-}
-
-struct M16State {
-  f32x4 o[32];
-  float m_ref, l_part;
-};
-
-// One 16-key subtile: S^T = K Q^T, online softmax with a lazily moved
-// reference max, O^T += V^T P^T.
-__device__ __forceinline__ void m16_compute(M16State& st, const bf16x8 (&kb)[18], const uint8_t* q_lds,
-                                            uint8_t* vs, float scale_log2, int kbase, int k1, int nrow,
-                                            int lane, int li, int g) {
-  // S^T[t][row]: lane holds keys t = kbase + 4g + i of row li.  Q^T comes
-  // from LDS every subtile (the compiler barrier keeps the reads here
-  // instead of hoisting them into 72 registers that would then spill).
-  asm volatile("" ::: "memory");
-  f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kk = 0; kk < 18; kk += 2) {
-    const bf16x8 qa = *reinterpret_cast<const bf16x8*>(q_lds + (kk * 64 + lane) * 16);
-    const bf16x8 qb = *reinterpret_cast<const bf16x8*>(q_lds + ((kk + 1) * 64 + lane) * 16);
-    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qa, sa, 0, 0, 0);
-    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk + 1], qb, sb, 0, 0, 0);
-  }
-  // the V part (first 512 columns) goes to this wave's LDS stage for the transposed read
-#pragma unroll
-  for (int kk = 0; kk < 16; ++kk)
-    *reinterpret_cast<bf16x8*>(vs + li * M16_VROW + (4 * kk + g) * 16) = kb[kk];
-
-  float p[4];
-  float mx = NEG_INF;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = kbase + 4 * g + i;
-    const float v = (t < k1 && t < nrow) ? (sa[i] + sb[i]) * scale_log2 : NEG_INF;
-    p[i] = v;
-    mx = fmaxf(mx, v);
-  }
-  // move the reference only when some row's max grew by more than 2^8 over it
-  if (__ballot(mx > st.m_ref + M16_RESCALE_LOG2) != 0) {
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (mx > st.m_ref + M16_RESCALE_LOG2) {
-      const float alpha = fast_exp2(st.m_ref - mx);
-      st.l_part *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < 32; ++mt) st.o[mt] *= alpha;
-      st.m_ref = mx;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    p[i] = (p[i] == NEG_INF) ? 0.f : fast_exp2(p[i] - st.m_ref);
-    st.l_part += p[i];
-  }
-  const bf16x4 pf = to_bf16x4(p[0], p[1], p[2], p[3]);
-  // O^T[dv][row] += V^T[dv][t] P^T[t][row]; the transposed read gives lane
-  // (li, g) V[4g+e][16*mt+li] when lane (q, g) points at row 4g+q/4,
-  // columns 16*mt + 4*(q%4)
-  const uint8_t* vread = vs + (4 * g + (li >> 2)) * M16_VROW + (li & 3) * 8;
-#pragma unroll
-  for (int mt0 = 0; mt0 < 32; mt0 += 8) {
-    i16x4 v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      v[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vread + (mt0 + j) * 32));
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      st.o[mt0 + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, v[j]), pf,
-                                                               st.o[mt0 + j], 0, 0, 0);
-  }
-}
-
-__global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[M16_SMEM];
-  __shared__ __attribute__((aligned(16))) uint8_t q_lds[M16_QBYTES];
-  __shared__ int64_t s_red[M16_WAVES];
-  __shared__ int64_t s_excl[M16_THREADS];
-  __shared__ int s_first, s_last;
-  __shared__ float mrg_m[M16_WAVES][M16_ROWS];
-  __shared__ float mrg_l[M16_ROWS];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, li = lane & 15;
-  const int w = xcd_range_index(blockIdx.x, a.G);
-  float* mrg_o = reinterpret_cast<float*>(smem);
-  uint8_t* vs = smem + wave * M16_VSTAGE;
-
-  // total units
+// ---------------------------------------------------------------- work ranges
+// Calls piece(bb, rt, k0, k1, seq, tot) for every (request, row tile) group
+// that overlaps this workgroup's balanced range of units, in unit order, with
+// the group's keys [k0, k1) inside the range.  Workgroup 0 also stores the
+// request offsets for the combine kernel.  All arguments of piece() are
+// wave-uniform.
+template <int NT, class F>
+__device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int w, int64_t* s_red, int64_t* s_excl,
+                                               int* s_first_last, F&& piece) {
+  const int tid = threadIdx.x;
   int64_t T = 0;
-  for (int base = 0; base < a.B; base += M16_THREADS) {
+  for (int base = 0; base < a.B; base += NT) {
     const int b = base + tid;
-    T += block_sum_i64<M16_THREADS>(b < a.B ? (int64_t)a.n_rt * request_keys(a, b) : 0, s_red);
+    T += block_sum_i64<NT>(b < a.B ? (int64_t)a.n_rt * request_keys(a, b) : 0, s_red);
   }
   const int64_t u0 = (int64_t)w * T / a.G, u1 = (int64_t)(w + 1) * T / a.G;
 
   int64_t carry = 0;
-  for (int base = 0; base < a.B; base += M16_THREADS) {
+  for (int base = 0; base < a.B; base += NT) {
     const int b = base + tid;
     const int64_t x = b < a.B ? (int64_t)a.n_rt * request_keys(a, b) : 0;
     int64_t chunk_total;
-    const int64_t incl = block_incl_scan_i64<M16_THREADS>(x, s_red, chunk_total) + carry;
+    const int64_t incl = block_incl_scan_i64<NT>(x, s_red, chunk_total) + carry;
     const int64_t excl = incl - x;
     if (w == 0 && b < a.B) {
       a.prefix[b + 1] = incl;
       if (b == 0) a.prefix[0] = 0;
     }
     s_excl[tid] = excl;
-    if (tid == 0) { s_first = 0x7fffffff; s_last = -1; }
+    if (tid == 0) { s_first_last[0] = 0x7fffffff; s_first_last[1] = -1; }
     __syncthreads();
     if (x > 0 && excl < u1 && incl > u0) {
-      atomicMin(&s_first, tid);
-      atomicMax(&s_last, tid);
+      atomicMin(&s_first_last[0], tid);
+      atomicMax(&s_first_last[1], tid);
     }
     __syncthreads();
-    const int first = s_first, last = s_last;
+    const int first = s_first_last[0], last = s_first_last[1];
     carry += chunk_total;
 
     for (int i = first; i <= last; ++i) {
@@ -294,97 +160,271 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
       const int nb = __builtin_amdgcn_readfirstlane(request_keys(a, bb));
       const int seq = __builtin_amdgcn_readfirstlane(a.seq_lens[bb]);
       const int tot = __builtin_amdgcn_readfirstlane(request_tot(a, bb, seq));
-      const int32_t* btr = a.bt + (int64_t)bb * a.max_blocks;
-      const int64_t lo = u0 > pb ? u0 - pb : 0;                       // first unit of the request in range
+      const int64_t lo = u0 > pb ? u0 - pb : 0;  // first unit of the request in range
       const int64_t hi = (u1 - pb) < (int64_t)a.n_rt * nb ? u1 - pb : (int64_t)a.n_rt * nb;
       for (int rt = (int)(lo / nb); (int64_t)rt * nb < hi; ++rt) {
         const int k0 = __builtin_amdgcn_readfirstlane((int)((int64_t)rt * nb < lo ? lo - (int64_t)rt * nb : 0));
         const int k1 = __builtin_amdgcn_readfirstlane((int)((int64_t)(rt + 1) * nb < hi ? nb : hi - (int64_t)rt * nb));
-        // ---- one piece: rows [16 rt, 16 rt + 16) of request bb, keys [k0, k1)
-        const int my_row = rt * M16_ROWS + li;
-        const bool row_ok = my_row < a.R;
-        const int nrow = row_ok ? row_bound(seq, tot, a.Q, my_row / a.H, a.W, a.rank, a.causal) : 0;
-        // Q^T fragments of the 16 rows into LDS, laid out [kk][g][row] x 16 bytes
-        for (int e = tid; e < 18 * 64; e += M16_THREADS) {
-          const int kk = e >> 6, gg = (e >> 4) & 3, rr = e & 15;
-          const int row = rt * M16_ROWS + rr;
-          bf16x8 v = zero_bf16x8();
-          if (row < a.R) v = gload_bf16x8(a.q + ((int64_t)bb * a.R + row) * ROW_BYTES + (4 * kk + gg) * 16);
-          *reinterpret_cast<bf16x8*>(q_lds + e * 16) = v;
-        }
-        __syncthreads();
-        M16State st;
-#pragma unroll
-        for (int mt = 0; mt < 32; ++mt) st.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        st.m_ref = NEG_INF;
-        st.l_part = 0.f;
-        const int nsub = (k1 - k0 + M16_SUB - 1) / M16_SUB;
-        // wave w takes subtiles w, w+4, w+8, ...; lane li loads key k0 + 16*s + li
-        constexpr int STEP = M16_WAVES * M16_SUB;
-        int t0 = k0 + M16_SUB * wave + li;
-        bf16x8 kb0[18], kb1[18];
-        m16_load(kb0, key_row(a, key_block(a, btr, t0), t0, k1), g);
-        m16_load(kb1, key_row(a, key_block(a, btr, t0 + STEP), t0 + STEP, k1), g);
-        int blk2 = key_block(a, btr, t0 + 2 * STEP);
-        int blk3 = key_block(a, btr, t0 + 3 * STEP);
-        // the scheduling barriers pin each prefetch right after the compute
-        // that frees its registers (left alone, the scheduler sinks the loads
-        // under the other buffer's compute and only one subtile is in flight)
-        for (int s = wave; s < nsub; s += 2 * M16_WAVES) {
-          m16_compute(st, kb0, q_lds, vs, a.scale_log2, k0 + M16_SUB * s, k1, nrow, lane, li, g);
-          __builtin_amdgcn_sched_barrier(0);
-          m16_load(kb0, key_row(a, blk2, t0 + 2 * STEP, k1), g);
-          blk2 = key_block(a, btr, t0 + 4 * STEP);
-          __builtin_amdgcn_sched_barrier(0);
-          // unconditional even past the last subtile (its keys are all masked):
-          // a conditional half would make every wait count conservative
-          m16_compute(st, kb1, q_lds, vs, a.scale_log2, k0 + M16_SUB * (s + M16_WAVES), k1, nrow, lane, li, g);
-          __builtin_amdgcn_sched_barrier(0);
-          m16_load(kb1, key_row(a, blk3, t0 + 3 * STEP, k1), g);
-          blk3 = key_block(a, btr, t0 + 5 * STEP);
-          __builtin_amdgcn_sched_barrier(0);
-          t0 += 2 * STEP;
-        }
-        float l_row = st.l_part;
-        l_row += __shfl_xor(l_row, 16, 64);
-        l_row += __shfl_xor(l_row, 32, 64);
-
-        // merge the waves' states of the 16 rows in LDS, in a fixed wave order
-        __syncthreads();
-        if (g == 0) mrg_m[wave][li] = st.m_ref;
-        __syncthreads();
-        float M = NEG_INF;
-#pragma unroll
-        for (int wv = 0; wv < M16_WAVES; ++wv) M = fmaxf(M, mrg_m[wv][li]);
-        const float f = (st.m_ref == NEG_INF) ? 0.f : fast_exp2(st.m_ref - M);
-        for (int wv = 0; wv < M16_WAVES; ++wv) {
-          if (wave == wv) {
-#pragma unroll
-            for (int mt = 0; mt < 32; ++mt)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                float* dst = &mrg_o[(16 * mt + 4 * g + i) * M16_MRG_LD + li];
-                *dst = (wv == 0 ? 0.f : *dst) + st.o[mt][i] * f;
-              }
-            if (g == 0) mrg_l[li] = (wv == 0 ? 0.f : mrg_l[li]) + l_row * f;
-          }
-          __syncthreads();
-        }
-        const int slot = w + bb * a.n_rt + rt;
-        float* ps = a.partials + (int64_t)slot * (M16_ROWS * D_V + 2 * M16_ROWS);
-        for (int e = tid; e < D_V * M16_ROWS; e += M16_THREADS)
-          ps[e] = mrg_o[(e >> 4) * M16_MRG_LD + (e & 15)];
-        if (tid < M16_ROWS) {
-          float Mt = NEG_INF;
-          for (int wv = 0; wv < M16_WAVES; ++wv) Mt = fmaxf(Mt, mrg_m[wv][tid]);
-          ps[D_V * M16_ROWS + tid] = Mt;
-          ps[D_V * M16_ROWS + M16_ROWS + tid] = mrg_l[tid];
-        }
-        __syncthreads();
+        piece(bb, rt, k0, k1, seq, tot);
       }
     }
     __syncthreads();
   }
+}
+
+// ---------------------------------------------------------------- LDS ring loads
+// Both kernel families stream key tiles into an LDS ring with direct
+// global->LDS loads (global_load_lds_dwordx4) issued from inline assembly and
+// waited on with explicit counts: the compiler does not know these loads, so
+// it neither drains them at every barrier nor serialises LDS reads behind
+// them.  Every loop iteration issues the same number of them (masked keys
+// read a zero row), which keeps the counts static.
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  // 64 lanes x 16 bytes from per-lane global addresses to lds_base + 16*lane
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(base) : "memory", "m0");
+}
+
+// A zero latent row: keys outside the piece (or with an invalid block id)
+// are loaded from here, so every lane issues the same loads and the V rows
+// of masked keys are exact zeros (0 * NaN garbage would poison P*V).
+__device__ __attribute__((aligned(64))) const uint4 kZeroRow[ROW_BYTES / 16] = {};
+
+__device__ __forceinline__ int block_of(const DecodeArgs& a, int t) {
+  return a.bs_shift >= 0 ? (t >> a.bs_shift) : t / a.bs;
+}
+
+// Row address of local key t (block-table entries of blocks e0.. in bt_lds),
+// or the zero row when t >= k1 or the block id is invalid.
+__device__ __forceinline__ const uint8_t* ring_row(const DecodeArgs& a, const int* bt_lds, int e0, int t, int k1) {
+  const uint8_t* rowp = reinterpret_cast<const uint8_t*>(kZeroRow);
+  asm volatile("" : "+v"(rowp));
+  if (t < k1) {
+    const int vb = block_of(a, t);
+    const int blk = bt_lds[vb - e0];
+    if ((unsigned)blk < (unsigned)a.num_blocks) rowp = a.kv + ((int64_t)blk * a.bs + (t - vb * a.bs)) * ROW_BYTES;
+  }
+  return rowp;
+}
+
+// ---------------------------------------------------------------- M16 partial
+// Memory-bound family: up to 16 rows per request (single-token decode with up
+// to 16 heads and similar), any block size.  256 threads = 4 waves per
+// workgroup, one workgroup per CU.  32-key tiles stream through a 4-stage LDS
+// ring (three tiles, 108 KiB, in flight per CU while one is computed).  Every
+// wave computes the full 16 x 32 score tile S^T = K Q^T itself
+// (v_mfma_f32_16x16x32_bf16, K from LDS, Q^T in 72 registers), so all four
+// waves hold the same online-softmax state and no merge is needed; the waves
+// split the 512 value columns instead: wave w accumulates
+// O^T[128w .. 128w+127][16 rows] (8 x 16 x 16 fp32 tiles, 32 MFMA
+// registers) with V^T from LDS by ds_read_b64_tr_b16.
+//
+// Stage layout: two 16-key halves of 18 KiB.  Within a half, 16-byte chunk c
+// of key row r sits at byte 1024*(c/4) + 16*(16*(c%4) + (r ^ 4*(c&1))): one
+// load instruction fills 1 KiB with 4 consecutive chunks of all 16 rows, the
+// K reads of an MFMA step are one contiguous 1 KiB, and the transposed V reads
+// (4 rows x 32 bytes per 16 lanes) hit 16 distinct 8-byte bank slots.
+constexpr int M16_THREADS = 256;
+constexpr int M16_ROWS = 16;
+constexpr int M16_TILE = 32;                       // keys per tile
+constexpr int M16_HALF = 16 * ROW_BYTES;           // 18 KiB
+constexpr int M16_STAGE = 2 * M16_HALF;            // 36 KiB
+constexpr int M16_NS = 4;                          // ring stages
+constexpr int M16_DMA_PER_WAVE = 9;                // 1 KiB load instructions per wave per tile
+constexpr int M16_BT_WIN = 1024;                   // block-table entries held in LDS per sub-piece
+constexpr int M16_DV_WAVE = D_V / 4;               // value columns per wave
+constexpr float M16_RESCALE_LOG2 = 8.f;            // keep exponentials <= 2^8 between rescales
+
+static_assert(M16_STAGE == 4 * M16_DMA_PER_WAVE * 1024, "a stage is exactly the four waves' loads");
+
+// Issue this wave's 9 loads of tile [ts, ts+32): wave w fills half w/2,
+// chunks 36*(w%2) .. 36*(w%2)+35 of its 16 rows.  Lane l loads row
+// (l%16) ^ 4*((l/16)&1), chunk 4m' + l/16 with m' = 9*(w%2) + m, which the
+// instruction writes to 1024*m' + 16*l of the half: the layout above.
+__device__ __forceinline__ void m16_issue_tile(const DecodeArgs& a, const int* bt_lds, int e0, int ts, int k1,
+                                               uint32_t stage_lds, int wave, int lane) {
+  const int gq = lane >> 4;
+  const int r = (lane & 15) ^ (4 * (gq & 1));
+  const uint8_t* rowp = ring_row(a, bt_lds, e0, ts + 16 * (wave >> 1) + r, k1) + 16 * gq + 576 * (wave & 1);
+#pragma unroll
+  for (int m = 0; m < M16_DMA_PER_WAVE; ++m)
+    dma16(rowp + 64 * m, stage_lds + 1024 * (M16_DMA_PER_WAVE * wave + m));
+}
+
+struct M16State {
+  f32x4 o[8];
+  float m_ref, l_part;
+};
+
+// One 32-key tile: S^T = K Q^T for both halves, online softmax with a lazily
+// moved reference max, then this wave's quarter of O^T += V^T P^T.
+__device__ __forceinline__ void m16_compute(M16State& st, const bf16x8 (&qf)[18], const uint8_t* stage,
+                                            float scale_log2, int ts, int k1, int nrow, int lane, int wave) {
+  const int li = lane & 15, g = lane >> 4;
+  // S^T[key][row]: lane (li, g) gets keys 4g+e of each half for row li; the
+  // K fragment of k-step kk is chunk 4kk+g of key row li
+  const uint8_t* kp = stage + 16 * (16 * g + (li ^ (4 * (g & 1))));
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  bf16x8 ka[3], kb[3];
+  ka[0] = *reinterpret_cast<const bf16x8*>(kp);
+  kb[0] = *reinterpret_cast<const bf16x8*>(kp + M16_HALF);
+  ka[1] = *reinterpret_cast<const bf16x8*>(kp + 1024);
+  kb[1] = *reinterpret_cast<const bf16x8*>(kp + M16_HALF + 1024);
+  // the scheduling barriers keep each step's reads two steps ahead of their
+  // MFMAs (left alone, the scheduler sinks every read next to its use and
+  // the LDS latency is exposed at each step)
+#pragma unroll
+  for (int kk = 0; kk < 18; ++kk) {
+    if (kk + 2 < 18) {
+      ka[(kk + 2) % 3] = *reinterpret_cast<const bf16x8*>(kp + 1024 * (kk + 2));
+      kb[(kk + 2) % 3] = *reinterpret_cast<const bf16x8*>(kp + M16_HALF + 1024 * (kk + 2));
+    }
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk % 3], qf[kk], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk % 3], qf[kk], s1, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  float p[8];
+  float mx = NEG_INF;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int t0 = ts + 4 * g + e, t1 = t0 + 16;
+    p[e] = (t0 < k1 && t0 < nrow) ? s0[e] * scale_log2 : NEG_INF;
+    p[4 + e] = (t1 < k1 && t1 < nrow) ? s1[e] * scale_log2 : NEG_INF;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mx = fmaxf(mx, p[e]);
+  // move the reference only when some row's max grew by more than 2^8 over it
+  if (__ballot(mx > st.m_ref + M16_RESCALE_LOG2) != 0) {
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (mx > st.m_ref + M16_RESCALE_LOG2) {
+      const float alpha = fast_exp2(st.m_ref - mx);
+      st.l_part *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // in place on the accumulator register (a plain multiply makes the
+          // register allocator copy every accumulator out of the MFMA
+          // registers at each tile)
+          float tmp;
+          asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                       : "+a"(st.o[mt][i]), "=&v"(tmp) : "v"(alpha));
+        }
+      st.m_ref = mx;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    p[e] = (p[e] == NEG_INF) ? 0.f : fast_exp2(p[e] - st.m_ref);
+    st.l_part += p[e];
+  }
+  // P^T as the B operand: contraction slot 8g+e is key 4g+e of half e/4
+  const bf16x4 plo = to_bf16x4(p[0], p[1], p[2], p[3]);
+  const bf16x4 phi = to_bf16x4(p[4], p[5], p[6], p[7]);
+  const bf16x8 pf = __builtin_shufflevector(plo, phi, 0, 1, 2, 3, 4, 5, 6, 7);
+  // V^T fragments: lane (li, g) of a transposed read points at key row
+  // 4g + li/4, value columns 16T + 4(li%4) .. +3 (chunk 2T + (li/2)%2, byte
+  // 8(li%2)) and receives column 16T + li of the 4 rows; T = 8*wave + mt
+  const int b1 = (li >> 1) & 1;
+  const uint8_t* vp = stage + 256 * b1 + 16 * ((4 * g + (li >> 2)) ^ (4 * b1)) + 8 * (li & 1) +
+                      (M16_DV_WAVE / 16) * 512 * wave;
+  i16x4 v[8][2];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    v[mt][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 512 * mt));
+    v[mt][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + M16_HALF + 512 * mt));
+  }
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    const bf16x4 a0 = __builtin_bit_cast(bf16x4, v[mt][0]);
+    const bf16x4 a1 = __builtin_bit_cast(bf16x4, v[mt][1]);
+    st.o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                       pf, st.o[mt], 0, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[M16_NS * M16_STAGE];
+  __shared__ int bt_lds[M16_BT_WIN];
+  __shared__ int64_t s_red[M16_THREADS / 64];
+  __shared__ int64_t s_excl[M16_THREADS];
+  __shared__ int s_first_last[2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, g = lane >> 4;
+  const int w = xcd_range_index(blockIdx.x, a.G);
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
+
+  for_each_piece<M16_THREADS>(a, w, s_red, s_excl, s_first_last, [&](int bb, int rt, int k0, int k1, int seq,
+                                                                    int tot) {
+    // ---- one piece: rows [16 rt, 16 rt + 16) of request bb, keys [k0, k1)
+    const int32_t* btr = a.bt + (int64_t)bb * a.max_blocks;
+    const int my_row = rt * M16_ROWS + li;
+    const bool row_ok = my_row < a.R;
+    const int nrow = row_ok ? row_bound(seq, tot, a.Q, my_row / a.H, a.W, a.rank, a.causal) : 0;
+    // Q^T fragments: lane (li, g) holds dims 32kk + 8g .. +7 of row li
+    bf16x8 qf[18];
+    {
+      const uint8_t* qrow = a.q + ((int64_t)bb * a.R + (row_ok ? my_row : 0)) * ROW_BYTES + 16 * g;
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) qf[kk] = row_ok ? gload_bf16x8(qrow + 64 * kk) : zero_bf16x8();
+      // wait for Q here, before any ring load is in flight: a first use
+      // inside the tile loop would make the compiler wait for every load
+      // there, on every iteration
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) asm volatile("" ::"v"(qf[kk]));
+    }
+    M16State st;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) st.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m_ref = NEG_INF;
+    st.l_part = 0.f;
+
+    // sub-pieces whose block-table span fits the LDS window
+    const int span_keys = (M16_BT_WIN - 1) * a.bs;
+    for (int ka = k0; ka < k1; ka += span_keys) {
+      const int kb = (k1 - ka) < span_keys ? k1 : ka + span_keys;
+      const int e0 = block_of(a, ka), e1 = block_of(a, kb - 1);
+      __syncthreads();  // the previous sub-piece is done with the window and the ring
+      for (int e = e0 + tid; e <= e1; e += M16_THREADS) bt_lds[e - e0] = e < a.max_blocks ? gload_i32(btr + e) : -1;
+      __syncthreads();
+      const int nt = (kb - ka + M16_TILE - 1) / M16_TILE;
+#pragma unroll
+      for (int s = 0; s < M16_NS - 1; ++s)
+        m16_issue_tile(a, bt_lds, e0, ka + s * M16_TILE, kb, ring_lds + s * M16_STAGE, wave, lane);
+      for (int it = 0; it < nt; ++it) {
+        // tile it landed (tiles it+1 .. it+NS-2 may still be in flight), and
+        // after the barrier every wave is done computing tile it-1 ...
+        WAIT_VMCNT(M16_DMA_PER_WAVE * (M16_NS - 2));
+        __syncthreads();
+        // ... so its stage can take tile it+NS-1
+        m16_issue_tile(a, bt_lds, e0, ka + (it + M16_NS - 1) * M16_TILE, kb,
+                       ring_lds + ((it + M16_NS - 1) % M16_NS) * M16_STAGE, wave, lane);
+        m16_compute(st, qf, ring + (it % M16_NS) * M16_STAGE, a.scale_log2, ka + it * M16_TILE, kb, nrow, lane,
+                    wave);
+      }
+      WAIT_VMCNT(0);
+    }
+    // partial slot: wave w's O^T tiles T = 8w + mt in the accumulator layout
+    // [T][lane][4] (one 16-byte store per lane and tile), then m and l per row
+    float l_row = st.l_part;
+    l_row += __shfl_xor(l_row, 16, 64);
+    l_row += __shfl_xor(l_row, 32, 64);
+    const int slot = w + bb * a.n_rt + rt;
+    float* ps = a.partials + (int64_t)slot * (M16_ROWS * D_V + 2 * M16_ROWS);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+      *reinterpret_cast<f32x4*>(ps + ((M16_DV_WAVE / 16) * wave + mt) * 256 + 4 * lane) = st.o[mt];
+    if (wave == 0 && g == 0) {
+      ps[M16_ROWS * D_V + li] = st.m_ref;
+      ps[M16_ROWS * D_V + M16_ROWS + li] = l_row;
+    }
+  });
 }
 
 // ---------------------------------------------------------------- R128 partial
@@ -412,15 +452,6 @@ constexpr int R128_QLDS = 36 - R128_QREG;
 constexpr float R128_RESCALE_LOG2 = 8.f;
 
 static_assert(R128_STAGE == 4 * R128_DMA_PER_WAVE * 1024, "a stage is exactly the four waves' loads");
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-#define R128_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
-
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  // 64 lanes x 16 bytes from per-lane global addresses to lds_base + 16*lane
-  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(base) : "memory", "m0");
-}
 
 // Swizzle of the 16-byte chunks of a key row in LDS: logical chunk c of row r
 // sits at (c & ~7) | ((c ^ f(r)) & 7), f(r) = g((r >> 1) & 7) with
@@ -590,9 +621,9 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
   __shared__ __attribute__((aligned(1024))) uint8_t ring[R128_NS * R128_STAGE];
   __shared__ int bt_lds[R128_BT_WIN];
   __shared__ __attribute__((aligned(16))) uint8_t q_tail_lds[4][R128_QLDS * 64 * 16];
-  __shared__ int64_t s_red[4];
+  __shared__ int64_t s_red[R128_THREADS / 64];
   __shared__ int64_t s_excl[R128_THREADS];
-  __shared__ int s_first, s_last;
+  __shared__ int s_first_last[2];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int w = xcd_range_index(blockIdx.x, a.G);
@@ -609,118 +640,76 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
     dma_sel_off[m] = 16 * c | ((row_rel != (64 * m) / 72) ? (1 << 15) : 0);
   }
 
-  int64_t T = 0;
-  for (int base = 0; base < a.B; base += R128_THREADS) {
-    const int b = base + tid;
-    T += block_sum_i64<R128_THREADS>(b < a.B ? (int64_t)a.n_rt * request_keys(a, b) : 0, s_red);
-  }
-  const int64_t u0 = (int64_t)w * T / a.G, u1 = (int64_t)(w + 1) * T / a.G;
-
-  int64_t carry = 0;
-  for (int base = 0; base < a.B; base += R128_THREADS) {
-    const int b = base + tid;
-    const int64_t x = b < a.B ? (int64_t)a.n_rt * request_keys(a, b) : 0;
-    int64_t chunk_total;
-    const int64_t incl = block_incl_scan_i64<R128_THREADS>(x, s_red, chunk_total) + carry;
-    const int64_t excl = incl - x;
-    if (w == 0 && b < a.B) {
-      a.prefix[b + 1] = incl;
-      if (b == 0) a.prefix[0] = 0;
+  for_each_piece<R128_THREADS>(a, w, s_red, s_excl, s_first_last, [&](int bb, int rt, int k0, int k1, int seq,
+                                                                     int tot) {
+    // ---- one piece: rows [128 rt, 128 rt + 128) of request bb, keys [k0, k1)
+    const int32_t* btr = a.bt + (int64_t)bb * a.max_blocks;
+    const int my_row = rt * R128_ROWS + wave * 32 + (lane & 31);
+    const bool row_ok = my_row < a.R;
+    const int nrow = row_ok ? row_bound(seq, tot, a.Q, my_row / a.H, a.W, a.rank, a.causal) : 0;
+    bf16x8 qf[R128_QREG];
+    uint8_t* q_tail = q_tail_lds[wave];
+    {
+      const uint8_t* qrow = a.q + ((int64_t)bb * a.R + (row_ok ? my_row : 0)) * ROW_BYTES + 16 * (lane >> 5);
+#pragma unroll
+      for (int kk = 0; kk < R128_QREG; ++kk) qf[kk] = row_ok ? gload_bf16x8(qrow + 32 * kk) : zero_bf16x8();
+#pragma unroll
+      for (int kk = 0; kk < R128_QLDS; ++kk)
+        *reinterpret_cast<bf16x8*>(q_tail + (kk * 64 + lane) * 16) =
+            row_ok ? gload_bf16x8(qrow + 32 * (R128_QREG + kk)) : zero_bf16x8();
     }
-    s_excl[tid] = excl;
-    if (tid == 0) { s_first = 0x7fffffff; s_last = -1; }
-    __syncthreads();
-    if (x > 0 && excl < u1 && incl > u0) {
-      atomicMin(&s_first, tid);
-      atomicMax(&s_last, tid);
-    }
-    __syncthreads();
-    const int first = s_first, last = s_last;
-    carry += chunk_total;
+    R128State st;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) st.o[m] = f32x16{};
+    st.m_ref = NEG_INF;
+    st.l_part = 0.f;
 
-    for (int ii = first; ii <= last; ++ii) {
-      const int bb = __builtin_amdgcn_readfirstlane(base + ii);
-      const int64_t pb = s_excl[ii];
-      const int nb = __builtin_amdgcn_readfirstlane(request_keys(a, bb));
-      const int seq = __builtin_amdgcn_readfirstlane(a.seq_lens[bb]);
-      const int tot = __builtin_amdgcn_readfirstlane(request_tot(a, bb, seq));
-      const int32_t* btr = a.bt + (int64_t)bb * a.max_blocks;
-      const int64_t lo = u0 > pb ? u0 - pb : 0;
-      const int64_t hi = (u1 - pb) < (int64_t)a.n_rt * nb ? u1 - pb : (int64_t)a.n_rt * nb;
-      for (int rt = (int)(lo / nb); (int64_t)rt * nb < hi; ++rt) {
-        const int k0 = __builtin_amdgcn_readfirstlane((int)((int64_t)rt * nb < lo ? lo - (int64_t)rt * nb : 0));
-        const int k1 = __builtin_amdgcn_readfirstlane((int)((int64_t)(rt + 1) * nb < hi ? nb : hi - (int64_t)rt * nb));
-        // ---- one piece: rows [128 rt, 128 rt + 128) of request bb, keys [k0, k1)
-        const int my_row = rt * R128_ROWS + wave * 32 + (lane & 31);
-        const bool row_ok = my_row < a.R;
-        const int nrow = row_ok ? row_bound(seq, tot, a.Q, my_row / a.H, a.W, a.rank, a.causal) : 0;
-        bf16x8 qf[R128_QREG];
-        uint8_t* q_tail = q_tail_lds[wave];
-        {
-          const uint8_t* qrow = a.q + ((int64_t)bb * a.R + (row_ok ? my_row : 0)) * ROW_BYTES + 16 * (lane >> 5);
-#pragma unroll
-          for (int kk = 0; kk < R128_QREG; ++kk) qf[kk] = row_ok ? gload_bf16x8(qrow + 32 * kk) : zero_bf16x8();
-#pragma unroll
-          for (int kk = 0; kk < R128_QLDS; ++kk)
-            *reinterpret_cast<bf16x8*>(q_tail + (kk * 64 + lane) * 16) =
-                row_ok ? gload_bf16x8(qrow + 32 * (R128_QREG + kk)) : zero_bf16x8();
-        }
-        R128State st;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) st.o[m] = f32x16{};
-        st.m_ref = NEG_INF;
-        st.l_part = 0.f;
-
-        // sub-pieces whose block-table span fits the LDS window
-        const int span_keys = (R128_BT_WIN - 1) * a.bs;
-        for (int ka = k0; ka < k1; ka += span_keys) {
-          const int kb = (k1 - ka) < span_keys ? k1 : ka + span_keys;
-          const int e0 = block_of(a, ka), e1 = block_of(a, kb - 1);
-          __syncthreads();  // previous sub-piece done with the window and the ring
-          for (int e = e0 + tid; e <= e1; e += R128_THREADS)
-            bt_lds[e - e0] = e < a.max_blocks ? btr[e] : -1;
-          __syncthreads();
-          const int nt = (kb - ka + R128_TILE - 1) / R128_TILE;
-          // prologue: tiles 0 and 1
-          r128_issue_tile(a, bt_lds, e0, ka, kb, ring_lds, wave, lane, dma_sel_off);
-          r128_issue_tile(a, bt_lds, e0, ka + R128_TILE, kb, ring_lds + R128_STAGE, wave, lane, dma_sel_off);
-          for (int it = 0; it < nt; ++it) {
-            // tile it landed (only tile it+1 may still be in flight), then
-            // every wave is also done computing tile it-1 ...
-            R128_WAIT_VMCNT(R128_DMA_PER_WAVE);  // tile it+1's 9 loads may stay in flight
-            __syncthreads();
-            // ... so its stage can take tile it+2
-            r128_issue_tile(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb,
-                            ring_lds + ((it + 2) % R128_NS) * R128_STAGE, wave, lane, dma_sel_off);
-            r128_compute(st, qf, q_tail, ring + (it % R128_NS) * R128_STAGE, a.scale_log2, ka + it * R128_TILE,
-                         kb, nrow, lane);
-          }
-          R128_WAIT_VMCNT(0);
-        }
-        // partial slot: O^T in the accumulator layout [m][row][h][i] (the 16
-        // values a lane holds per 32x32 tile are contiguous: 4 x 16-byte
-        // stores), then m and l per row
-        float l_row = st.l_part + __shfl_xor(st.l_part, 32, 64);
-        const int slot = w + bb * a.n_rt + rt;
-        float* ps = a.partials + (int64_t)slot * (R128_ROWS * D_V + 2 * R128_ROWS);
-        const int prow = wave * 32 + (lane & 31), h = lane >> 5;
-        float* pl = ps + (prow * 2 + h) * 16;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            *reinterpret_cast<f32x4*>(pl + m * (R128_ROWS * 32) + 4 * c) =
-                f32x4{st.o[m][4 * c], st.o[m][4 * c + 1], st.o[m][4 * c + 2], st.o[m][4 * c + 3]};
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (h == 0) {
-          ps[R128_ROWS * D_V + prow] = st.m_ref;
-          ps[R128_ROWS * D_V + R128_ROWS + prow] = l_row;
-        }
+    // sub-pieces whose block-table span fits the LDS window
+    const int span_keys = (R128_BT_WIN - 1) * a.bs;
+    for (int ka = k0; ka < k1; ka += span_keys) {
+      const int kb = (k1 - ka) < span_keys ? k1 : ka + span_keys;
+      const int e0 = block_of(a, ka), e1 = block_of(a, kb - 1);
+      __syncthreads();  // previous sub-piece done with the window and the ring
+      for (int e = e0 + tid; e <= e1; e += R128_THREADS) bt_lds[e - e0] = e < a.max_blocks ? gload_i32(btr + e) : -1;
+      __syncthreads();
+      const int nt = (kb - ka + R128_TILE - 1) / R128_TILE;
+      // prologue: tiles 0 and 1
+      r128_issue_tile(a, bt_lds, e0, ka, kb, ring_lds, wave, lane, dma_sel_off);
+      r128_issue_tile(a, bt_lds, e0, ka + R128_TILE, kb, ring_lds + R128_STAGE, wave, lane, dma_sel_off);
+      for (int it = 0; it < nt; ++it) {
+        // tile it landed (only tile it+1 may still be in flight), then
+        // every wave is also done computing tile it-1 ...
+        WAIT_VMCNT(R128_DMA_PER_WAVE);  // tile it+1's 9 loads may stay in flight
+        __syncthreads();
+        // ... so its stage can take tile it+2
+        r128_issue_tile(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb, ring_lds + ((it + 2) % R128_NS) * R128_STAGE,
+                        wave, lane, dma_sel_off);
+        r128_compute(st, qf, q_tail, ring + (it % R128_NS) * R128_STAGE, a.scale_log2, ka + it * R128_TILE, kb,
+                     nrow, lane);
       }
+      WAIT_VMCNT(0);
     }
-    __syncthreads();
-  }
+    // partial slot: O^T in the accumulator layout [m][row][h][i] (the 16
+    // values a lane holds per 32x32 tile are contiguous: 4 x 16-byte
+    // stores), then m and l per row
+    float l_row = st.l_part + __shfl_xor(st.l_part, 32, 64);
+    const int slot = w + bb * a.n_rt + rt;
+    float* ps = a.partials + (int64_t)slot * (R128_ROWS * D_V + 2 * R128_ROWS);
+    const int prow = wave * 32 + (lane & 31), h = lane >> 5;
+    float* pl = ps + (prow * 2 + h) * 16;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<f32x4*>(pl + m * (R128_ROWS * 32) + 4 * c) =
+            f32x4{st.o[m][4 * c], st.o[m][4 * c + 1], st.o[m][4 * c + 2], st.o[m][4 * c + 3]};
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (h == 0) {
+      ps[R128_ROWS * D_V + prow] = st.m_ref;
+      ps[R128_ROWS * D_V + R128_ROWS + prow] = l_row;
+    }
+  });
 }
 
 // ---------------------------------------------------------------- combine
@@ -728,12 +717,12 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
 // the partial slots of the workgroups that covered the group and writes bf16
 // out and (slice 0) the LSE.  Groups no workgroup covered (no visible keys)
 // get out = 0, lse = -inf.
-// Partial slot element (row, dv): the M16 kernel stores O^T as [dv][row];
-// the R128 kernel stores its accumulator layout [dv/32][row][h][i] with
-// dv % 32 = 8*(i/4) + 4h + i%4.
+// Partial slot element (row, dv): both kernels store their MFMA accumulator
+// layouts.  M16: [dv/16][g][row][i] with dv % 16 = 4g + i; R128:
+// [dv/32][row][h][i] with dv % 32 = 8*(i/4) + 4h + i%4.
 template <int ROWS>
 __device__ __forceinline__ int slot_index(int row, int dv) {
-  if (ROWS == M16_ROWS) return dv * ROWS + row;
+  if (ROWS == M16_ROWS) return (dv >> 4) * 256 + ((dv & 15) >> 2) * 64 + row * 4 + (dv & 3);
   const int r32 = dv & 31;
   return ((dv >> 5) * ROWS + row) * 32 + ((r32 >> 2) & 1) * 16 + (r32 >> 3) * 4 + (r32 & 3);
 }
