@@ -61,14 +61,15 @@ struct DecodeArgs {
   float* lse;              // [B*R] or null
 };
 
-__device__ __forceinline__ int request_tot(const DecodeArgs& a, int b, int seq) {
-  return a.glob ? a.glob[b] : seq;
-}
-
-// Keys of the largest row of request b (row j = q_len-1 has the longest prefix).
-__device__ __forceinline__ int request_keys(const DecodeArgs& a, int b) {
-  int seq = a.seq_lens[b];
-  return row_bound(seq, request_tot(a, b, seq), a.Q, a.Q - 1, a.W, a.rank, a.causal);
+// Key count of the largest row (row j = q_len-1 has the longest prefix),
+// local length and global length of request b; zeros past B.
+__device__ __forceinline__ void request_info(const DecodeArgs& a, int b, int& nb, int& seq, int& tot) {
+  nb = seq = tot = 0;
+  if (b < a.B) {
+    seq = gload_i32(a.seq_lens + b);
+    tot = a.glob ? gload_i32(a.glob + b) : seq;
+    nb = row_bound(seq, tot, a.Q, a.Q - 1, a.W, a.rank, a.causal);
+  }
 }
 
 // Workgroups are dispatched to the 8 XCDs round-robin (blockIdx % 8).  The
@@ -116,56 +117,78 @@ __device__ __forceinline__ int64_t block_incl_scan_i64(int64_t v, int64_t* s_red
 }
 
 // ---------------------------------------------------------------- work ranges
+template <int NT>
+struct PlanLds {
+  int64_t red[NT / 64];
+  int64_t excl[NT];
+  int nb[NT], seq[NT], tot[NT];
+  int first_last[2];
+};
+
 // Calls piece(bb, rt, k0, k1, seq, tot) for every (request, row tile) group
 // that overlaps this workgroup's balanced range of units, in unit order, with
 // the group's keys [k0, k1) inside the range.  Workgroup 0 also stores the
 // request offsets for the combine kernel.  All arguments of piece() are
-// wave-uniform.
+// wave-uniform.  With up to NT requests (the usual case) the lengths are
+// read from memory once and one block scan gives both the total and the
+// offsets.
 template <int NT, class F>
-__device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int w, int64_t* s_red, int64_t* s_excl,
-                                               int* s_first_last, F&& piece) {
+__device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int w, PlanLds<NT>& pl, F&& piece) {
   const int tid = threadIdx.x;
-  int64_t T = 0;
-  for (int base = 0; base < a.B; base += NT) {
-    const int b = base + tid;
-    T += block_sum_i64<NT>(b < a.B ? (int64_t)a.n_rt * request_keys(a, b) : 0, s_red);
+  int nb, seq, tot;
+  request_info(a, tid, nb, seq, tot);
+  int64_t total0;
+  const int64_t incl0 = block_incl_scan_i64<NT>((int64_t)a.n_rt * nb, pl.red, total0);
+  int64_t T = total0;
+  for (int base = NT; base < a.B; base += NT) {
+    int nb2, seq2, tot2;
+    request_info(a, base + tid, nb2, seq2, tot2);
+    T += block_sum_i64<NT>((int64_t)a.n_rt * nb2, pl.red);
   }
   const int64_t u0 = (int64_t)w * T / a.G, u1 = (int64_t)(w + 1) * T / a.G;
 
   int64_t carry = 0;
   for (int base = 0; base < a.B; base += NT) {
+    int64_t incl = incl0, chunk_total = total0;
+    if (base > 0) {
+      request_info(a, base + tid, nb, seq, tot);
+      incl = block_incl_scan_i64<NT>((int64_t)a.n_rt * nb, pl.red, chunk_total);
+    }
     const int b = base + tid;
-    const int64_t x = b < a.B ? (int64_t)a.n_rt * request_keys(a, b) : 0;
-    int64_t chunk_total;
-    const int64_t incl = block_incl_scan_i64<NT>(x, s_red, chunk_total) + carry;
+    const int64_t x = (int64_t)a.n_rt * nb;
+    incl += carry;
     const int64_t excl = incl - x;
     if (w == 0 && b < a.B) {
       a.prefix[b + 1] = incl;
       if (b == 0) a.prefix[0] = 0;
     }
-    s_excl[tid] = excl;
-    if (tid == 0) { s_first_last[0] = 0x7fffffff; s_first_last[1] = -1; }
+    pl.excl[tid] = excl;
+    pl.nb[tid] = nb;
+    pl.seq[tid] = seq;
+    pl.tot[tid] = tot;
+    if (tid == 0) { pl.first_last[0] = 0x7fffffff; pl.first_last[1] = -1; }
     __syncthreads();
     if (x > 0 && excl < u1 && incl > u0) {
-      atomicMin(&s_first_last[0], tid);
-      atomicMax(&s_first_last[1], tid);
+      atomicMin(&pl.first_last[0], tid);
+      atomicMax(&pl.first_last[1], tid);
     }
     __syncthreads();
-    const int first = s_first_last[0], last = s_first_last[1];
+    const int first = pl.first_last[0], last = pl.first_last[1];
     carry += chunk_total;
 
     for (int i = first; i <= last; ++i) {
       const int bb = __builtin_amdgcn_readfirstlane(base + i);
-      const int64_t pb = s_excl[i];
-      const int nb = __builtin_amdgcn_readfirstlane(request_keys(a, bb));
-      const int seq = __builtin_amdgcn_readfirstlane(a.seq_lens[bb]);
-      const int tot = __builtin_amdgcn_readfirstlane(request_tot(a, bb, seq));
+      const int64_t pb = pl.excl[i];
+      const int nbb = __builtin_amdgcn_readfirstlane(pl.nb[i]);
+      const int sq = __builtin_amdgcn_readfirstlane(pl.seq[i]);
+      const int tt = __builtin_amdgcn_readfirstlane(pl.tot[i]);
       const int64_t lo = u0 > pb ? u0 - pb : 0;  // first unit of the request in range
-      const int64_t hi = (u1 - pb) < (int64_t)a.n_rt * nb ? u1 - pb : (int64_t)a.n_rt * nb;
-      for (int rt = (int)(lo / nb); (int64_t)rt * nb < hi; ++rt) {
-        const int k0 = __builtin_amdgcn_readfirstlane((int)((int64_t)rt * nb < lo ? lo - (int64_t)rt * nb : 0));
-        const int k1 = __builtin_amdgcn_readfirstlane((int)((int64_t)(rt + 1) * nb < hi ? nb : hi - (int64_t)rt * nb));
-        piece(bb, rt, k0, k1, seq, tot);
+      const int64_t hi = (u1 - pb) < (int64_t)a.n_rt * nbb ? u1 - pb : (int64_t)a.n_rt * nbb;
+      for (int rt = (int)(lo / nbb); (int64_t)rt * nbb < hi; ++rt) {
+        const int k0 = __builtin_amdgcn_readfirstlane((int)((int64_t)rt * nbb < lo ? lo - (int64_t)rt * nbb : 0));
+        const int k1 =
+            __builtin_amdgcn_readfirstlane((int)((int64_t)(rt + 1) * nbb < hi ? nbb : hi - (int64_t)rt * nbb));
+        piece(bb, rt, k0, k1, sq, tt);
       }
     }
     __syncthreads();
@@ -215,19 +238,30 @@ __device__ __forceinline__ const uint8_t* ring_row(const DecodeArgs& a, const in
 // Memory-bound family: up to 16 rows per request (single-token decode with up
 // to 16 heads and similar), any block size.  256 threads = 4 waves per
 // workgroup, one workgroup per CU.  32-key tiles stream through a 4-stage LDS
-// ring (three tiles, 108 KiB, in flight per CU while one is computed).  Every
-// wave computes the full 16 x 32 score tile S^T = K Q^T itself
-// (v_mfma_f32_16x16x32_bf16, K from LDS, Q^T in 72 registers), so all four
-// waves hold the same online-softmax state and no merge is needed; the waves
-// split the 512 value columns instead: wave w accumulates
-// O^T[128w .. 128w+127][16 rows] (8 x 16 x 16 fp32 tiles, 32 MFMA
-// registers) with V^T from LDS by ds_read_b64_tr_b16.
+// ring (three tiles, 108 KiB, in flight per CU while one is computed).
+//
+// Work split.  The 16 x 32 score tile S^T = K Q^T (v_mfma_f32_16x16x32_bf16,
+// K from LDS, Q^T in registers) is cut four ways: wave w computes the keys of
+// half w%2 over dims [288 (w/2), 288 (w/2) + 288), 9 MFMA steps.  The fp32
+// partial tiles go through LDS and every wave adds them up in the same order,
+// so all four waves hold bit-identical scores and the same online-softmax
+// state; no merge is needed at the end.  The 512 value columns are split
+// instead: wave w accumulates O^T[128w .. 128w+127][16 rows] (8 x 16 x 16
+// fp32 tiles, 32 MFMA registers) with V^T from LDS by ds_read_b64_tr_b16.
 //
 // Stage layout: two 16-key halves of 18 KiB.  Within a half, 16-byte chunk c
 // of key row r sits at byte 1024*(c/4) + 16*(16*(c%4) + (r ^ 4*(c&1))): one
 // load instruction fills 1 KiB with 4 consecutive chunks of all 16 rows, the
 // K reads of an MFMA step are one contiguous 1 KiB, and the transposed V reads
 // (4 rows x 32 bytes per 16 lanes) hit 16 distinct 8-byte bank slots.
+//
+// Pipeline.  The ring items are, per piece, the query rows (loaded through
+// the ring like a key half, then read into registers) followed by the
+// piece's key tiles, so neither a new request nor a new row tile drains the
+// ring.  The block-table entries of all pieces of a batch are staged in LDS
+// first; a batch ends when the LDS window or the segment list is full, and a
+// piece too long for one window continues in the next batch with its state
+// kept in registers.
 constexpr int M16_THREADS = 256;
 constexpr int M16_ROWS = 16;
 constexpr int M16_TILE = 32;                       // keys per tile
@@ -235,58 +269,121 @@ constexpr int M16_HALF = 16 * ROW_BYTES;           // 18 KiB
 constexpr int M16_STAGE = 2 * M16_HALF;            // 36 KiB
 constexpr int M16_NS = 4;                          // ring stages
 constexpr int M16_DMA_PER_WAVE = 9;                // 1 KiB load instructions per wave per tile
-constexpr int M16_BT_WIN = 1024;                   // block-table entries held in LDS per sub-piece
+constexpr int M16_KSTEPS = 9;                      // 32-dim MFMA steps per wave (half of 576)
+constexpr int M16_BT_WIN = 1024;                   // block-table entries held in LDS per batch
+constexpr int M16_MAXSEG = 16;                     // segments per batch
 constexpr int M16_DV_WAVE = D_V / 4;               // value columns per wave
 constexpr float M16_RESCALE_LOG2 = 8.f;            // keep exponentials <= 2^8 between rescales
+constexpr int M16_SEG_FIRST = 1;   // segment starts its (request, row tile) group: a Q item precedes it
+constexpr int M16_SEG_LAST = 2;    // segment ends its group: the partial is written after its last tile
 
 static_assert(M16_STAGE == 4 * M16_DMA_PER_WAVE * 1024, "a stage is exactly the four waves' loads");
-
-// Issue this wave's 9 loads of tile [ts, ts+32): wave w fills half w/2,
-// chunks 36*(w%2) .. 36*(w%2)+35 of its 16 rows.  Lane l loads row
-// (l%16) ^ 4*((l/16)&1), chunk 4m' + l/16 with m' = 9*(w%2) + m, which the
-// instruction writes to 1024*m' + 16*l of the half: the layout above.
-__device__ __forceinline__ void m16_issue_tile(const DecodeArgs& a, const int* bt_lds, int e0, int ts, int k1,
-                                               uint32_t stage_lds, int wave, int lane) {
-  const int gq = lane >> 4;
-  const int r = (lane & 15) ^ (4 * (gq & 1));
-  const uint8_t* rowp = ring_row(a, bt_lds, e0, ts + 16 * (wave >> 1) + r, k1) + 16 * gq + 576 * (wave & 1);
-#pragma unroll
-  for (int m = 0; m < M16_DMA_PER_WAVE; ++m)
-    dma16(rowp + 64 * m, stage_lds + 1024 * (M16_DMA_PER_WAVE * wave + m));
-}
 
 struct M16State {
   f32x4 o[8];
   float m_ref, l_part;
 };
 
-// One 32-key tile: S^T = K Q^T for both halves, online softmax with a lazily
-// moved reference max, then this wave's quarter of O^T += V^T P^T.
-__device__ __forceinline__ void m16_compute(M16State& st, const bf16x8 (&qf)[18], const uint8_t* stage,
-                                            float scale_log2, int ts, int k1, int nrow, int lane, int wave) {
-  const int li = lane & 15, g = lane >> 4;
-  // S^T[key][row]: lane (li, g) gets keys 4g+e of each half for row li; the
-  // K fragment of k-step kk is chunk 4kk+g of key row li
-  const uint8_t* kp = stage + 16 * (16 * g + (li ^ (4 * (g & 1))));
-  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-  bf16x8 ka[3], kb[3];
-  ka[0] = *reinterpret_cast<const bf16x8*>(kp);
-  kb[0] = *reinterpret_cast<const bf16x8*>(kp + M16_HALF);
-  ka[1] = *reinterpret_cast<const bf16x8*>(kp + 1024);
-  kb[1] = *reinterpret_cast<const bf16x8*>(kp + M16_HALF + 1024);
-  // the scheduling barriers keep each step's reads two steps ahead of their
-  // MFMAs (left alone, the scheduler sinks every read next to its use and
-  // the LDS latency is exposed at each step)
-#pragma unroll
-  for (int kk = 0; kk < 18; ++kk) {
-    if (kk + 2 < 18) {
-      ka[(kk + 2) % 3] = *reinterpret_cast<const bf16x8*>(kp + 1024 * (kk + 2));
-      kb[(kk + 2) % 3] = *reinterpret_cast<const bf16x8*>(kp + M16_HALF + 1024 * (kk + 2));
-    }
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk % 3], qf[kk], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk % 3], qf[kk], s1, 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+struct M16Seg {
+  int bb, rt, ka, kb, seq, tot, e_base, flags;
+};
+
+// Ring position: segment s (with its descriptor), tile j (-1: the segment's
+// Q item).  s >= nseg: past the end.
+struct M16Cursor {
+  int s, j, nt;
+  M16Seg d;
+};
+
+__device__ __forceinline__ void m16_load_seg(M16Cursor& c, const M16Seg* segs, int nseg) {
+  if (c.s >= nseg) return;
+  const M16Seg d = segs[c.s];
+  c.d.bb = __builtin_amdgcn_readfirstlane(d.bb);
+  c.d.rt = __builtin_amdgcn_readfirstlane(d.rt);
+  c.d.ka = __builtin_amdgcn_readfirstlane(d.ka);
+  c.d.kb = __builtin_amdgcn_readfirstlane(d.kb);
+  c.d.seq = __builtin_amdgcn_readfirstlane(d.seq);
+  c.d.tot = __builtin_amdgcn_readfirstlane(d.tot);
+  c.d.e_base = __builtin_amdgcn_readfirstlane(d.e_base);
+  c.d.flags = __builtin_amdgcn_readfirstlane(d.flags);
+  c.nt = (c.d.kb - c.d.ka + M16_TILE - 1) / M16_TILE;
+  c.j = (c.d.flags & M16_SEG_FIRST) ? -1 : 0;
+}
+
+__device__ __forceinline__ void m16_advance(M16Cursor& c, const M16Seg* segs, int nseg) {
+  if (c.s >= nseg) return;
+  if (c.j + 1 < c.nt) {
+    ++c.j;
+  } else {
+    ++c.s;
+    m16_load_seg(c, segs, nseg);
   }
+}
+
+// Issue this wave's 9 loads of ring item c: wave w fills half w/2, chunks
+// 36*(w%2) .. 36*(w%2)+35 of its 16 rows.  Lane l loads row
+// (l%16) ^ 4*((l/16)&1), chunk 4m' + l/16 with m' = 9*(w%2) + m, which the
+// instruction writes to 1024*m' + 16*l of the half: the layout above.  A Q
+// item loads the group's 16 query rows into half 0 (waves 0 and 1); items
+// past the end, and the other half of a Q item, load the zero row, so every
+// wave issues 9 loads per item.
+__device__ __forceinline__ void m16_issue_item(const DecodeArgs& a, const int* bt_lds, int nseg, const M16Cursor& c,
+                                               uint32_t stage_lds, int wave, int lane) {
+  const int gq = lane >> 4;
+  const int r = (lane & 15) ^ (4 * (gq & 1));
+  const uint8_t* rowp = reinterpret_cast<const uint8_t*>(kZeroRow);
+  asm volatile("" : "+v"(rowp));
+  if (c.s < nseg) {
+    if (c.j < 0) {
+      const int qr = c.d.rt * M16_ROWS + r;
+      if (wave < 2 && qr < a.R) rowp = a.q + ((int64_t)c.d.bb * a.R + qr) * ROW_BYTES;
+    } else {
+      const int t = c.d.ka + M16_TILE * c.j + 16 * (wave >> 1) + r;
+      if (t < c.d.kb) {
+        const int vb = block_of(a, t);
+        const int blk = bt_lds[c.d.e_base + vb];
+        if ((unsigned)blk < (unsigned)a.num_blocks) rowp = a.kv + ((int64_t)blk * a.bs + (t - vb * a.bs)) * ROW_BYTES;
+      }
+    }
+  }
+  rowp += 16 * gq + 576 * (wave & 1);
+#pragma unroll
+  for (int m = 0; m < M16_DMA_PER_WAVE; ++m)
+    dma16(rowp + 64 * m, stage_lds + 1024 * (M16_DMA_PER_WAVE * wave + m));
+}
+
+// One 32-key tile: this wave's quarter of S^T, the exchange of the partial
+// tiles, online softmax with a lazily moved reference max, then this wave's
+// quarter of O^T += V^T P^T.  qf holds the wave's 9 k-steps of Q^T.
+__device__ __forceinline__ void m16_compute(M16State& st, const bf16x8 (&qf)[M16_KSTEPS], const uint8_t* stage,
+                                            uint8_t* xchg, float scale_log2, int ts, int k1, int nrow, int lane,
+                                            int wave) {
+  const int li = lane & 15, g = lane >> 4;
+  // S^T[key][row] of half wave%2: lane (li, g) gets keys 4g+e for row li;
+  // the K fragment of k-step kk is chunk 4kk+g of key row li
+  const uint8_t* kp = stage + (wave & 1) * M16_HALF + 1024 * M16_KSTEPS * (wave >> 1) +
+                      16 * (16 * g + (li ^ (4 * (g & 1))));
+  f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+  bf16x8 kf[M16_KSTEPS];
+  // all nine reads first, then the MFMAs in two chains (one chain of nine
+  // dependent MFMAs would wait out the MFMA latency at every step)
+#pragma unroll
+  for (int kk = 0; kk < M16_KSTEPS; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(kp + 1024 * kk);
+#pragma unroll
+  for (int kk = 0; kk < M16_KSTEPS; ++kk) {
+    if (kk & 1)
+      sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[kk], sb, 0, 0, 0);
+    else
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[kk], sa, 0, 0, 0);
+  }
+  // exchange: xchg[w] holds wave w's partial tile in the accumulator layout
+  *reinterpret_cast<f32x4*>(xchg + 1024 * wave + 16 * lane) = sa + sb;
+  __syncthreads();
+  const f32x4 p0 = *reinterpret_cast<const f32x4*>(xchg + 16 * lane);
+  const f32x4 p1 = *reinterpret_cast<const f32x4*>(xchg + 1024 + 16 * lane);
+  const f32x4 p2 = *reinterpret_cast<const f32x4*>(xchg + 2048 + 16 * lane);
+  const f32x4 p3 = *reinterpret_cast<const f32x4*>(xchg + 3072 + 16 * lane);
+  const f32x4 s0 = p0 + p2, s1 = p1 + p3;  // same order in every wave: identical scores
   float p[8];
   float mx = NEG_INF;
 #pragma unroll
@@ -350,81 +447,116 @@ __device__ __forceinline__ void m16_compute(M16State& st, const bf16x8 (&qf)[18]
 
 __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[M16_NS * M16_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t xchg[4 * 1024];
   __shared__ int bt_lds[M16_BT_WIN];
-  __shared__ int64_t s_red[M16_THREADS / 64];
-  __shared__ int64_t s_excl[M16_THREADS];
-  __shared__ int s_first_last[2];
+  __shared__ M16Seg segs[M16_MAXSEG];
+  __shared__ PlanLds<M16_THREADS> plan;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, g = lane >> 4;
   const int w = xcd_range_index(blockIdx.x, a.G);
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
 
-  for_each_piece<M16_THREADS>(a, w, s_red, s_excl, s_first_last, [&](int bb, int rt, int k0, int k1, int seq,
-                                                                    int tot) {
-    // ---- one piece: rows [16 rt, 16 rt + 16) of request bb, keys [k0, k1)
-    const int32_t* btr = a.bt + (int64_t)bb * a.max_blocks;
-    const int my_row = rt * M16_ROWS + li;
-    const bool row_ok = my_row < a.R;
-    const int nrow = row_ok ? row_bound(seq, tot, a.Q, my_row / a.H, a.W, a.rank, a.causal) : 0;
-    // Q^T fragments: lane (li, g) holds dims 32kk + 8g .. +7 of row li
-    bf16x8 qf[18];
-    {
-      const uint8_t* qrow = a.q + ((int64_t)bb * a.R + (row_ok ? my_row : 0)) * ROW_BYTES + 16 * g;
+  // state of the group being computed; it survives batch boundaries
+  bf16x8 qf[M16_KSTEPS];
 #pragma unroll
-      for (int kk = 0; kk < 18; ++kk) qf[kk] = row_ok ? gload_bf16x8(qrow + 64 * kk) : zero_bf16x8();
-      // wait for Q here, before any ring load is in flight: a first use
-      // inside the tile loop would make the compiler wait for every load
-      // there, on every iteration
+  for (int kk = 0; kk < M16_KSTEPS; ++kk) qf[kk] = zero_bf16x8();
+  M16State st;
 #pragma unroll
-      for (int kk = 0; kk < 18; ++kk) asm volatile("" ::"v"(qf[kk]));
-    }
-    M16State st;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) st.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    st.m_ref = NEG_INF;
-    st.l_part = 0.f;
+  for (int mt = 0; mt < 8; ++mt) st.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m_ref = NEG_INF;
+  st.l_part = 0.f;
+  int nrow = 0;
+  int nseg = 0, nent = 0;  // segments and window entries of the batch being built
 
-    // sub-pieces whose block-table span fits the LDS window
-    const int span_keys = (M16_BT_WIN - 1) * a.bs;
-    for (int ka = k0; ka < k1; ka += span_keys) {
-      const int kb = (k1 - ka) < span_keys ? k1 : ka + span_keys;
-      const int e0 = block_of(a, ka), e1 = block_of(a, kb - 1);
-      __syncthreads();  // the previous sub-piece is done with the window and the ring
-      for (int e = e0 + tid; e <= e1; e += M16_THREADS) bt_lds[e - e0] = e < a.max_blocks ? gload_i32(btr + e) : -1;
-      __syncthreads();
-      const int nt = (kb - ka + M16_TILE - 1) / M16_TILE;
-#pragma unroll
-      for (int s = 0; s < M16_NS - 1; ++s)
-        m16_issue_tile(a, bt_lds, e0, ka + s * M16_TILE, kb, ring_lds + s * M16_STAGE, wave, lane);
-      for (int it = 0; it < nt; ++it) {
-        // tile it landed (tiles it+1 .. it+NS-2 may still be in flight), and
-        // after the barrier every wave is done computing tile it-1 ...
-        WAIT_VMCNT(M16_DMA_PER_WAVE * (M16_NS - 2));
-        __syncthreads();
-        // ... so its stage can take tile it+NS-1
-        m16_issue_tile(a, bt_lds, e0, ka + (it + M16_NS - 1) * M16_TILE, kb,
-                       ring_lds + ((it + M16_NS - 1) % M16_NS) * M16_STAGE, wave, lane);
-        m16_compute(st, qf, ring + (it % M16_NS) * M16_STAGE, a.scale_log2, ka + it * M16_TILE, kb, nrow, lane,
-                    wave);
-      }
-      WAIT_VMCNT(0);
+  auto run_batch = [&]() __attribute__((always_inline)) {
+    if (nseg == 0) return;
+    __syncthreads();  // window and segment list written
+    M16Cursor ci{0, 0, 0, {}};
+    m16_load_seg(ci, segs, nseg);
+    int n_items = 0;
+    for (int s = 0; s < nseg; ++s) {
+      const int fl = __builtin_amdgcn_readfirstlane(segs[s].flags);
+      const int ka = __builtin_amdgcn_readfirstlane(segs[s].ka), kb = __builtin_amdgcn_readfirstlane(segs[s].kb);
+      n_items += ((fl & M16_SEG_FIRST) ? 1 : 0) + (kb - ka + M16_TILE - 1) / M16_TILE;
     }
-    // partial slot: wave w's O^T tiles T = 8w + mt in the accumulator layout
-    // [T][lane][4] (one 16-byte store per lane and tile), then m and l per row
-    float l_row = st.l_part;
-    l_row += __shfl_xor(l_row, 16, 64);
-    l_row += __shfl_xor(l_row, 32, 64);
-    const int slot = w + bb * a.n_rt + rt;
-    float* ps = a.partials + (int64_t)slot * (M16_ROWS * D_V + 2 * M16_ROWS);
+    M16Cursor cc = ci;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-      *reinterpret_cast<f32x4*>(ps + ((M16_DV_WAVE / 16) * wave + mt) * 256 + 4 * lane) = st.o[mt];
-    if (wave == 0 && g == 0) {
-      ps[M16_ROWS * D_V + li] = st.m_ref;
-      ps[M16_ROWS * D_V + M16_ROWS + li] = l_row;
+    for (int p = 0; p < M16_NS - 1; ++p) {
+      m16_issue_item(a, bt_lds, nseg, ci, ring_lds + p * M16_STAGE, wave, lane);
+      m16_advance(ci, segs, nseg);
+    }
+    for (int it = 0; it < n_items; ++it) {
+      // item it landed (items it+1 .. it+NS-2 may still be in flight), and
+      // after the barrier every wave is done with item it-1 ...
+      WAIT_VMCNT(M16_DMA_PER_WAVE * (M16_NS - 2));
+      __syncthreads();
+      // ... so its stage can take item it+NS-1
+      m16_issue_item(a, bt_lds, nseg, ci, ring_lds + ((it + M16_NS - 1) % M16_NS) * M16_STAGE, wave, lane);
+      m16_advance(ci, segs, nseg);
+      const uint8_t* stage = ring + (it % M16_NS) * M16_STAGE;
+      if (cc.j < 0) {
+        // Q item: this wave's k-steps of Q^T (lane (li, g): dims
+        // 32kk + 8g .. +7 of row li, laid out like a key half) into
+        // registers, and a fresh state
+        const uint8_t* qp = stage + 1024 * M16_KSTEPS * (wave >> 1) + 16 * (16 * g + (li ^ (4 * (g & 1))));
+#pragma unroll
+        for (int kk = 0; kk < M16_KSTEPS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 1024 * kk);
+        const int my_row = cc.d.rt * M16_ROWS + li;
+        nrow = my_row < a.R ? row_bound(cc.d.seq, cc.d.tot, a.Q, my_row / a.H, a.W, a.rank, a.causal) : 0;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) st.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st.m_ref = NEG_INF;
+        st.l_part = 0.f;
+      } else {
+        m16_compute(st, qf, stage, xchg, a.scale_log2, cc.d.ka + M16_TILE * cc.j, cc.d.kb, nrow, lane, wave);
+        if (cc.j == cc.nt - 1 && (cc.d.flags & M16_SEG_LAST)) {
+          // partial slot: wave w's O^T tiles T = 8w + mt in the accumulator
+          // layout [T][lane][4] (one 16-byte store per lane and tile), then m
+          // and l per row
+          float l_row = st.l_part;
+          l_row += __shfl_xor(l_row, 16, 64);
+          l_row += __shfl_xor(l_row, 32, 64);
+          const int slot = w + cc.d.bb * a.n_rt + cc.d.rt;
+          float* ps = a.partials + (int64_t)slot * (M16_ROWS * D_V + 2 * M16_ROWS);
+#pragma unroll
+          for (int mt = 0; mt < 8; ++mt)
+            *reinterpret_cast<f32x4*>(ps + ((M16_DV_WAVE / 16) * wave + mt) * 256 + 4 * lane) = st.o[mt];
+          if (wave == 0 && g == 0) {
+            ps[M16_ROWS * D_V + li] = st.m_ref;
+            ps[M16_ROWS * D_V + M16_ROWS + li] = l_row;
+          }
+        }
+      }
+      m16_advance(cc, segs, nseg);
+    }
+    WAIT_VMCNT(0);
+    __syncthreads();  // the ring, the window and the segment list are free again
+    nseg = 0;
+    nent = 0;
+  };
+
+  for_each_piece<M16_THREADS>(a, w, plan, [&](int bb, int rt, int k0, int k1, int seq, int tot) {
+    // append the piece (rows [16 rt, 16 rt + 16) of request bb, keys [k0, k1))
+    // to the batch as one or more segments
+    const int32_t* btr = a.bt + (int64_t)bb * a.max_blocks;
+    int flags = M16_SEG_FIRST;
+    for (int ka = k0; ka < k1;) {
+      if (nseg == M16_MAXSEG || M16_BT_WIN - nent < 2) run_batch();
+      const int room = M16_BT_WIN - nent;
+      const int64_t max_keys = (int64_t)(room - 1) * a.bs;  // any such key range spans <= room blocks
+      const int kb = (int64_t)(k1 - ka) <= max_keys ? k1 : ka + (int)max_keys;
+      const int e0 = block_of(a, ka), e1 = block_of(a, kb - 1);
+      for (int e = e0 + tid; e <= e1; e += M16_THREADS)
+        bt_lds[nent + e - e0] = e < a.max_blocks ? gload_i32(btr + e) : -1;
+      if (tid == 0) segs[nseg] = M16Seg{bb, rt, ka, kb, seq, tot, nent - e0, flags | (kb == k1 ? M16_SEG_LAST : 0)};
+      ++nseg;
+      nent += e1 - e0 + 1;
+      ka = kb;
+      flags = 0;
     }
   });
+  run_batch();
 }
 
 // ---------------------------------------------------------------- R128 partial
@@ -621,9 +753,7 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
   __shared__ __attribute__((aligned(1024))) uint8_t ring[R128_NS * R128_STAGE];
   __shared__ int bt_lds[R128_BT_WIN];
   __shared__ __attribute__((aligned(16))) uint8_t q_tail_lds[4][R128_QLDS * 64 * 16];
-  __shared__ int64_t s_red[R128_THREADS / 64];
-  __shared__ int64_t s_excl[R128_THREADS];
-  __shared__ int s_first_last[2];
+  __shared__ PlanLds<R128_THREADS> plan;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int w = xcd_range_index(blockIdx.x, a.G);
@@ -640,8 +770,7 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
     dma_sel_off[m] = 16 * c | ((row_rel != (64 * m) / 72) ? (1 << 15) : 0);
   }
 
-  for_each_piece<R128_THREADS>(a, w, s_red, s_excl, s_first_last, [&](int bb, int rt, int k0, int k1, int seq,
-                                                                     int tot) {
+  for_each_piece<R128_THREADS>(a, w, plan, [&](int bb, int rt, int k0, int k1, int seq, int tot) {
     // ---- one piece: rows [128 rt, 128 rt + 128) of request bb, keys [k0, k1)
     const int32_t* btr = a.bt + (int64_t)bb * a.max_blocks;
     const int my_row = rt * R128_ROWS + wave * 32 + (lane & 31);

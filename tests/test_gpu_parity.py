@@ -57,6 +57,10 @@ CASES = [
     spec("peaky_h128", 2, 128, 4, True, [100, 1500], q_mult=8.0, global_is_null=True),
     spec("h1_q1", 3, 1, 1, True, [5, 64, 300], global_is_null=True),
     spec("h3_q5", 2, 3, 5, True, [10, 400], W=3),
+    # 300 requests of 0..4 keys: more than 256 requests (several scan chunks)
+    # and far more pieces per workgroup range than one batch of segments holds
+    spec("many_tiny_requests", 300, 16, 1, True, [(7 * i) % 5 for i in range(300)], global_is_null=True),
+    spec("many_tiny_requests_h128", 40, 128, 2, True, [(3 * i) % 4 for i in range(40)], W=2),
 ]
 
 
@@ -71,6 +75,37 @@ def test_decode_matches_oracle(sp):
             torch.cuda.synchronize()
             ro, rl = oracle_rank(wl, r, base)
             compare(out, lse, ro, rl, f"{sp.name} r{r} {base}")
+
+
+@pytest.mark.parametrize("name", ["many_tiny_requests", "many_tiny_requests_h128"])
+def test_tight_max_seq_len_packs_many_pieces_per_workgroup(name):
+    # max_seq_len = the longest local length: few workgroups, each covering
+    # dozens of (request, row tile) pieces
+    sp = next(c for c in CASES if c.name == name)
+    wl = WL.build(sp)
+    up = Uploaded(wl)
+    for r in sorted(wl.pools):
+        msl = max(int(wl.seq_lens[r].max()), 1)
+        say(f"{sp.name} rank {r} max_seq_len {msl}")
+        out, lse = up.run(r, "e", max_seq_len=msl)
+        torch.cuda.synchronize()
+        ro, rl = oracle_rank(wl, r, "e")
+        compare(out, lse, ro, rl, f"{sp.name} r{r} tight")
+
+
+def test_long_piece_spans_several_block_table_windows():
+    # block size 1 and 270k keys: each workgroup range covers more block-table
+    # entries than one LDS window holds, so a piece continues across batches;
+    # sampled rows against the oracle
+    sp = spec("bs1_270k", 1, 2, 1, True, [270000], bs=1, global_is_null=True, seed=4242)
+    say(f"{sp.name}: generating")
+    wl = WL.build(sp)
+    up = Uploaded(wl)
+    out, lse = up.run(0, "e")
+    torch.cuda.synchronize()
+    rows = [(0, 0, 0), (0, 0, 1)]
+    ro, rl = oracle.mla_decode(wl.q_bits, wl.global_rows, wl.seq_lens[0], None, 1, 0, True, sp.scale, "e", rows=rows)
+    compare(out, lse, ro, rl, sp.name, rows=[(0, 0), (0, 1)])
 
 
 def test_zero_query_lse_is_log_of_visible_count():
