@@ -27,7 +27,10 @@
 // read from LDS by the transposing ds_read_b64_tr_b16.  The running max is a
 // reference that only moves when a row's max grows by more than 2^8, so the
 // accumulators are rarely rescaled (the exponentials stay <= 256, exact in
-// fp32 and in bf16 range).
+// fp32 and in bf16 range).  P enters P*V rounded to bf16; the output is
+// normalised by the sum of those same rounded values (a row dominated by one
+// key then reproduces that key's value row instead of being off by the
+// rounding of its weight), while the LSE uses the fp32 sum.
 #include <hip/hip_runtime.h>
 #include <cmath>
 #include <cstdint>
@@ -54,12 +57,20 @@ struct DecodeArgs {
   float scale_log2;        // softmax scale times log2(e)
   int lse_base;
   int n_rt;                // row tiles per request
+  int ovh;                 // work units charged per (request, row tile) group on top of its keys
   int G;                   // partial workgroups
   int64_t* prefix;         // [B+1] unit offsets of the requests
   float* partials;         // [G + B*n_rt] slots
   uint16_t* out;           // bf16 [B*R, 512]
   float* lse;              // [B*R] or null
 };
+
+// Work units of a request: per row tile, its keys plus a fixed overhead
+// (the query rows' load and the partial's store), so that ranges crossing a
+// group boundary get fewer keys.  Requests without keys cost nothing.
+__device__ __forceinline__ int64_t request_units(const DecodeArgs& a, int nb) {
+  return nb > 0 ? (int64_t)a.n_rt * (nb + a.ovh) : 0;
+}
 
 // Key count of the largest row (row j = q_len-1 has the longest prefix),
 // local length and global length of request b; zeros past B.
@@ -138,12 +149,12 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int w, PlanL
   int nb, seq, tot;
   request_info(a, tid, nb, seq, tot);
   int64_t total0;
-  const int64_t incl0 = block_incl_scan_i64<NT>((int64_t)a.n_rt * nb, pl.red, total0);
+  const int64_t incl0 = block_incl_scan_i64<NT>(request_units(a, nb), pl.red, total0);
   int64_t T = total0;
   for (int base = NT; base < a.B; base += NT) {
     int nb2, seq2, tot2;
     request_info(a, base + tid, nb2, seq2, tot2);
-    T += block_sum_i64<NT>((int64_t)a.n_rt * nb2, pl.red);
+    T += block_sum_i64<NT>(request_units(a, nb2), pl.red);
   }
   const int64_t u0 = (int64_t)w * T / a.G, u1 = (int64_t)(w + 1) * T / a.G;
 
@@ -152,10 +163,10 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int w, PlanL
     int64_t incl = incl0, chunk_total = total0;
     if (base > 0) {
       request_info(a, base + tid, nb, seq, tot);
-      incl = block_incl_scan_i64<NT>((int64_t)a.n_rt * nb, pl.red, chunk_total);
+      incl = block_incl_scan_i64<NT>(request_units(a, nb), pl.red, chunk_total);
     }
     const int b = base + tid;
-    const int64_t x = (int64_t)a.n_rt * nb;
+    const int64_t x = request_units(a, nb);
     incl += carry;
     const int64_t excl = incl - x;
     if (w == 0 && b < a.B) {
@@ -182,12 +193,17 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int w, PlanL
       const int nbb = __builtin_amdgcn_readfirstlane(pl.nb[i]);
       const int sq = __builtin_amdgcn_readfirstlane(pl.seq[i]);
       const int tt = __builtin_amdgcn_readfirstlane(pl.tot[i]);
+      if (nbb == 0) continue;  // no keys: no units, no pieces
+      const int64_t gu = (int64_t)nbb + a.ovh;    // units per group
       const int64_t lo = u0 > pb ? u0 - pb : 0;  // first unit of the request in range
-      const int64_t hi = (u1 - pb) < (int64_t)a.n_rt * nbb ? u1 - pb : (int64_t)a.n_rt * nbb;
-      for (int rt = (int)(lo / nbb); (int64_t)rt * nbb < hi; ++rt) {
-        const int k0 = __builtin_amdgcn_readfirstlane((int)((int64_t)rt * nbb < lo ? lo - (int64_t)rt * nbb : 0));
-        const int k1 =
-            __builtin_amdgcn_readfirstlane((int)((int64_t)(rt + 1) * nbb < hi ? nbb : hi - (int64_t)rt * nbb));
+      const int64_t hi = (u1 - pb) < a.n_rt * gu ? u1 - pb : a.n_rt * gu;
+      for (int rt = (int)(lo / gu); (int64_t)rt * gu < hi; ++rt) {
+        // the group's units [rt*gu, (rt+1)*gu): ovh overhead units, then its keys
+        const int64_t g0 = (int64_t)rt * gu;
+        const int64_t a0 = (lo > g0 ? lo - g0 : 0) - a.ovh, a1 = (hi - g0 < gu ? hi - g0 : gu) - a.ovh;
+        const int k0 = __builtin_amdgcn_readfirstlane((int)(a0 > 0 ? a0 : 0));
+        const int k1 = __builtin_amdgcn_readfirstlane((int)(a1 > 0 ? a1 : 0));
+        if (k1 <= k0) continue;  // this range holds only the group's overhead units
         piece(bb, rt, k0, k1, sq, tt);
       }
     }
@@ -234,6 +250,67 @@ __device__ __forceinline__ const uint8_t* ring_row(const DecodeArgs& a, const in
   return rowp;
 }
 
+// Stage layout shared by both families: a stage holds 32 key rows of 1152
+// bytes, unpadded, row r at byte 1152*r.  The 16-byte chunks of a row are
+// swizzled: logical chunk c of row r sits at (c & ~7) | ((c ^ f(r)) & 7),
+// f(r) = g((r >> 1) & 7) with g(v) = (v >> 1) | ((v & 1) << 2).  Rows are
+// 1152 bytes (8 mod 16 in 16-byte bank groups), so odd rows already land on
+// the other half of the banks; f is a permutation over even (and over odd)
+// rows, which makes the score reads (8 consecutive rows, one chunk)
+// conflict-free, and f(4u) ^ f(4u+2) = 4, which does the same for the
+// transposed V reads (4 rows x 2-4 chunks).
+__device__ __forceinline__ int ring_swz(int r) {
+  const int v = (r >> 1) & 7;
+  return (v >> 1) | ((v & 1) << 2);
+}
+
+constexpr int RING_TILE = 32;                          // key rows per stage
+constexpr int RING_STAGE = RING_TILE * ROW_BYTES;      // 36 KiB
+constexpr int RING_DMA_PER_WAVE = 9;                   // 1 KiB load instructions per wave per stage
+static_assert(RING_STAGE == 4 * RING_DMA_PER_WAVE * 1024, "a stage is exactly the four waves' loads");
+
+// Wave w loads rows 8w..8w+7 of a stage with 9 instructions: instruction m,
+// lane l fills stage byte 1024*(9w+m) + 16*l, i.e. row 8w + (64m+l)/72,
+// physical chunk (64m+l)%72.  sel_off[m] (per lane, fixed) holds the logical
+// byte offset of that chunk in its row and, in bit 15, whether the row is
+// the higher of the two rows instruction m touches.
+__device__ __forceinline__ void ring_dma_offsets(int (&sel_off)[RING_DMA_PER_WAVE], int wave, int lane) {
+#pragma unroll
+  for (int m = 0; m < RING_DMA_PER_WAVE; ++m) {
+    const int cidx = 64 * m + lane;
+    const int row_rel = cidx / 72, pch = cidx - 72 * (cidx / 72);
+    const int c = (pch & ~7) | ((pch ^ ring_swz(8 * wave + row_rel)) & 7);
+    sel_off[m] = 16 * c | ((row_rel != (64 * m) / 72) ? (1 << 15) : 0);
+  }
+}
+
+// Issue this wave's 9 loads of its 8 rows; lane k < 8 holds the global
+// address of row 8w + k in rowp (the other lanes' values are ignored).
+__device__ __forceinline__ void ring_issue_rows(const uint8_t* rowp, uint32_t stage_lds, int wave,
+                                                const int (&sel_off)[RING_DMA_PER_WAVE]) {
+  const uint64_t row64 = reinterpret_cast<uint64_t>(rowp);
+  uint64_t rows[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)row64, j);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(row64 >> 32), j);
+    rows[j] = ((uint64_t)hi << 32) | lo;
+  }
+#pragma unroll
+  for (int m = 0; m < RING_DMA_PER_WAVE; ++m) {
+    const int rlo = (64 * m) / 72;
+    const int rhi = (64 * m + 63) / 72;
+    const int so = sel_off[m];
+    // lanes in the higher row add the (uniform) distance between the two row
+    // addresses; arithmetic rather than a select keeps the compiler from
+    // turning it into a compare chain over all eight rows
+    const uint64_t dist = rows[rhi] - rows[rlo];
+    const uint64_t msk = (uint64_t)0 - (uint64_t)((uint32_t)so >> 15);
+    dma16(reinterpret_cast<const void*>(rows[rlo] + (dist & msk) + (so & 0x7fff)),
+          stage_lds + 1024 * (RING_DMA_PER_WAVE * wave + m));
+  }
+}
+
 // ---------------------------------------------------------------- M16 partial
 // Memory-bound family: up to 16 rows per request (single-token decode with up
 // to 16 heads and similar), any block size.  256 threads = 4 waves per
@@ -249,11 +326,10 @@ __device__ __forceinline__ const uint8_t* ring_row(const DecodeArgs& a, const in
 // instead: wave w accumulates O^T[128w .. 128w+127][16 rows] (8 x 16 x 16
 // fp32 tiles, 32 MFMA registers) with V^T from LDS by ds_read_b64_tr_b16.
 //
-// Stage layout: two 16-key halves of 18 KiB.  Within a half, 16-byte chunk c
-// of key row r sits at byte 1024*(c/4) + 16*(16*(c%4) + (r ^ 4*(c&1))): one
-// load instruction fills 1 KiB with 4 consecutive chunks of all 16 rows, the
-// K reads of an MFMA step are one contiguous 1 KiB, and the transposed V reads
-// (4 rows x 32 bytes per 16 lanes) hit 16 distinct 8-byte bank slots.
+// Stages use the shared swizzled row layout; the two 16-key halves are rows
+// 0..15 and 16..31.  The dims are split between wave pairs by MFMA step
+// parity (wave w takes k-steps 2k + w/2), which keeps every score read of a
+// wave at one chunk position per row group.
 //
 // Pipeline.  The ring items are, per piece, the query rows (loaded through
 // the ring like a key half, then read into registers) followed by the
@@ -264,11 +340,11 @@ __device__ __forceinline__ const uint8_t* ring_row(const DecodeArgs& a, const in
 // kept in registers.
 constexpr int M16_THREADS = 256;
 constexpr int M16_ROWS = 16;
-constexpr int M16_TILE = 32;                       // keys per tile
-constexpr int M16_HALF = 16 * ROW_BYTES;           // 18 KiB
-constexpr int M16_STAGE = 2 * M16_HALF;            // 36 KiB
+constexpr int M16_TILE = RING_TILE;                // keys per tile
+constexpr int M16_HALF = 16 * ROW_BYTES;           // bytes of a 16-key half of a stage
+constexpr int M16_STAGE = RING_STAGE;              // 36 KiB
 constexpr int M16_NS = 4;                          // ring stages
-constexpr int M16_DMA_PER_WAVE = 9;                // 1 KiB load instructions per wave per tile
+constexpr int M16_DMA_PER_WAVE = RING_DMA_PER_WAVE;
 constexpr int M16_KSTEPS = 9;                      // 32-dim MFMA steps per wave (half of 576)
 constexpr int M16_BT_WIN = 1024;                   // block-table entries held in LDS per batch
 constexpr int M16_MAXSEG = 16;                     // segments per batch
@@ -277,11 +353,10 @@ constexpr float M16_RESCALE_LOG2 = 8.f;            // keep exponentials <= 2^8 b
 constexpr int M16_SEG_FIRST = 1;   // segment starts its (request, row tile) group: a Q item precedes it
 constexpr int M16_SEG_LAST = 2;    // segment ends its group: the partial is written after its last tile
 
-static_assert(M16_STAGE == 4 * M16_DMA_PER_WAVE * 1024, "a stage is exactly the four waves' loads");
 
 struct M16State {
   f32x4 o[8];
-  float m_ref, l_part;
+  float m_ref, l_part, l_out;  // l_part: sum of fp32 P (LSE); l_out: of bf16 P (output)
 };
 
 struct M16Seg {
@@ -320,25 +395,22 @@ __device__ __forceinline__ void m16_advance(M16Cursor& c, const M16Seg* segs, in
   }
 }
 
-// Issue this wave's 9 loads of ring item c: wave w fills half w/2, chunks
-// 36*(w%2) .. 36*(w%2)+35 of its 16 rows.  Lane l loads row
-// (l%16) ^ 4*((l/16)&1), chunk 4m' + l/16 with m' = 9*(w%2) + m, which the
-// instruction writes to 1024*m' + 16*l of the half: the layout above.  A Q
-// item loads the group's 16 query rows into half 0 (waves 0 and 1); items
-// past the end, and the other half of a Q item, load the zero row, so every
-// wave issues 9 loads per item.
+// Issue this wave's 9 loads of ring item c (rows 8w..8w+7 of the stage).  A
+// Q item loads the group's 16 query rows as rows 0..15 (waves 0 and 1);
+// items past the end, and rows 16..31 of a Q item, load the zero row, so
+// every wave issues 9 loads per item.
 __device__ __forceinline__ void m16_issue_item(const DecodeArgs& a, const int* bt_lds, int nseg, const M16Cursor& c,
-                                               uint32_t stage_lds, int wave, int lane) {
-  const int gq = lane >> 4;
-  const int r = (lane & 15) ^ (4 * (gq & 1));
+                                               uint32_t stage_lds, int wave, int lane,
+                                               const int (&sel_off)[RING_DMA_PER_WAVE]) {
+  const int r = 8 * wave + (lane & 7);  // the stage row this lane resolves (lanes 0..7 matter)
   const uint8_t* rowp = reinterpret_cast<const uint8_t*>(kZeroRow);
   asm volatile("" : "+v"(rowp));
   if (c.s < nseg) {
     if (c.j < 0) {
       const int qr = c.d.rt * M16_ROWS + r;
-      if (wave < 2 && qr < a.R) rowp = a.q + ((int64_t)c.d.bb * a.R + qr) * ROW_BYTES;
+      if (r < M16_ROWS && qr < a.R) rowp = a.q + ((int64_t)c.d.bb * a.R + qr) * ROW_BYTES;
     } else {
-      const int t = c.d.ka + M16_TILE * c.j + 16 * (wave >> 1) + r;
+      const int t = c.d.ka + M16_TILE * c.j + r;
       if (t < c.d.kb) {
         const int vb = block_of(a, t);
         const int blk = bt_lds[c.d.e_base + vb];
@@ -346,10 +418,7 @@ __device__ __forceinline__ void m16_issue_item(const DecodeArgs& a, const int* b
       }
     }
   }
-  rowp += 16 * gq + 576 * (wave & 1);
-#pragma unroll
-  for (int m = 0; m < M16_DMA_PER_WAVE; ++m)
-    dma16(rowp + 64 * m, stage_lds + 1024 * (M16_DMA_PER_WAVE * wave + m));
+  ring_issue_rows(rowp, stage_lds, wave, sel_off);
 }
 
 // One 32-key tile: this wave's quarter of S^T, the exchange of the partial
@@ -360,15 +429,16 @@ __device__ __forceinline__ void m16_compute(M16State& st, const bf16x8 (&qf)[M16
                                             int wave) {
   const int li = lane & 15, g = lane >> 4;
   // S^T[key][row] of half wave%2: lane (li, g) gets keys 4g+e for row li;
-  // the K fragment of k-step kk is chunk 4kk+g of key row li
-  const uint8_t* kp = stage + (wave & 1) * M16_HALF + 1024 * M16_KSTEPS * (wave >> 1) +
-                      16 * (16 * g + (li ^ (4 * (g & 1))));
+  // the K fragment of k-step kk = 2k + wave/2 is logical chunk 4kk + g of key
+  // row li, i.e. physical byte 128k + 16*((4*(wave/2) + g) ^ f(row))
+  const int kr = 16 * (wave & 1) + li;
+  const uint8_t* kp = stage + ROW_BYTES * kr + 16 * ((4 * (wave >> 1) + g) ^ ring_swz(kr));
   f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
   bf16x8 kf[M16_KSTEPS];
   // all nine reads first, then the MFMAs in two chains (one chain of nine
   // dependent MFMAs would wait out the MFMA latency at every step)
 #pragma unroll
-  for (int kk = 0; kk < M16_KSTEPS; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(kp + 1024 * kk);
+  for (int kk = 0; kk < M16_KSTEPS; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(kp + 128 * kk);
 #pragma unroll
   for (int kk = 0; kk < M16_KSTEPS; ++kk) {
     if (kk & 1)
@@ -401,6 +471,7 @@ __device__ __forceinline__ void m16_compute(M16State& st, const bf16x8 (&qf)[M16
     if (mx > st.m_ref + M16_RESCALE_LOG2) {
       const float alpha = fast_exp2(st.m_ref - mx);
       st.l_part *= alpha;
+      st.l_out *= alpha;
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -424,17 +495,22 @@ __device__ __forceinline__ void m16_compute(M16State& st, const bf16x8 (&qf)[M16
   const bf16x4 plo = to_bf16x4(p[0], p[1], p[2], p[3]);
   const bf16x4 phi = to_bf16x4(p[4], p[5], p[6], p[7]);
   const bf16x8 pf = __builtin_shufflevector(plo, phi, 0, 1, 2, 3, 4, 5, 6, 7);
+  st.l_out = sum_bf16x8(pf, st.l_out);
   // V^T fragments: lane (li, g) of a transposed read points at key row
-  // 4g + li/4, value columns 16T + 4(li%4) .. +3 (chunk 2T + (li/2)%2, byte
-  // 8(li%2)) and receives column 16T + li of the 4 rows; T = 8*wave + mt
-  const int b1 = (li >> 1) & 1;
-  const uint8_t* vp = stage + 256 * b1 + 16 * ((4 * g + (li >> 2)) ^ (4 * b1)) + 8 * (li & 1) +
-                      (M16_DV_WAVE / 16) * 512 * wave;
+  // 16h + 4g + li/4, value columns 16T + 4(li%4) .. +3 (logical chunk
+  // 2T + (li/2)%2, byte 8(li%2)) and receives column 16T + li of the 4 rows;
+  // T = 8*wave + mt, so the chunk is 8(2*wave + mt/4) + 2(mt%4) + (li/2)%2
+  const int vr = 4 * g + (li >> 2);
+  const int vsw = ring_swz(vr);  // equal for rows vr and 16 + vr
+  const uint8_t* vrow = stage + ROW_BYTES * vr + 256 * wave + 8 * (li & 1);
+  const uint8_t* vp[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) vp[q] = vrow + 16 * ((2 * q + ((li >> 1) & 1)) ^ vsw);
   i16x4 v[8][2];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
-    v[mt][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 512 * mt));
-    v[mt][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + M16_HALF + 512 * mt));
+    v[mt][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp[mt & 3] + 128 * (mt >> 2)));
+    v[mt][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp[mt & 3] + M16_HALF + 128 * (mt >> 2)));
   }
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
@@ -456,6 +532,8 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
   const int li = lane & 15, g = lane >> 4;
   const int w = xcd_range_index(blockIdx.x, a.G);
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
+  int sel_off[RING_DMA_PER_WAVE];  // per-lane constants of this wave's ring loads
+  ring_dma_offsets(sel_off, wave, lane);
 
   // state of the group being computed; it survives batch boundaries
   bf16x8 qf[M16_KSTEPS];
@@ -466,6 +544,7 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
   for (int mt = 0; mt < 8; ++mt) st.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m_ref = NEG_INF;
   st.l_part = 0.f;
+  st.l_out = 0.f;
   int nrow = 0;
   int nseg = 0, nent = 0;  // segments and window entries of the batch being built
 
@@ -483,7 +562,7 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
     M16Cursor cc = ci;
 #pragma unroll
     for (int p = 0; p < M16_NS - 1; ++p) {
-      m16_issue_item(a, bt_lds, nseg, ci, ring_lds + p * M16_STAGE, wave, lane);
+      m16_issue_item(a, bt_lds, nseg, ci, ring_lds + p * M16_STAGE, wave, lane, sel_off);
       m16_advance(ci, segs, nseg);
     }
     for (int it = 0; it < n_items; ++it) {
@@ -492,39 +571,44 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
       WAIT_VMCNT(M16_DMA_PER_WAVE * (M16_NS - 2));
       __syncthreads();
       // ... so its stage can take item it+NS-1
-      m16_issue_item(a, bt_lds, nseg, ci, ring_lds + ((it + M16_NS - 1) % M16_NS) * M16_STAGE, wave, lane);
+      m16_issue_item(a, bt_lds, nseg, ci, ring_lds + ((it + M16_NS - 1) % M16_NS) * M16_STAGE, wave, lane,
+                     sel_off);
       m16_advance(ci, segs, nseg);
       const uint8_t* stage = ring + (it % M16_NS) * M16_STAGE;
       if (cc.j < 0) {
         // Q item: this wave's k-steps of Q^T (lane (li, g): dims
-        // 32kk + 8g .. +7 of row li, laid out like a key half) into
-        // registers, and a fresh state
-        const uint8_t* qp = stage + 1024 * M16_KSTEPS * (wave >> 1) + 16 * (16 * g + (li ^ (4 * (g & 1))));
+        // 32kk + 8g .. +7 of row li, kk = 2k + wave/2; stored like key rows
+        // 0..15) into registers, and a fresh state
+        const uint8_t* qp = stage + ROW_BYTES * li + 16 * ((4 * (wave >> 1) + g) ^ ring_swz(li));
 #pragma unroll
-        for (int kk = 0; kk < M16_KSTEPS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 1024 * kk);
+        for (int kk = 0; kk < M16_KSTEPS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 128 * kk);
         const int my_row = cc.d.rt * M16_ROWS + li;
         nrow = my_row < a.R ? row_bound(cc.d.seq, cc.d.tot, a.Q, my_row / a.H, a.W, a.rank, a.causal) : 0;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) st.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         st.m_ref = NEG_INF;
         st.l_part = 0.f;
+        st.l_out = 0.f;
       } else {
         m16_compute(st, qf, stage, xchg, a.scale_log2, cc.d.ka + M16_TILE * cc.j, cc.d.kb, nrow, lane, wave);
         if (cc.j == cc.nt - 1 && (cc.d.flags & M16_SEG_LAST)) {
           // partial slot: wave w's O^T tiles T = 8w + mt in the accumulator
-          // layout [T][lane][4] (one 16-byte store per lane and tile), then m
-          // and l per row
-          float l_row = st.l_part;
+          // layout [T][lane][4] (one 16-byte store per lane and tile), then
+          // per row m, the fp32 and the bf16 sums of P
+          float l_row = st.l_part, lo_row = st.l_out;
           l_row += __shfl_xor(l_row, 16, 64);
           l_row += __shfl_xor(l_row, 32, 64);
+          lo_row += __shfl_xor(lo_row, 16, 64);
+          lo_row += __shfl_xor(lo_row, 32, 64);
           const int slot = w + cc.d.bb * a.n_rt + cc.d.rt;
-          float* ps = a.partials + (int64_t)slot * (M16_ROWS * D_V + 2 * M16_ROWS);
+          float* ps = a.partials + (int64_t)slot * (M16_ROWS * D_V + 3 * M16_ROWS);
 #pragma unroll
           for (int mt = 0; mt < 8; ++mt)
             *reinterpret_cast<f32x4*>(ps + ((M16_DV_WAVE / 16) * wave + mt) * 256 + 4 * lane) = st.o[mt];
           if (wave == 0 && g == 0) {
             ps[M16_ROWS * D_V + li] = st.m_ref;
             ps[M16_ROWS * D_V + M16_ROWS + li] = l_row;
+            ps[M16_ROWS * D_V + 2 * M16_ROWS + li] = lo_row;
           }
         }
       }
@@ -573,38 +657,21 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
 // LDS load at each barrier.
 constexpr int R128_THREADS = 256;
 constexpr int R128_ROWS = 128;
-constexpr int R128_TILE = 32;                 // keys per tile
+constexpr int R128_TILE = RING_TILE;          // keys per tile
 constexpr int R128_ROWB = ROW_BYTES;          // LDS bytes per key row (unpadded; chunks are swizzled instead)
-constexpr int R128_DMA_PER_WAVE = 9;          // 1 KiB load instructions per wave per tile: its 8 rows
-constexpr int R128_STAGE = R128_TILE * R128_ROWB;   // 36 KiB
+constexpr int R128_DMA_PER_WAVE = RING_DMA_PER_WAVE;
+constexpr int R128_STAGE = RING_STAGE;        // 36 KiB
 constexpr int R128_NS = 3;                    // ring stages
 constexpr int R128_BT_WIN = 1024;             // block-table entries held in LDS per sub-piece
 constexpr int R128_QREG = 28;                 // Q^T k-steps (of 16 dims) kept in registers; the rest in LDS
 constexpr int R128_QLDS = 36 - R128_QREG;
 constexpr float R128_RESCALE_LOG2 = 8.f;
 
-static_assert(R128_STAGE == 4 * R128_DMA_PER_WAVE * 1024, "a stage is exactly the four waves' loads");
 
-// Swizzle of the 16-byte chunks of a key row in LDS: logical chunk c of row r
-// sits at (c & ~7) | ((c ^ f(r)) & 7), f(r) = g((r >> 1) & 7) with
-// g(v) = (v >> 1) | ((v & 1) << 2).  Rows are 1152 bytes (72 chunks, 8 mod 16
-// in 16-byte bank groups), so odd rows already land on the other half of the
-// banks; f is a permutation over even (and over odd) rows, which makes the
-// QK^T reads (16 rows, one chunk) conflict-free, and f(4u) ^ f(4u+2) = 4,
-// which does the same for the transposed V reads (4 rows x 2-4 chunks).
-__device__ __forceinline__ int r128_f(int r) {
-  const int v = (r >> 1) & 7;
-  return (v >> 1) | ((v & 1) << 2);
-}
-
-// Issue this wave's loads of tile [ts, ts+32) into a stage: wave w loads keys
-// 8w..8w+7 with 9 instructions; instruction m, lane l fills stage byte
-// 1024*(9w+m) + 16*l, i.e. row 8w + (64m+l)/72, physical chunk (64m+l)%72.
-// dma_sel_off[m] (per lane, fixed) holds the logical byte offset of that chunk
-// and whether its row is the higher of the two rows instruction m touches.
+// Issue this wave's loads of tile [ts, ts+32) into a stage (rows 8w..8w+7).
 __device__ __forceinline__ void r128_issue_tile(const DecodeArgs& a, const int* bt_lds, int e0, int ts, int k1,
                                                 uint32_t stage_lds, int wave, int lane,
-                                                const int (&dma_sel_off)[R128_DMA_PER_WAVE]) {
+                                                const int (&dma_sel_off)[RING_DMA_PER_WAVE]) {
   // lanes 0..7 resolve the row address of key ts + 8*wave + lane (or the zero row)
   const int k = lane & 7;
   const int t = ts + 8 * wave + k;
@@ -616,32 +683,12 @@ __device__ __forceinline__ void r128_issue_tile(const DecodeArgs& a, const int* 
     if ((unsigned)blk < (unsigned)a.num_blocks)
       rowp = a.kv + ((int64_t)blk * a.bs + (t & (a.bs - 1))) * ROW_BYTES;
   }
-  const uint64_t row64 = reinterpret_cast<uint64_t>(rowp);
-  uint64_t rows[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)row64, j);
-    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(row64 >> 32), j);
-    rows[j] = ((uint64_t)hi << 32) | lo;
-  }
-#pragma unroll
-  for (int m = 0; m < R128_DMA_PER_WAVE; ++m) {
-    const int rlo = (64 * m) / 72;
-    const int rhi = (64 * m + 63) / 72;
-    const int so = dma_sel_off[m];
-    // lanes in the higher row add the (uniform) distance between the two row
-    // addresses; arithmetic rather than a select keeps the compiler from
-    // turning it into a compare chain over all eight rows
-    const uint64_t dist = rows[rhi] - rows[rlo];
-    const uint64_t msk = (uint64_t)0 - (uint64_t)((uint32_t)so >> 15);
-    dma16(reinterpret_cast<const void*>(rows[rlo] + (dist & msk) + (so & 0x7fff)),
-          stage_lds + 1024 * (R128_DMA_PER_WAVE * wave + m));
-  }
+  ring_issue_rows(rowp, stage_lds, wave, dma_sel_off);
 }
 
 struct R128State {
   f32x16 o[16];
-  float m_ref, l_part;
+  float m_ref, l_part, l_out;  // l_part: sum of fp32 P (LSE); l_out: of bf16 P (output)
 };
 
 __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R128_QREG], const uint8_t* q_tail,
@@ -652,7 +699,7 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R
   f32x16 sc = {};
   // k-step kk = 4a + b reads logical chunk 2kk + h of row r: physical byte
   // 128a + 16*((2b + h) ^ f(r)) of the row
-  const int fk = r128_f(r);
+  const int fk = ring_swz(r);
   const uint8_t* krow = stage + r * R128_ROWB;
   const uint8_t* kp[4];
 #pragma unroll
@@ -683,6 +730,7 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R
     if (mx > st.m_ref + R128_RESCALE_LOG2) {
       const float alpha = fast_exp2(st.m_ref - mx);
       st.l_part *= alpha;
+      st.l_out *= alpha;
       // one 16-register tile at a time, so the rare rescale never needs 256
       // temporaries at once
 #pragma unroll
@@ -709,6 +757,7 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R
     const bf16x4 lo4 = to_bf16x4(sc[8 * ks + 0], sc[8 * ks + 1], sc[8 * ks + 2], sc[8 * ks + 3]);
     const bf16x4 hi4 = to_bf16x4(sc[8 * ks + 4], sc[8 * ks + 5], sc[8 * ks + 6], sc[8 * ks + 7]);
     pf[ks] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+    st.l_out = sum_bf16x8(pf[ks], st.l_out);
   }
   // V^T fragments: the MFMA's contraction slot 8h + s pairs with key
   // 16*ks + 8*(s/4) + 4h + s%4 on the P^T side, so lane (q = lane/16, i)
@@ -721,7 +770,7 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R
   const uint8_t* vp[2][2];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
-    const int ft = r128_f(8 * hh + 4 * h + (i16 >> 2));
+    const int ft = ring_swz(8 * hh + 4 * h + (i16 >> 2));
 #pragma unroll
     for (int par = 0; par < 2; ++par)
       vp[hh][par] = vrow + 8 * hh * R128_ROWB + 16 * ((4 * par + 2 * (q & 1) + ((i16 & 3) >> 1)) ^ ft);
@@ -758,17 +807,8 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int w = xcd_range_index(blockIdx.x, a.G);
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
-  // per-lane constants of this wave's ring loads (see r128_issue_tile):
-  // logical byte offset of the chunk, bit 15 set when its row is the higher
-  // of the two rows the instruction touches
-  int dma_sel_off[R128_DMA_PER_WAVE];
-#pragma unroll
-  for (int m = 0; m < R128_DMA_PER_WAVE; ++m) {
-    const int cidx = 64 * m + lane;
-    const int row_rel = cidx / 72, pch = cidx - 72 * (cidx / 72);
-    const int c = (pch & ~7) | ((pch ^ r128_f(8 * wave + row_rel)) & 7);
-    dma_sel_off[m] = 16 * c | ((row_rel != (64 * m) / 72) ? (1 << 15) : 0);
-  }
+  int dma_sel_off[RING_DMA_PER_WAVE];  // per-lane constants of this wave's ring loads
+  ring_dma_offsets(dma_sel_off, wave, lane);
 
   for_each_piece<R128_THREADS>(a, w, plan, [&](int bb, int rt, int k0, int k1, int seq, int tot) {
     // ---- one piece: rows [128 rt, 128 rt + 128) of request bb, keys [k0, k1)
@@ -792,6 +832,7 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
     for (int m = 0; m < 16; ++m) st.o[m] = f32x16{};
     st.m_ref = NEG_INF;
     st.l_part = 0.f;
+    st.l_out = 0.f;
 
     // sub-pieces whose block-table span fits the LDS window
     const int span_keys = (R128_BT_WIN - 1) * a.bs;
@@ -820,10 +861,11 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
     }
     // partial slot: O^T in the accumulator layout [m][row][h][i] (the 16
     // values a lane holds per 32x32 tile are contiguous: 4 x 16-byte
-    // stores), then m and l per row
-    float l_row = st.l_part + __shfl_xor(st.l_part, 32, 64);
+    // stores), then per row m, the fp32 and the bf16 sums of P
+    const float l_row = st.l_part + __shfl_xor(st.l_part, 32, 64);
+    const float lo_row = st.l_out + __shfl_xor(st.l_out, 32, 64);
     const int slot = w + bb * a.n_rt + rt;
-    float* ps = a.partials + (int64_t)slot * (R128_ROWS * D_V + 2 * R128_ROWS);
+    float* ps = a.partials + (int64_t)slot * (R128_ROWS * D_V + 3 * R128_ROWS);
     const int prow = wave * 32 + (lane & 31), h = lane >> 5;
     float* pl = ps + (prow * 2 + h) * 16;
 #pragma unroll
@@ -837,6 +879,7 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
     if (h == 0) {
       ps[R128_ROWS * D_V + prow] = st.m_ref;
       ps[R128_ROWS * D_V + R128_ROWS + prow] = l_row;
+      ps[R128_ROWS * D_V + 2 * R128_ROWS + prow] = lo_row;
     }
   });
 }
@@ -848,7 +891,9 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
 // get out = 0, lse = -inf.
 // Partial slot element (row, dv): both kernels store their MFMA accumulator
 // layouts.  M16: [dv/16][g][row][i] with dv % 16 = 4g + i; R128:
-// [dv/32][row][h][i] with dv % 32 = 8*(i/4) + 4h + i%4.
+// [dv/32][row][h][i] with dv % 32 = 8*(i/4) + 4h + i%4.  After the ROWS*512
+// values: m[ROWS] (log2 units), the fp32 sums of P[ROWS] (for the LSE) and
+// the sums of P as rounded to bf16[ROWS] (for the output).
 template <int ROWS>
 __device__ __forceinline__ int slot_index(int row, int dv) {
   if (ROWS == M16_ROWS) return (dv >> 4) * 256 + ((dv & 15) >> 2) * 64 + row * 4 + (dv & 3);
@@ -860,7 +905,7 @@ template <int ROWS>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   constexpr int SLICE = 64;                       // output columns per workgroup
   constexpr int PER = ROWS * SLICE / 256;         // outputs per thread
-  constexpr int SLOT = ROWS * D_V + 2 * ROWS;
+  constexpr int SLOT = ROWS * D_V + 3 * ROWS;
   const int grp = blockIdx.x >> 3, slice = blockIdx.x & 7;
   const int b = grp / a.n_rt, rt = grp - b * a.n_rt;
   const int row = threadIdx.x % ROWS;
@@ -869,10 +914,11 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   if (row_idx >= a.R) return;
   const int64_t T = a.prefix[a.B];
   const int64_t pb = a.prefix[b], pb1 = a.prefix[b + 1];
-  const int nb = (int)((pb1 - pb) / a.n_rt);
+  const int nb = pb1 > pb ? (int)((pb1 - pb) / a.n_rt - a.ovh) : 0;
   int w0 = 0, w1 = -1;
   if (nb > 0) {
-    const int64_t ustart = pb + (int64_t)rt * nb;
+    // the group's key units follow its overhead units
+    const int64_t ustart = pb + (int64_t)rt * (nb + a.ovh) + a.ovh;
     w0 = range_owner(ustart, T, a.G);
     w1 = range_owner(ustart + nb - 1, T, a.G);
   }
@@ -887,7 +933,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     if (a.lse && slice == 0 && threadIdx.x < ROWS) a.lse[orow] = NEG_INF;
     return;
   }
-  float L = 0.f;
+  float L = 0.f, Lo = 0.f;
   float acc[PER];
 #pragma unroll
   for (int c = 0; c < PER; ++c) acc[c] = 0.f;
@@ -896,10 +942,11 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     const float mw = ps[ROWS * D_V + row];
     const float f = (mw == NEG_INF) ? 0.f : fast_exp2(mw - M);
     L += f * ps[ROWS * D_V + ROWS + row];
+    Lo += f * ps[ROWS * D_V + 2 * ROWS + row];
 #pragma unroll
     for (int c = 0; c < PER; ++c) acc[c] += f * ps[slot_index<ROWS>(row, col0 + c)];
   }
-  const float inv = 1.f / L;
+  const float inv = 1.f / Lo;
 #pragma unroll
   for (int c0 = 0; c0 < PER; c0 += 4)
     *reinterpret_cast<bf16x4*>(op + c0) = to_bf16x4(acc[c0] * inv, acc[c0 + 1] * inv, acc[c0 + 2] * inv,
@@ -914,6 +961,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 struct Plan {
   int rows_tile;
   int n_rt;
+  int ovh;
   int G;
   size_t prefix_off, partial_off, bytes;
 };
@@ -942,12 +990,16 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool allow_r12
   const int64_t R = (int64_t)q_len * H;
   p.rows_tile = (R <= M16_ROWS || !allow_r128) ? M16_ROWS : R128_ROWS;
   p.n_rt = (int)((R + p.rows_tile - 1) / p.rows_tile);
-  const int64_t units = (int64_t)B * p.n_rt * (max_seq_len > 0 ? max_seq_len : 1);
+  // per-group overhead in key units, about what a group's start and end
+  // cost in ring time: M16 ~1.5 tiles (the query item and a partial tile),
+  // R128 ~3 tiles (query load, ring refill and the 256 KiB partial store)
+  p.ovh = p.rows_tile == M16_ROWS ? 48 : 96;
+  const int64_t units = (int64_t)B * p.n_rt * ((max_seq_len > 0 ? max_seq_len : 1) + p.ovh);
   int64_t G = (units + 255) / 256;  // at least 256 keys per workgroup
   if (G > cus) G = cus;
   if (G < 1) G = 1;
   p.G = (int)G;
-  const size_t slot = (size_t)(p.rows_tile * D_V + 2 * p.rows_tile) * sizeof(float);
+  const size_t slot = (size_t)(p.rows_tile * D_V + 3 * p.rows_tile) * sizeof(float);
   p.prefix_off = 0;
   p.partial_off = align_up((size_t)(B + 1) * sizeof(int64_t));
   p.bytes = p.partial_off + align_up(((size_t)p.G + (size_t)B * p.n_rt) * slot);
@@ -1006,6 +1058,7 @@ extern "C" int mla_decode(const void* q, const void* kv_cache, const int32_t* bl
   a.scale_log2 = scale * LOG2E;
   a.lse_base = lse_base;
   a.n_rt = p.n_rt;
+  a.ovh = p.ovh;
   a.G = p.G;
   a.prefix = reinterpret_cast<int64_t*>(static_cast<uint8_t*>(workspace) + p.prefix_off);
   a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + p.partial_off);

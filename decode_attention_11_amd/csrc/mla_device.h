@@ -34,6 +34,17 @@ __device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) 
   return __builtin_convertvector(v, bf16x4);
 }
 
+// acc + the sum of the 8 bf16 values (v_dot2c_f32_bf16 against ones, fp32
+// accumulation): the denominator that matches P as the P*V product sees it.
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), ones, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), ones, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), ones, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), ones, acc, false);
+  return acc;
+}
+
 typedef __attribute__((address_space(1))) const bf16x8 global_bf16x8;
 typedef __attribute__((address_space(1))) const int32_t global_i32;
 
