@@ -284,31 +284,50 @@ __device__ __forceinline__ void ring_dma_offsets(int (&sel_off)[RING_DMA_PER_WAV
   }
 }
 
-// Issue this wave's 9 loads of its 8 rows; lane k < 8 holds the global
-// address of row 8w + k in rowp (the other lanes' values are ignored).
-__device__ __forceinline__ void ring_issue_rows(const uint8_t* rowp, uint32_t stage_lds, int wave,
-                                                const int (&sel_off)[RING_DMA_PER_WAVE]) {
-  const uint64_t row64 = reinterpret_cast<uint64_t>(rowp);
+// The 8 row addresses of a wave's share of a tile (lane k < 8 of rowp holds
+// the global address of row 8w + k; the other lanes' values are ignored),
+// made wave-uniform, and the stage they go to.
+struct RingRows {
   uint64_t rows[8];
+  uint32_t stage_lds;
+};
+
+__device__ __forceinline__ RingRows ring_rows(const uint8_t* rowp, uint32_t stage_lds) {
+  RingRows rr;
+  const uint64_t row64 = reinterpret_cast<uint64_t>(rowp);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)row64, j);
     const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(row64 >> 32), j);
-    rows[j] = ((uint64_t)hi << 32) | lo;
+    rr.rows[j] = ((uint64_t)hi << 32) | lo;
   }
+  rr.stage_lds = stage_lds;
+  return rr;
+}
+
+// Load instruction m (0..8) of a wave's share.  Issuing the nine one at a
+// time between MFMAs keeps the address unit busy in the background instead
+// of stalling every wave behind a burst of 36 loads.
+__device__ __forceinline__ void ring_issue_one(const RingRows& rr, int m, int wave,
+                                               const int (&sel_off)[RING_DMA_PER_WAVE]) {
+  const int rlo = (64 * m) / 72;
+  const int rhi = (64 * m + 63) / 72;
+  const int so = sel_off[m];
+  // lanes in the higher row add the (uniform) distance between the two row
+  // addresses; arithmetic rather than a select keeps the compiler from
+  // turning it into a compare chain over all eight rows
+  const uint64_t dist = rr.rows[rhi] - rr.rows[rlo];
+  const uint64_t msk = (uint64_t)0 - (uint64_t)((uint32_t)so >> 15);
+  dma16(reinterpret_cast<const void*>(rr.rows[rlo] + (dist & msk) + (so & 0x7fff)),
+        rr.stage_lds + 1024 * (RING_DMA_PER_WAVE * wave + m));
+}
+
+// All nine loads of a wave's 8 rows at once.
+__device__ __forceinline__ void ring_issue_rows(const uint8_t* rowp, uint32_t stage_lds, int wave,
+                                                const int (&sel_off)[RING_DMA_PER_WAVE]) {
+  const RingRows rr = ring_rows(rowp, stage_lds);
 #pragma unroll
-  for (int m = 0; m < RING_DMA_PER_WAVE; ++m) {
-    const int rlo = (64 * m) / 72;
-    const int rhi = (64 * m + 63) / 72;
-    const int so = sel_off[m];
-    // lanes in the higher row add the (uniform) distance between the two row
-    // addresses; arithmetic rather than a select keeps the compiler from
-    // turning it into a compare chain over all eight rows
-    const uint64_t dist = rows[rhi] - rows[rlo];
-    const uint64_t msk = (uint64_t)0 - (uint64_t)((uint32_t)so >> 15);
-    dma16(reinterpret_cast<const void*>(rows[rlo] + (dist & msk) + (so & 0x7fff)),
-          stage_lds + 1024 * (RING_DMA_PER_WAVE * wave + m));
-  }
+  for (int m = 0; m < RING_DMA_PER_WAVE; ++m) ring_issue_one(rr, m, wave, sel_off);
 }
 
 // ---------------------------------------------------------------- M16 partial
@@ -645,16 +664,19 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
 
 // ---------------------------------------------------------------- R128 partial
 // Compute-bound family: more than 16 rows per request (multi-token or many
-// heads: 4 x 128 or 16 x 128 rows).  A workgroup owns 128 rows (4 waves x 32
-// rows) of one request and a key range; the 32-key tiles of the latent KV are
-// shared by the four waves through a 3-stage LDS ring filled by direct
-// global->LDS loads.  Scores S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with K
-// from LDS and Q^T in registers (144 VGPRs); each lane then holds 16 keys of
-// one row, so P^T feeds O^T += V^T P^T (V^T by ds_read_b64_tr_b16) without
-// leaving registers; O^T (32 rows x 512) lives in 256 MFMA accumulator
-// registers.  The ring's loads are issued by inline assembly and waited on
-// with explicit counts: the compiler would otherwise drain every in-flight
-// LDS load at each barrier.
+// heads: 4 x 128 or 16 x 128 rows), power-of-two block sizes.  A workgroup
+// owns 128 rows of one request and a key range; the 32-key tiles of the latent
+// KV are shared by the four waves through a 3-stage LDS ring.
+//
+// Work split.  Scores and softmax: wave w owns rows 32w .. 32w+31 and
+// computes S^T = K Q^T for them on v_mfma_f32_32x32x16_bf16 (K from LDS, Q^T
+// in registers and LDS); each lane then holds 16 keys of one row.  The wave
+// writes its bf16 P tile and a per-row rescale factor to LDS.  After one
+// barrier, values are split by column instead: wave w accumulates
+// O^T[128w .. 128w+127][all 128 rows] (16 32x32 fp32 blocks in the 256 MFMA
+// accumulator registers) from V^T (ds_read_b64_tr_b16, its own 128 columns
+// only) and P^T read back from LDS.  Every wave therefore reads each V
+// column once per tile instead of all 512, and P crosses LDS once.
 constexpr int R128_THREADS = 256;
 constexpr int R128_ROWS = 128;
 constexpr int R128_TILE = RING_TILE;          // keys per tile
@@ -665,13 +687,13 @@ constexpr int R128_NS = 3;                    // ring stages
 constexpr int R128_BT_WIN = 1024;             // block-table entries held in LDS per sub-piece
 constexpr int R128_QREG = 28;                 // Q^T k-steps (of 16 dims) kept in registers; the rest in LDS
 constexpr int R128_QLDS = 36 - R128_QREG;
+constexpr int R128_PROW = 80;                 // LDS bytes per row of the P tile (64 + 16: conflict-free reads)
 constexpr float R128_RESCALE_LOG2 = 8.f;
 
 
-// Issue this wave's loads of tile [ts, ts+32) into a stage (rows 8w..8w+7).
-__device__ __forceinline__ void r128_issue_tile(const DecodeArgs& a, const int* bt_lds, int e0, int ts, int k1,
-                                                uint32_t stage_lds, int wave, int lane,
-                                                const int (&dma_sel_off)[RING_DMA_PER_WAVE]) {
+// Row addresses of this wave's share (rows 8w..8w+7) of tile [ts, ts+32).
+__device__ __forceinline__ RingRows r128_tile_rows(const DecodeArgs& a, const int* bt_lds, int e0, int ts, int k1,
+                                                   uint32_t stage_lds, int wave, int lane) {
   // lanes 0..7 resolve the row address of key ts + 8*wave + lane (or the zero row)
   const int k = lane & 7;
   const int t = ts + 8 * wave + k;
@@ -683,19 +705,26 @@ __device__ __forceinline__ void r128_issue_tile(const DecodeArgs& a, const int* 
     if ((unsigned)blk < (unsigned)a.num_blocks)
       rowp = a.kv + ((int64_t)blk * a.bs + (t & (a.bs - 1))) * ROW_BYTES;
   }
-  ring_issue_rows(rowp, stage_lds, wave, dma_sel_off);
+  return ring_rows(rowp, stage_lds);
 }
 
+// o[4d + rb]: value columns 128w + 32d .. +31, rows 32rb .. +31 of O^T.
+// m_ref, l_part, l_out: the softmax state of this wave's own row
+// 32w + lane%32 (both lane halves hold the same values).
 struct R128State {
   f32x16 o[16];
-  float m_ref, l_part, l_out;  // l_part: sum of fp32 P (LSE); l_out: of bf16 P (output)
+  float m_ref, l_part, l_out;
 };
 
+// One 32-key tile; the nine ring loads of a later tile (nxt) are issued one
+// every four score MFMAs.
 __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R128_QREG], const uint8_t* q_tail,
-                                             const uint8_t* stage, float scale_log2, int ts, int k1, int nrow,
-                                             int lane) {
+                                             const uint8_t* stage, uint8_t* p_lds, float* alpha_lds,
+                                             float scale_log2, int ts, int k1, int nrow, int lane, int wave,
+                                             const RingRows& nxt, const int (&sel_off)[RING_DMA_PER_WAVE]) {
   const int r = lane & 31, h = lane >> 5;
-  // S^T[key][row]: lane holds keys 8*(i/4) + 4h + i%4 of row r
+  // ---- scores of this wave's rows: S^T[key][row], lane holds keys
+  // 8*(i/4) + 4h + i%4 of row r
   f32x16 sc = {};
   // k-step kk = 4a + b reads logical chunk 2kk + h of row r: physical byte
   // 128a + 16*((2b + h) ^ f(r)) of the row
@@ -704,20 +733,28 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R
   const uint8_t* kp[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) kp[b] = krow + 16 * ((2 * b + h) ^ fk);
-  // K fragments are read two k-steps ahead of their MFMA (LDS latency would
-  // otherwise be exposed at every step); the last dims of Q^T come from this
-  // wave's LDS copy, laid out [kk][lane]
-  bf16x8 kf[3];
-  kf[0] = *reinterpret_cast<const bf16x8*>(kp[0]);
-  kf[1] = *reinterpret_cast<const bf16x8*>(kp[1]);
+  // K fragments (and the last k-steps of Q^T, from this wave's LDS copy laid
+  // out [kk][lane]) are read three k-steps ahead of their MFMA
+  bf16x8 kf[4], qt[4];
+  auto q_at = [&](int kk) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(q_tail + ((kk - R128_QREG) * 64 + lane) * 16);
+  };
+#pragma unroll
+  for (int kk = 0; kk < 3; ++kk) {
+    kf[kk] = *reinterpret_cast<const bf16x8*>(kp[kk & 3] + 128 * (kk >> 2));
+    if (kk >= R128_QREG) qt[kk % 4] = q_at(kk);
+  }
 #pragma unroll
   for (int kk = 0; kk < 36; ++kk) {
-    if (kk + 2 < 36)
-      kf[(kk + 2) % 3] = *reinterpret_cast<const bf16x8*>(kp[(kk + 2) & 3] + 128 * ((kk + 2) >> 2));
-    const bf16x8 qv = kk < R128_QREG ? qf[kk < R128_QREG ? kk : 0]
-                                     : *reinterpret_cast<const bf16x8*>(q_tail + ((kk - R128_QREG) * 64 + lane) * 16);
-    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % 3], qv, sc, 0, 0, 0);
+    if (kk + 3 < 36) {
+      kf[(kk + 3) % 4] = *reinterpret_cast<const bf16x8*>(kp[(kk + 3) & 3] + 128 * ((kk + 3) >> 2));
+      if (kk + 3 >= R128_QREG) qt[(kk + 3) % 4] = q_at(kk + 3);
+    }
+    if ((kk & 3) == 0) ring_issue_one(nxt, kk >> 2, wave, sel_off);
+    const bf16x8 qv = kk < R128_QREG ? qf[kk < R128_QREG ? kk : 0] : qt[kk % 4];
+    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % 4], qv, sc, 0, 0, 0);
   }
+  // ---- online softmax of the wave's rows
   float mx = NEG_INF;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -725,24 +762,13 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R
     sc[i] = (t < k1 && t < nrow) ? sc[i] * scale_log2 : NEG_INF;
     mx = fmaxf(mx, sc[i]);
   }
+  float alpha = 1.f;
   if (__ballot(mx > st.m_ref + R128_RESCALE_LOG2) != 0) {
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     if (mx > st.m_ref + R128_RESCALE_LOG2) {
-      const float alpha = fast_exp2(st.m_ref - mx);
+      alpha = fast_exp2(st.m_ref - mx);
       st.l_part *= alpha;
       st.l_out *= alpha;
-      // one 16-register tile at a time, so the rare rescale never needs 256
-      // temporaries at once
-#pragma unroll
-      for (int m = 0; m < 16; ++m)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          // in place on the accumulator register (a plain multiply makes the
-          // register allocator keep two copies of all 256 accumulators)
-          float tmp;
-          asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                       : "+a"(st.o[m][i]), "=&v"(tmp) : "v"(alpha));
-        }
       st.m_ref = mx;
     }
   }
@@ -751,50 +777,76 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R
     sc[i] = (sc[i] == NEG_INF) ? 0.f : fast_exp2(sc[i] - st.m_ref);
     st.l_part += sc[i];
   }
-  bf16x8 pf[2];
+  // P (bf16) of row 32w + r, keys 8q + 4h .. +3 for q = 0..3, into the
+  // workgroup's [128 rows][32 keys] tile; the row's rescale factor beside it
+  uint8_t* prow = p_lds + (32 * wave + r) * R128_PROW + 8 * h;
+  bf16x4 p4[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    p4[q] = to_bf16x4(sc[4 * q + 0], sc[4 * q + 1], sc[4 * q + 2], sc[4 * q + 3]);
+    *reinterpret_cast<bf16x4*>(prow + 16 * q) = p4[q];
+  }
+  st.l_out = sum_bf16x8(__builtin_shufflevector(p4[0], p4[1], 0, 1, 2, 3, 4, 5, 6, 7), st.l_out);
+  st.l_out = sum_bf16x8(__builtin_shufflevector(p4[2], p4[3], 0, 1, 2, 3, 4, 5, 6, 7), st.l_out);
+  if (h == 0) alpha_lds[32 * wave + r] = alpha;
+  __syncthreads();
+  // ---- this wave's value columns for all 128 rows.  The accumulator
+  // column of lane l is row 32rb + l%32 in block rb: rescale the blocks whose
+  // rows moved their reference (rare)
+  float ab[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) ab[rb] = alpha_lds[32 * rb + r];
+  if (__ballot(ab[0] != 1.f || ab[1] != 1.f || ab[2] != 1.f || ab[3] != 1.f) != 0) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          // in place on the accumulator register (a plain multiply makes the
+          // register allocator keep two copies of all 256 accumulators)
+          float tmp;
+          asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                       : "+a"(st.o[4 * d + rb][i]), "=&v"(tmp) : "v"(ab[rb]));
+        }
+  }
+  // O^T[dv][row] += V^T[dv][key] P^T[key][row] over 2 k-steps of 16 keys:
+  // contraction slot 8h + s is key 16ks + 8h + s on both sides.
+  //   B (P^T): lane reads keys 16ks + 8h .. +7 of row 32rb + r (16 bytes).
+  //   A (V^T): two transposed reads, keys 16ks + 8h + 4rd + (i16/4), value
+  //   columns 32D + 16(q%2) + 4(i16%4) .. +3 for D = 4w + d (q = lane/16,
+  //   i16 = lane%16): logical chunk 4D + 2(q%2) + (i16%4)/2, byte 8(i16%2).
+  const int q = lane >> 4, i16 = lane & 15;
+  const uint8_t* vp[2][2];  // [rd][d%2]
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd) {
+    const int vr = 8 * h + 4 * rd + (i16 >> 2);
+    const int fs = ring_swz(vr);
+    const uint8_t* vrow = stage + vr * R128_ROWB + 256 * wave + 8 * (i16 & 1);
+#pragma unroll
+    for (int dp = 0; dp < 2; ++dp) vp[rd][dp] = vrow + 16 * ((4 * dp + 2 * (q & 1) + ((i16 & 3) >> 1)) ^ fs);
+  }
+  const uint8_t* pb = p_lds + r * R128_PROW + 16 * h;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    const bf16x4 lo4 = to_bf16x4(sc[8 * ks + 0], sc[8 * ks + 1], sc[8 * ks + 2], sc[8 * ks + 3]);
-    const bf16x4 hi4 = to_bf16x4(sc[8 * ks + 4], sc[8 * ks + 5], sc[8 * ks + 6], sc[8 * ks + 7]);
-    pf[ks] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-    st.l_out = sum_bf16x8(pf[ks], st.l_out);
-  }
-  // V^T fragments: the MFMA's contraction slot 8h + s pairs with key
-  // 16*ks + 8*(s/4) + 4h + s%4 on the P^T side, so lane (q = lane/16, i)
-  // reads rows 16*ks + 4h (+8) of columns 32*m + 16*(q%2) + i.
-  // Lane (q, i) of a transposed read covers row 16ks + 8hh + 4h + i/4,
-  // logical chunk 4m + 2(q%2) + (i%4)/2, byte 8*(i%2) of it; the swizzle
-  // only depends on hh and on m's parity (per lane).
-  const int q = lane >> 4, i16 = lane & 15;
-  const uint8_t* vrow = stage + (4 * h + (i16 >> 2)) * R128_ROWB + 8 * (i16 & 1);
-  const uint8_t* vp[2][2];
+    bf16x8 bp[4];
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int ft = ring_swz(8 * hh + 4 * h + (i16 >> 2));
+    for (int rb = 0; rb < 4; ++rb) bp[rb] = *reinterpret_cast<const bf16x8*>(pb + 32 * rb * R128_PROW + 32 * ks);
+    i16x4 v[4][2];
 #pragma unroll
-    for (int par = 0; par < 2; ++par)
-      vp[hh][par] = vrow + 8 * hh * R128_ROWB + 16 * ((4 * par + 2 * (q & 1) + ((i16 & 3) >> 1)) ^ ft);
-  }
+    for (int d = 0; d < 4; ++d)
 #pragma unroll
-  for (int m0 = 0; m0 < 16; m0 += 2) {
-    i16x4 v[2][2][2];
+      for (int rd = 0; rd < 2; ++rd)
+        v[d][rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vp[rd][d & 1] + 16 * ks * R128_ROWB + 128 * (d >> 1)));
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int d = 0; d < 4; ++d) {
+      const bf16x8 av = __builtin_shufflevector(__builtin_bit_cast(bf16x4, v[d][0]), __builtin_bit_cast(bf16x4, v[d][1]),
+                                                0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          v[m][ks][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vp[hh][(m0 + m) & 1] + 16 * ks * R128_ROWB + 128 * ((m0 + m) >> 1)));
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x4 a0 = __builtin_bit_cast(bf16x4, v[m][ks][0]);
-        const bf16x4 a1 = __builtin_bit_cast(bf16x4, v[m][ks][1]);
-        st.o[m0 + m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), pf[ks], st.o[m0 + m], 0, 0, 0);
-      }
+      for (int rb = 0; rb < 4; ++rb)
+        st.o[4 * d + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bp[rb], st.o[4 * d + rb], 0, 0, 0);
+    }
   }
 }
 
@@ -802,6 +854,8 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
   __shared__ __attribute__((aligned(1024))) uint8_t ring[R128_NS * R128_STAGE];
   __shared__ int bt_lds[R128_BT_WIN];
   __shared__ __attribute__((aligned(16))) uint8_t q_tail_lds[4][R128_QLDS * 64 * 16];
+  __shared__ __attribute__((aligned(16))) uint8_t p_lds[R128_ROWS * R128_PROW];
+  __shared__ float alpha_lds[R128_ROWS];
   __shared__ PlanLds<R128_THREADS> plan;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -844,39 +898,46 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
       __syncthreads();
       const int nt = (kb - ka + R128_TILE - 1) / R128_TILE;
       // prologue: tiles 0 and 1
-      r128_issue_tile(a, bt_lds, e0, ka, kb, ring_lds, wave, lane, dma_sel_off);
-      r128_issue_tile(a, bt_lds, e0, ka + R128_TILE, kb, ring_lds + R128_STAGE, wave, lane, dma_sel_off);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const RingRows rr = r128_tile_rows(a, bt_lds, e0, ka + p * R128_TILE, kb, ring_lds + p * R128_STAGE, wave, lane);
+#pragma unroll
+        for (int m = 0; m < RING_DMA_PER_WAVE; ++m) ring_issue_one(rr, m, wave, dma_sel_off);
+      }
       for (int it = 0; it < nt; ++it) {
         // tile it landed (only tile it+1 may still be in flight), then
-        // every wave is also done computing tile it-1 ...
+        // every wave is also done with tile it-1 (its stage and the P tile) ...
         WAIT_VMCNT(R128_DMA_PER_WAVE);  // tile it+1's 9 loads may stay in flight
         __syncthreads();
-        // ... so its stage can take tile it+2
-        r128_issue_tile(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb, ring_lds + ((it + 2) % R128_NS) * R128_STAGE,
-                        wave, lane, dma_sel_off);
-        r128_compute(st, qf, q_tail, ring + (it % R128_NS) * R128_STAGE, a.scale_log2, ka + it * R128_TILE, kb,
-                     nrow, lane);
+        // ... so its stage can take tile it+2, loaded while tile it is computed
+        const RingRows nxt = r128_tile_rows(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb,
+                                            ring_lds + ((it + 2) % R128_NS) * R128_STAGE, wave, lane);
+        r128_compute(st, qf, q_tail, ring + (it % R128_NS) * R128_STAGE, p_lds, alpha_lds, a.scale_log2,
+                     ka + it * R128_TILE, kb, nrow, lane, wave, nxt, dma_sel_off);
       }
       WAIT_VMCNT(0);
     }
-    // partial slot: O^T in the accumulator layout [m][row][h][i] (the 16
-    // values a lane holds per 32x32 tile are contiguous: 4 x 16-byte
+    // partial slot: O^T in the accumulator layout [dv/32][row][h][i] (the 16
+    // values a lane holds per 32x32 block are contiguous: 4 x 16-byte
     // stores), then per row m, the fp32 and the bf16 sums of P
     const float l_row = st.l_part + __shfl_xor(st.l_part, 32, 64);
     const float lo_row = st.l_out + __shfl_xor(st.l_out, 32, 64);
     const int slot = w + bb * a.n_rt + rt;
     float* ps = a.partials + (int64_t)slot * (R128_ROWS * D_V + 3 * R128_ROWS);
-    const int prow = wave * 32 + (lane & 31), h = lane >> 5;
-    float* pl = ps + (prow * 2 + h) * 16;
+    const int r = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
+    for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<f32x4*>(pl + m * (R128_ROWS * 32) + 4 * c) =
-            f32x4{st.o[m][4 * c], st.o[m][4 * c + 1], st.o[m][4 * c + 2], st.o[m][4 * c + 3]};
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      for (int rb = 0; rb < 4; ++rb) {
+        float* pl = ps + ((4 * wave + d) * R128_ROWS + 32 * rb + r) * 32 + h * 16;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          *reinterpret_cast<f32x4*>(pl + 4 * c) = f32x4{st.o[4 * d + rb][4 * c], st.o[4 * d + rb][4 * c + 1],
+                                                        st.o[4 * d + rb][4 * c + 2], st.o[4 * d + rb][4 * c + 3]};
+        __builtin_amdgcn_sched_barrier(0);
+      }
     if (h == 0) {
+      const int prow = wave * 32 + r;
       ps[R128_ROWS * D_V + prow] = st.m_ref;
       ps[R128_ROWS * D_V + R128_ROWS + prow] = l_row;
       ps[R128_ROWS * D_V + 2 * R128_ROWS + prow] = lo_row;
