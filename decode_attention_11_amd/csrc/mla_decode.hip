@@ -505,9 +505,12 @@ __device__ __forceinline__ void m16_compute(M16State& st, const bf16x8 (&qf)[M16
       st.m_ref = mx;
     }
   }
+  // masked scores are -inf and exp2(-inf) = 0; a row with no visible key
+  // yet has only -inf scores and a -inf reference, so it subtracts 0
+  const float m_sub = st.m_ref == NEG_INF ? 0.f : st.m_ref;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    p[e] = (p[e] == NEG_INF) ? 0.f : fast_exp2(p[e] - st.m_ref);
+    p[e] = fast_exp2(p[e] - m_sub);
     st.l_part += p[e];
   }
   // P^T as the B operand: contraction slot 8g+e is key 4g+e of half e/4
@@ -720,8 +723,9 @@ struct R128State {
 // every four score MFMAs.
 __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R128_QREG], const uint8_t* q_tail,
                                              const uint8_t* stage, uint8_t* p_lds, float* alpha_lds,
-                                             float scale_log2, int ts, int k1, int nrow, int lane, int wave,
-                                             const RingRows& nxt, const int (&sel_off)[RING_DMA_PER_WAVE]) {
+                                             float scale_log2, int ts, int k1, int nrow, int kfull, int lane,
+                                             int wave, const RingRows& nxt,
+                                             const int (&sel_off)[RING_DMA_PER_WAVE]) {
   const int r = lane & 31, h = lane >> 5;
   // ---- scores of this wave's rows: S^T[key][row], lane holds keys
   // 8*(i/4) + 4h + i%4 of row r
@@ -753,14 +757,27 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R
     if ((kk & 3) == 0) ring_issue_one(nxt, kk >> 2, wave, sel_off);
     const bf16x8 qv = kk < R128_QREG ? qf[kk < R128_QREG ? kk : 0] : qt[kk % 4];
     sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % 4], qv, sc, 0, 0, 0);
+    // keep each step's reads three steps ahead of their MFMA (the scheduler
+    // would otherwise sink them next to their use)
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // ---- online softmax of the wave's rows
+  // ---- online softmax of the wave's rows (keys past the piece or past a
+  // row's bound masked; tiles below kfull, the wave's smallest bound, need
+  // no mask)
   float mx = NEG_INF;
+  if (ts + R128_TILE <= kfull) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int t = ts + 8 * (i >> 2) + 4 * h + (i & 3);
-    sc[i] = (t < k1 && t < nrow) ? sc[i] * scale_log2 : NEG_INF;
-    mx = fmaxf(mx, sc[i]);
+    for (int i = 0; i < 16; ++i) {
+      sc[i] *= scale_log2;
+      mx = fmaxf(mx, sc[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = ts + 8 * (i >> 2) + 4 * h + (i & 3);
+      sc[i] = (t < k1 && t < nrow) ? sc[i] * scale_log2 : NEG_INF;
+      mx = fmaxf(mx, sc[i]);
+    }
   }
   float alpha = 1.f;
   if (__ballot(mx > st.m_ref + R128_RESCALE_LOG2) != 0) {
@@ -772,9 +789,12 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R
       st.m_ref = mx;
     }
   }
+  // masked scores are -inf and exp2(-inf) = 0; a row with no visible key
+  // yet has only -inf scores and a -inf reference, so it subtracts 0
+  const float m_sub = st.m_ref == NEG_INF ? 0.f : st.m_ref;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    sc[i] = (sc[i] == NEG_INF) ? 0.f : fast_exp2(sc[i] - st.m_ref);
+    sc[i] = fast_exp2(sc[i] - m_sub);
     st.l_part += sc[i];
   }
   // P (bf16) of row 32w + r, keys 8q + 4h .. +3 for q = 0..3, into the
@@ -870,6 +890,11 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
     const int my_row = rt * R128_ROWS + wave * 32 + (lane & 31);
     const bool row_ok = my_row < a.R;
     const int nrow = row_ok ? row_bound(seq, tot, a.Q, my_row / a.H, a.W, a.rank, a.causal) : 0;
+    // the smallest bound over the wave's rows: tiles below it are unmasked
+    int nmin = nrow;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) nmin = min(nmin, __shfl_xor(nmin, off, 64));
+    nmin = __builtin_amdgcn_readfirstlane(nmin);
     bf16x8 qf[R128_QREG];
     uint8_t* q_tail = q_tail_lds[wave];
     {
@@ -913,7 +938,7 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
         const RingRows nxt = r128_tile_rows(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb,
                                             ring_lds + ((it + 2) % R128_NS) * R128_STAGE, wave, lane);
         r128_compute(st, qf, q_tail, ring + (it % R128_NS) * R128_STAGE, p_lds, alpha_lds, a.scale_log2,
-                     ka + it * R128_TILE, kb, nrow, lane, wave, nxt, dma_sel_off);
+                     ka + it * R128_TILE, kb, nrow, min(kb, nmin), lane, wave, nxt, dma_sel_off);
       }
       WAIT_VMCNT(0);
     }
