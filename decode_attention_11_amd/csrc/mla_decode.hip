@@ -711,6 +711,38 @@ __device__ __forceinline__ RingRows r128_tile_rows(const DecodeArgs& a, const in
   return ring_rows(rowp, stage_lds);
 }
 
+// Per-lane LDS byte offsets inside a stage, fixed for the whole kernel (the
+// stage base is one wave-uniform value per tile, so every address costs a
+// single add).
+struct R128LaneOff {
+  uint32_t k[4];      // K fragment of k-step 4a + b: k[b] + 128a
+  uint32_t v[2][2];   // V^T transposed reads [rd][d%2]: + 16*1152*ks + 128*(d/2)
+};
+
+__device__ __forceinline__ R128LaneOff r128_lane_offsets(int lane, int wave) {
+  R128LaneOff lo;
+  const int r = lane & 31, h = lane >> 5;
+  // k-step kk = 4a + b reads logical chunk 2kk + h of row r: physical byte
+  // 128a + 16*((2b + h) ^ f(r)) of the row
+  const int fk = ring_swz(r);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) lo.k[b] = r * R128_ROWB + 16 * ((2 * b + h) ^ fk);
+  // V^T: lane (q, i16) of a transposed read covers key row 8h + 4rd + i16/4
+  // (+16ks), logical chunk 4D + 2(q%2) + (i16%4)/2 for D = 4w + d, byte
+  // 8(i16%2)
+  const int q = lane >> 4, i16 = lane & 15;
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd) {
+    const int vr = 8 * h + 4 * rd + (i16 >> 2);
+    const int fs = ring_swz(vr);
+#pragma unroll
+    for (int dp = 0; dp < 2; ++dp)
+      lo.v[rd][dp] = vr * R128_ROWB + 256 * wave + 8 * (i16 & 1) +
+                     16 * ((4 * dp + 2 * (q & 1) + ((i16 & 3) >> 1)) ^ fs);
+  }
+  return lo;
+}
+
 // o[4d + rb]: value columns 128w + 32d .. +31, rows 32rb .. +31 of O^T.
 // m_ref, l_part, l_out: the softmax state of this wave's own row
 // 32w + lane%32 (both lane halves hold the same values).
@@ -725,18 +757,14 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R
                                              const uint8_t* stage, uint8_t* p_lds, float* alpha_lds,
                                              float scale_log2, int ts, int k1, int nrow, int kfull, int lane,
                                              int wave, const RingRows& nxt,
-                                             const int (&sel_off)[RING_DMA_PER_WAVE]) {
+                                             const int (&sel_off)[RING_DMA_PER_WAVE], const R128LaneOff& lo) {
   const int r = lane & 31, h = lane >> 5;
   // ---- scores of this wave's rows: S^T[key][row], lane holds keys
   // 8*(i/4) + 4h + i%4 of row r
   f32x16 sc = {};
-  // k-step kk = 4a + b reads logical chunk 2kk + h of row r: physical byte
-  // 128a + 16*((2b + h) ^ f(r)) of the row
-  const int fk = ring_swz(r);
-  const uint8_t* krow = stage + r * R128_ROWB;
   const uint8_t* kp[4];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) kp[b] = krow + 16 * ((2 * b + h) ^ fk);
+  for (int b = 0; b < 4; ++b) kp[b] = stage + lo.k[b];
   // K fragments (and the last k-steps of Q^T, from this wave's LDS copy laid
   // out [kk][lane]) are read three k-steps ahead of their MFMA
   bf16x8 kf[4], qt[4];
@@ -836,16 +864,11 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R
   //   A (V^T): two transposed reads, keys 16ks + 8h + 4rd + (i16/4), value
   //   columns 32D + 16(q%2) + 4(i16%4) .. +3 for D = 4w + d (q = lane/16,
   //   i16 = lane%16): logical chunk 4D + 2(q%2) + (i16%4)/2, byte 8(i16%2).
-  const int q = lane >> 4, i16 = lane & 15;
   const uint8_t* vp[2][2];  // [rd][d%2]
 #pragma unroll
-  for (int rd = 0; rd < 2; ++rd) {
-    const int vr = 8 * h + 4 * rd + (i16 >> 2);
-    const int fs = ring_swz(vr);
-    const uint8_t* vrow = stage + vr * R128_ROWB + 256 * wave + 8 * (i16 & 1);
+  for (int rd = 0; rd < 2; ++rd)
 #pragma unroll
-    for (int dp = 0; dp < 2; ++dp) vp[rd][dp] = vrow + 16 * ((4 * dp + 2 * (q & 1) + ((i16 & 3) >> 1)) ^ fs);
-  }
+    for (int dp = 0; dp < 2; ++dp) vp[rd][dp] = stage + lo.v[rd][dp];
   const uint8_t* pb = p_lds + r * R128_PROW + 16 * h;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
@@ -883,6 +906,7 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
   int dma_sel_off[RING_DMA_PER_WAVE];  // per-lane constants of this wave's ring loads
   ring_dma_offsets(dma_sel_off, wave, lane);
+  const R128LaneOff lane_off = r128_lane_offsets(lane, wave);
 
   for_each_piece<R128_THREADS>(a, w, plan, [&](int bb, int rt, int k0, int k1, int seq, int tot) {
     // ---- one piece: rows [128 rt, 128 rt + 128) of request bb, keys [k0, k1)
@@ -929,16 +953,21 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
 #pragma unroll
         for (int m = 0; m < RING_DMA_PER_WAVE; ++m) ring_issue_one(rr, m, wave, dma_sel_off);
       }
+      // stage offsets of tiles it and it+2, rotated instead of computed
+      // from it % 3 (which costs every LDS address extra instructions)
+      uint32_t cur = 0, nxt_off = 2 * R128_STAGE;
       for (int it = 0; it < nt; ++it) {
         // tile it landed (only tile it+1 may still be in flight), then
         // every wave is also done with tile it-1 (its stage and the P tile) ...
         WAIT_VMCNT(R128_DMA_PER_WAVE);  // tile it+1's 9 loads may stay in flight
         __syncthreads();
         // ... so its stage can take tile it+2, loaded while tile it is computed
-        const RingRows nxt = r128_tile_rows(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb,
-                                            ring_lds + ((it + 2) % R128_NS) * R128_STAGE, wave, lane);
-        r128_compute(st, qf, q_tail, ring + (it % R128_NS) * R128_STAGE, p_lds, alpha_lds, a.scale_log2,
-                     ka + it * R128_TILE, kb, nrow, min(kb, nmin), lane, wave, nxt, dma_sel_off);
+        const RingRows nxt = r128_tile_rows(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb, ring_lds + nxt_off, wave,
+                                            lane);
+        r128_compute(st, qf, q_tail, ring + cur, p_lds, alpha_lds, a.scale_log2, ka + it * R128_TILE, kb, nrow,
+                     min(kb, nmin), lane, wave, nxt, dma_sel_off, lane_off);
+        nxt_off = cur;
+        cur = __builtin_amdgcn_readfirstlane(cur == (R128_NS - 1) * R128_STAGE ? 0u : cur + R128_STAGE);
       }
       WAIT_VMCNT(0);
     }
