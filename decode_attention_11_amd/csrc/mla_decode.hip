@@ -322,10 +322,8 @@ __device__ __forceinline__ void ring_issue_one(const RingRows& rr, int m, int wa
         rr.stage_lds + 1024 * (RING_DMA_PER_WAVE * wave + m));
 }
 
-// All nine loads of a wave's 8 rows at once.
-__device__ __forceinline__ void ring_issue_rows(const uint8_t* rowp, uint32_t stage_lds, int wave,
-                                                const int (&sel_off)[RING_DMA_PER_WAVE]) {
-  const RingRows rr = ring_rows(rowp, stage_lds);
+// All nine loads of a wave's share at once.
+__device__ __forceinline__ void ring_issue_all(const RingRows& rr, int wave, const int (&sel_off)[RING_DMA_PER_WAVE]) {
 #pragma unroll
   for (int m = 0; m < RING_DMA_PER_WAVE; ++m) ring_issue_one(rr, m, wave, sel_off);
 }
@@ -414,13 +412,13 @@ __device__ __forceinline__ void m16_advance(M16Cursor& c, const M16Seg* segs, in
   }
 }
 
-// Issue this wave's 9 loads of ring item c (rows 8w..8w+7 of the stage).  A
+// Row addresses of this wave's share of ring item c (rows 8w..8w+7 of the
+// stage; its 9 loads are issued from them).  A
 // Q item loads the group's 16 query rows as rows 0..15 (waves 0 and 1);
 // items past the end, and rows 16..31 of a Q item, load the zero row, so
 // every wave issues 9 loads per item.
-__device__ __forceinline__ void m16_issue_item(const DecodeArgs& a, const int* bt_lds, int nseg, const M16Cursor& c,
-                                               uint32_t stage_lds, int wave, int lane,
-                                               const int (&sel_off)[RING_DMA_PER_WAVE]) {
+__device__ __forceinline__ RingRows m16_item_rows(const DecodeArgs& a, const int* bt_lds, int nseg,
+                                                  const M16Cursor& c, uint32_t stage_lds, int wave, int lane) {
   const int r = 8 * wave + (lane & 7);  // the stage row this lane resolves (lanes 0..7 matter)
   const uint8_t* rowp = reinterpret_cast<const uint8_t*>(kZeroRow);
   asm volatile("" : "+v"(rowp));
@@ -437,7 +435,7 @@ __device__ __forceinline__ void m16_issue_item(const DecodeArgs& a, const int* b
       }
     }
   }
-  ring_issue_rows(rowp, stage_lds, wave, sel_off);
+  return ring_rows(rowp, stage_lds);
 }
 
 // One 32-key tile: this wave's quarter of S^T, the exchange of the partial
@@ -445,7 +443,7 @@ __device__ __forceinline__ void m16_issue_item(const DecodeArgs& a, const int* b
 // quarter of O^T += V^T P^T.  qf holds the wave's 9 k-steps of Q^T.
 __device__ __forceinline__ void m16_compute(M16State& st, const bf16x8 (&qf)[M16_KSTEPS], const uint8_t* stage,
                                             uint8_t* xchg, float scale_log2, int ts, int k1, int nrow, int lane,
-                                            int wave) {
+                                            int wave, const RingRows& nxt, const int (&sel_off)[RING_DMA_PER_WAVE]) {
   const int li = lane & 15, g = lane >> 4;
   // S^T[key][row] of half wave%2: lane (li, g) gets keys 4g+e for row li;
   // the K fragment of k-step kk = 2k + wave/2 is logical chunk 4kk + g of key
@@ -458,8 +456,11 @@ __device__ __forceinline__ void m16_compute(M16State& st, const bf16x8 (&qf)[M16
   // dependent MFMAs would wait out the MFMA latency at every step)
 #pragma unroll
   for (int kk = 0; kk < M16_KSTEPS; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(kp + 128 * kk);
+  // one ring load of a later item per MFMA step (a burst of 36 after the
+  // barrier would stall the waves behind the address unit)
 #pragma unroll
   for (int kk = 0; kk < M16_KSTEPS; ++kk) {
+    ring_issue_one(nxt, kk, wave, sel_off);
     if (kk & 1)
       sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[kk], sb, 0, 0, 0);
     else
@@ -584,7 +585,7 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
     M16Cursor cc = ci;
 #pragma unroll
     for (int p = 0; p < M16_NS - 1; ++p) {
-      m16_issue_item(a, bt_lds, nseg, ci, ring_lds + p * M16_STAGE, wave, lane, sel_off);
+      ring_issue_all(m16_item_rows(a, bt_lds, nseg, ci, ring_lds + p * M16_STAGE, wave, lane), wave, sel_off);
       m16_advance(ci, segs, nseg);
     }
     for (int it = 0; it < n_items; ++it) {
@@ -593,8 +594,8 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
       WAIT_VMCNT(M16_DMA_PER_WAVE * (M16_NS - 2));
       __syncthreads();
       // ... so its stage can take item it+NS-1
-      m16_issue_item(a, bt_lds, nseg, ci, ring_lds + ((it + M16_NS - 1) % M16_NS) * M16_STAGE, wave, lane,
-                     sel_off);
+      const RingRows nxt =
+          m16_item_rows(a, bt_lds, nseg, ci, ring_lds + ((it + M16_NS - 1) % M16_NS) * M16_STAGE, wave, lane);
       m16_advance(ci, segs, nseg);
       const uint8_t* stage = ring + (it % M16_NS) * M16_STAGE;
       if (cc.j < 0) {
@@ -604,6 +605,7 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
         const uint8_t* qp = stage + ROW_BYTES * li + 16 * ((4 * (wave >> 1) + g) ^ ring_swz(li));
 #pragma unroll
         for (int kk = 0; kk < M16_KSTEPS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 128 * kk);
+        ring_issue_all(nxt, wave, sel_off);
         const int my_row = cc.d.rt * M16_ROWS + li;
         nrow = my_row < a.R ? row_bound(cc.d.seq, cc.d.tot, a.Q, my_row / a.H, a.W, a.rank, a.causal) : 0;
 #pragma unroll
@@ -612,7 +614,8 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
         st.l_part = 0.f;
         st.l_out = 0.f;
       } else {
-        m16_compute(st, qf, stage, xchg, a.scale_log2, cc.d.ka + M16_TILE * cc.j, cc.d.kb, nrow, lane, wave);
+        m16_compute(st, qf, stage, xchg, a.scale_log2, cc.d.ka + M16_TILE * cc.j, cc.d.kb, nrow, lane, wave, nxt,
+                    sel_off);
         if (cc.j == cc.nt - 1 && (cc.d.flags & M16_SEG_LAST)) {
           // partial slot: wave w's O^T tiles T = 8w + mt in the accumulator
           // layout [T][lane][4] (one 16-byte store per lane and tile), then
@@ -950,8 +953,7 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         const RingRows rr = r128_tile_rows(a, bt_lds, e0, ka + p * R128_TILE, kb, ring_lds + p * R128_STAGE, wave, lane);
-#pragma unroll
-        for (int m = 0; m < RING_DMA_PER_WAVE; ++m) ring_issue_one(rr, m, wave, dma_sel_off);
+        ring_issue_all(rr, wave, dma_sel_off);
       }
       // stage offsets of tiles it and it+2, rotated instead of computed
       // from it % 3 (which costs every LDS address extra instructions)
