@@ -136,13 +136,32 @@ struct PlanLds {
   int first_last[2];
 };
 
+// The pieces of request bb (unit offset pb, nbb keys) inside [u0, u1).
+template <class F>
+__device__ __forceinline__ void request_pieces(const DecodeArgs& a, int bb, int64_t pb, int nbb, int sq, int tt,
+                                               int64_t u0, int64_t u1, F&& piece) {
+  if (nbb == 0) return;  // no keys: no units, no pieces
+  const int64_t gu = (int64_t)nbb + a.ovh;    // units per group
+  const int64_t lo = u0 > pb ? u0 - pb : 0;  // first unit of the request in range
+  const int64_t hi = (u1 - pb) < a.n_rt * gu ? u1 - pb : a.n_rt * gu;
+  for (int rt = (int)(lo / gu); (int64_t)rt * gu < hi; ++rt) {
+    // the group's units [rt*gu, (rt+1)*gu): ovh overhead units, then its keys
+    const int64_t g0 = (int64_t)rt * gu;
+    const int64_t a0 = (lo > g0 ? lo - g0 : 0) - a.ovh, a1 = (hi - g0 < gu ? hi - g0 : gu) - a.ovh;
+    const int k0 = __builtin_amdgcn_readfirstlane((int)(a0 > 0 ? a0 : 0));
+    const int k1 = __builtin_amdgcn_readfirstlane((int)(a1 > 0 ? a1 : 0));
+    if (k1 <= k0) continue;  // this range holds only the group's overhead units
+    piece(bb, rt, k0, k1, sq, tt);
+  }
+}
+
 // Calls piece(bb, rt, k0, k1, seq, tot) for every (request, row tile) group
 // that overlaps this workgroup's balanced range of units, in unit order, with
 // the group's keys [k0, k1) inside the range.  Workgroup 0 also stores the
 // request offsets for the combine kernel.  All arguments of piece() are
-// wave-uniform.  With up to NT requests (the usual case) the lengths are
-// read from memory once and one block scan gives both the total and the
-// offsets.
+// wave-uniform.  The workgroup scans the requests in chunks of NT, reading
+// each length once per chunk (with up to NT requests one scan gives both the
+// total and the offsets).
 template <int NT, class F>
 __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int w, PlanLds<NT>& pl, F&& piece) {
   const int tid = threadIdx.x;
@@ -187,26 +206,10 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int w, PlanL
     const int first = pl.first_last[0], last = pl.first_last[1];
     carry += chunk_total;
 
-    for (int i = first; i <= last; ++i) {
-      const int bb = __builtin_amdgcn_readfirstlane(base + i);
-      const int64_t pb = pl.excl[i];
-      const int nbb = __builtin_amdgcn_readfirstlane(pl.nb[i]);
-      const int sq = __builtin_amdgcn_readfirstlane(pl.seq[i]);
-      const int tt = __builtin_amdgcn_readfirstlane(pl.tot[i]);
-      if (nbb == 0) continue;  // no keys: no units, no pieces
-      const int64_t gu = (int64_t)nbb + a.ovh;    // units per group
-      const int64_t lo = u0 > pb ? u0 - pb : 0;  // first unit of the request in range
-      const int64_t hi = (u1 - pb) < a.n_rt * gu ? u1 - pb : a.n_rt * gu;
-      for (int rt = (int)(lo / gu); (int64_t)rt * gu < hi; ++rt) {
-        // the group's units [rt*gu, (rt+1)*gu): ovh overhead units, then its keys
-        const int64_t g0 = (int64_t)rt * gu;
-        const int64_t a0 = (lo > g0 ? lo - g0 : 0) - a.ovh, a1 = (hi - g0 < gu ? hi - g0 : gu) - a.ovh;
-        const int k0 = __builtin_amdgcn_readfirstlane((int)(a0 > 0 ? a0 : 0));
-        const int k1 = __builtin_amdgcn_readfirstlane((int)(a1 > 0 ? a1 : 0));
-        if (k1 <= k0) continue;  // this range holds only the group's overhead units
-        piece(bb, rt, k0, k1, sq, tt);
-      }
-    }
+    for (int i = first; i <= last; ++i)
+      request_pieces(a, __builtin_amdgcn_readfirstlane(base + i), pl.excl[i], __builtin_amdgcn_readfirstlane(pl.nb[i]),
+                     __builtin_amdgcn_readfirstlane(pl.seq[i]), __builtin_amdgcn_readfirstlane(pl.tot[i]), u0, u1,
+                     piece);
     __syncthreads();
   }
 }
@@ -553,7 +556,10 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, g = lane >> 4;
-  const int w = xcd_range_index(blockIdx.x, a.G);
+  // ranges in launch order: each key is read by one workgroup only, so there
+  // is no L2 sharing to gain from grouping ranges by XCD, and grouping
+  // concentrates slow requests on a few XCDs
+  const int w = blockIdx.x;
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
   int sel_off[RING_DMA_PER_WAVE];  // per-lane constants of this wave's ring loads
   ring_dma_offsets(sel_off, wave, lane);
