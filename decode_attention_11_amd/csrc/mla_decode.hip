@@ -57,19 +57,27 @@ struct DecodeArgs {
   float scale_log2;        // softmax scale times log2(e)
   int lse_base;
   int n_rt;                // row tiles per request
-  int ovh;                 // work units charged per (request, row tile) group on top of its keys
-  int G;                   // partial workgroups
+  int ovh;                 // work units charged per piece on top of its keys
+  int nbund;               // balanced key ranges (bundles)
+  int G;                   // partial workgroups: nbund * n_rt, one per (bundle, row tile)
   int64_t* prefix;         // [B+1] unit offsets of the requests
-  float* partials;         // [G + B*n_rt] slots
+  float* partials;         // [(nbund + B) * n_rt] slots
   uint16_t* out;           // bf16 [B*R, 512]
   float* lse;              // [B*R] or null
 };
 
-// Work units of a request: per row tile, its keys plus a fixed overhead
-// (the query rows' load and the partial's store), so that ranges crossing a
-// group boundary get fewer keys.  Requests without keys cost nothing.
+// Work units of a request: its keys plus a fixed overhead (the query rows'
+// load and the partial's store), so that ranges crossing a request boundary
+// get fewer keys.  Requests without keys cost nothing.  The units are those
+// of one row tile: every row tile of a request has the same keys.
 __device__ __forceinline__ int64_t request_units(const DecodeArgs& a, int nb) {
-  return nb > 0 ? (int64_t)a.n_rt * (nb + a.ovh) : 0;
+  return nb > 0 ? (int64_t)nb + a.ovh : 0;
+}
+
+// Partial slot of bundle j's piece of request bb, row tile rt.  For a fixed
+// row tile, the bundles cover the requests in order, so j + bb never repeats.
+__device__ __forceinline__ int64_t piece_slot(const DecodeArgs& a, int j, int bb, int rt) {
+  return ((int64_t)j + bb) * a.n_rt + rt;
 }
 
 // Key count of the largest row (row j = q_len-1 has the longest prefix),
@@ -83,10 +91,10 @@ __device__ __forceinline__ void request_info(const DecodeArgs& a, int b, int& nb
   }
 }
 
-// Workgroups are dispatched to the 8 XCDs round-robin (blockIdx % 8).  The
-// balanced ranges are numbered so that consecutive ranges (the row tiles of
-// one request read the same keys at the same time) sit on one XCD and share
-// its L2.
+// Workgroups are dispatched to the 8 XCDs round-robin (blockIdx % 8).
+// Numbered this way, consecutive indices sit on one XCD; with G/8 a multiple
+// of n_rt, the n_rt workgroups of one bundle (the row tiles of the same keys,
+// read at the same time) share that XCD's L2.
 __device__ __forceinline__ int xcd_range_index(int block, int G) {
   return (G % 8 == 0) ? (block % 8) * (G / 8) + block / 8 : block;
 }
@@ -136,34 +144,29 @@ struct PlanLds {
   int first_last[2];
 };
 
-// The pieces of request bb (unit offset pb, nbb keys) inside [u0, u1).
+// The piece of request bb (unit offset pb, nbb keys) inside [u0, u1): the
+// request's units are ovh overhead units, then one per key.
 template <class F>
-__device__ __forceinline__ void request_pieces(const DecodeArgs& a, int bb, int64_t pb, int nbb, int sq, int tt,
-                                               int64_t u0, int64_t u1, F&& piece) {
-  if (nbb == 0) return;  // no keys: no units, no pieces
-  const int64_t gu = (int64_t)nbb + a.ovh;    // units per group
-  const int64_t lo = u0 > pb ? u0 - pb : 0;  // first unit of the request in range
-  const int64_t hi = (u1 - pb) < a.n_rt * gu ? u1 - pb : a.n_rt * gu;
-  for (int rt = (int)(lo / gu); (int64_t)rt * gu < hi; ++rt) {
-    // the group's units [rt*gu, (rt+1)*gu): ovh overhead units, then its keys
-    const int64_t g0 = (int64_t)rt * gu;
-    const int64_t a0 = (lo > g0 ? lo - g0 : 0) - a.ovh, a1 = (hi - g0 < gu ? hi - g0 : gu) - a.ovh;
-    const int k0 = __builtin_amdgcn_readfirstlane((int)(a0 > 0 ? a0 : 0));
-    const int k1 = __builtin_amdgcn_readfirstlane((int)(a1 > 0 ? a1 : 0));
-    if (k1 <= k0) continue;  // this range holds only the group's overhead units
-    piece(bb, rt, k0, k1, sq, tt);
-  }
+__device__ __forceinline__ void request_piece(const DecodeArgs& a, int bb, int64_t pb, int nbb, int sq, int tt,
+                                              int64_t u0, int64_t u1, int rt, F&& piece) {
+  if (nbb == 0) return;  // no keys: no units, no piece
+  const int64_t a0 = u0 - pb - a.ovh, a1 = u1 - pb - a.ovh;
+  const int k0 = __builtin_amdgcn_readfirstlane((int)(a0 > 0 ? a0 : 0));
+  const int k1 = __builtin_amdgcn_readfirstlane((int)(a1 < nbb ? a1 : nbb));
+  if (k1 <= k0) return;  // the range holds only the request's overhead units
+  piece(bb, rt, k0, k1, sq, tt);
 }
 
-// Calls piece(bb, rt, k0, k1, seq, tot) for every (request, row tile) group
-// that overlaps this workgroup's balanced range of units, in unit order, with
-// the group's keys [k0, k1) inside the range.  Workgroup 0 also stores the
-// request offsets for the combine kernel.  All arguments of piece() are
-// wave-uniform.  The workgroup scans the requests in chunks of NT, reading
-// each length once per chunk (with up to NT requests one scan gives both the
-// total and the offsets).
+// The requests' units are laid end to end and cut into nbund balanced
+// ranges; bundle j's range is processed by n_rt workgroups, one per row tile.
+// Calls piece(bb, rt, k0, k1, seq, tot) for every request that overlaps
+// bundle j's range, in order, with the request's keys [k0, k1) inside the
+// range.  Workgroup (0, 0) also stores the request offsets for the combine
+// kernel.  All arguments of piece() are wave-uniform.  The workgroup scans
+// the requests in chunks of NT, reading each length once per chunk (with up
+// to NT requests one scan gives both the total and the offsets).
 template <int NT, class F>
-__device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int w, PlanLds<NT>& pl, F&& piece) {
+__device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int j, int rt, PlanLds<NT>& pl, F&& piece) {
   const int tid = threadIdx.x;
   int nb, seq, tot;
   request_info(a, tid, nb, seq, tot);
@@ -175,7 +178,7 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int w, PlanL
     request_info(a, base + tid, nb2, seq2, tot2);
     T += block_sum_i64<NT>(request_units(a, nb2), pl.red);
   }
-  const int64_t u0 = (int64_t)w * T / a.G, u1 = (int64_t)(w + 1) * T / a.G;
+  const int64_t u0 = (int64_t)j * T / a.nbund, u1 = (int64_t)(j + 1) * T / a.nbund;
 
   int64_t carry = 0;
   for (int base = 0; base < a.B; base += NT) {
@@ -188,7 +191,7 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int w, PlanL
     const int64_t x = request_units(a, nb);
     incl += carry;
     const int64_t excl = incl - x;
-    if (w == 0 && b < a.B) {
+    if (j == 0 && rt == 0 && b < a.B) {
       a.prefix[b + 1] = incl;
       if (b == 0) a.prefix[0] = 0;
     }
@@ -207,9 +210,9 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int w, PlanL
     carry += chunk_total;
 
     for (int i = first; i <= last; ++i)
-      request_pieces(a, __builtin_amdgcn_readfirstlane(base + i), pl.excl[i], __builtin_amdgcn_readfirstlane(pl.nb[i]),
-                     __builtin_amdgcn_readfirstlane(pl.seq[i]), __builtin_amdgcn_readfirstlane(pl.tot[i]), u0, u1,
-                     piece);
+      request_piece(a, __builtin_amdgcn_readfirstlane(base + i), pl.excl[i], __builtin_amdgcn_readfirstlane(pl.nb[i]),
+                    __builtin_amdgcn_readfirstlane(pl.seq[i]), __builtin_amdgcn_readfirstlane(pl.tot[i]), u0, u1, rt,
+                    piece);
     __syncthreads();
   }
 }
@@ -556,10 +559,10 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, g = lane >> 4;
-  // ranges in launch order: each key is read by one workgroup only, so there
-  // is no L2 sharing to gain from grouping ranges by XCD, and grouping
-  // concentrates slow requests on a few XCDs
-  const int w = blockIdx.x;
+  // ranges in launch order: with one row tile per request each key is read
+  // by one workgroup only, so there is no L2 sharing to gain from grouping
+  // ranges by XCD, and grouping concentrates slow requests on a few XCDs
+  const int bund = blockIdx.x / a.n_rt, tile = blockIdx.x - bund * a.n_rt;
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
   int sel_off[RING_DMA_PER_WAVE];  // per-lane constants of this wave's ring loads
   ring_dma_offsets(sel_off, wave, lane);
@@ -631,8 +634,7 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
           l_row += __shfl_xor(l_row, 32, 64);
           lo_row += __shfl_xor(lo_row, 16, 64);
           lo_row += __shfl_xor(lo_row, 32, 64);
-          const int slot = w + cc.d.bb * a.n_rt + cc.d.rt;
-          float* ps = a.partials + (int64_t)slot * (M16_ROWS * D_V + 3 * M16_ROWS);
+          float* ps = a.partials + piece_slot(a, bund, cc.d.bb, cc.d.rt) * (M16_ROWS * D_V + 3 * M16_ROWS);
 #pragma unroll
           for (int mt = 0; mt < 8; ++mt)
             *reinterpret_cast<f32x4*>(ps + ((M16_DV_WAVE / 16) * wave + mt) * 256 + 4 * lane) = st.o[mt];
@@ -651,7 +653,7 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
     nent = 0;
   };
 
-  for_each_piece<M16_THREADS>(a, w, plan, [&](int bb, int rt, int k0, int k1, int seq, int tot) {
+  for_each_piece<M16_THREADS>(a, bund, tile, plan, [&](int bb, int rt, int k0, int k1, int seq, int tot) {
     // append the piece (rows [16 rt, 16 rt + 16) of request bb, keys [k0, k1))
     // to the batch as one or more segments
     const int32_t* btr = a.bt + (int64_t)bb * a.max_blocks;
@@ -912,12 +914,13 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int w = xcd_range_index(blockIdx.x, a.G);
+  const int bund = w / a.n_rt, tile = w - bund * a.n_rt;
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
   int dma_sel_off[RING_DMA_PER_WAVE];  // per-lane constants of this wave's ring loads
   ring_dma_offsets(dma_sel_off, wave, lane);
   const R128LaneOff lane_off = r128_lane_offsets(lane, wave);
 
-  for_each_piece<R128_THREADS>(a, w, plan, [&](int bb, int rt, int k0, int k1, int seq, int tot) {
+  for_each_piece<R128_THREADS>(a, bund, tile, plan, [&](int bb, int rt, int k0, int k1, int seq, int tot) {
     // ---- one piece: rows [128 rt, 128 rt + 128) of request bb, keys [k0, k1)
     const int32_t* btr = a.bt + (int64_t)bb * a.max_blocks;
     const int my_row = rt * R128_ROWS + wave * 32 + (lane & 31);
@@ -984,8 +987,7 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
     // stores), then per row m, the fp32 and the bf16 sums of P
     const float l_row = st.l_part + __shfl_xor(st.l_part, 32, 64);
     const float lo_row = st.l_out + __shfl_xor(st.l_out, 32, 64);
-    const int slot = w + bb * a.n_rt + rt;
-    float* ps = a.partials + (int64_t)slot * (R128_ROWS * D_V + 3 * R128_ROWS);
+    float* ps = a.partials + piece_slot(a, bund, bb, rt) * (R128_ROWS * D_V + 3 * R128_ROWS);
     const int r = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
@@ -1037,16 +1039,18 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   if (row_idx >= a.R) return;
   const int64_t T = a.prefix[a.B];
   const int64_t pb = a.prefix[b], pb1 = a.prefix[b + 1];
-  const int nb = pb1 > pb ? (int)((pb1 - pb) / a.n_rt - a.ovh) : 0;
-  int w0 = 0, w1 = -1;
+  const int nb = pb1 > pb ? (int)(pb1 - pb - a.ovh) : 0;
+  int j0 = 0, j1 = -1;
   if (nb > 0) {
-    // the group's key units follow its overhead units
-    const int64_t ustart = pb + (int64_t)rt * (nb + a.ovh) + a.ovh;
-    w0 = range_owner(ustart, T, a.G);
-    w1 = range_owner(ustart + nb - 1, T, a.G);
+    // the bundles that hold the request's key units (after its overhead units)
+    j0 = range_owner(pb + a.ovh, T, a.nbund);
+    j1 = range_owner(pb + a.ovh + nb - 1, T, a.nbund);
   }
+  // bundle j's slot of this group: (j + b) * n_rt + rt = j * n_rt + grp; a
+  // bundle with an empty range wrote nothing
   float M = NEG_INF;
-  for (int w = w0; w <= w1; ++w) M = fmaxf(M, a.partials[(int64_t)(w + grp) * SLOT + ROWS * D_V + row]);
+  for (int j = j0; j <= j1; ++j)
+    if (range_nonempty(j, T, a.nbund)) M = fmaxf(M, a.partials[((int64_t)j * a.n_rt + grp) * SLOT + ROWS * D_V + row]);
   const int64_t orow = (int64_t)b * a.R + row_idx;
   uint16_t* op = a.out + orow * D_V + col0;
   static_assert(PER % 4 == 0, "outputs are stored 4 columns at a time");
@@ -1060,8 +1064,9 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   float acc[PER];
 #pragma unroll
   for (int c = 0; c < PER; ++c) acc[c] = 0.f;
-  for (int w = w0; w <= w1; ++w) {
-    const float* ps = a.partials + (int64_t)(w + grp) * SLOT;
+  for (int j = j0; j <= j1; ++j) {
+    if (!range_nonempty(j, T, a.nbund)) continue;
+    const float* ps = a.partials + ((int64_t)j * a.n_rt + grp) * SLOT;
     const float mw = ps[ROWS * D_V + row];
     const float f = (mw == NEG_INF) ? 0.f : fast_exp2(mw - M);
     L += f * ps[ROWS * D_V + ROWS + row];
@@ -1085,6 +1090,7 @@ struct Plan {
   int rows_tile;
   int n_rt;
   int ovh;
+  int nbund;
   int G;
   size_t prefix_off, partial_off, bytes;
 };
@@ -1117,11 +1123,19 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool allow_r12
   // cost in ring time: M16 ~1.5 tiles (the query item and a partial tile),
   // R128 ~3 tiles (query load, ring refill and the 256 KiB partial store)
   p.ovh = p.rows_tile == M16_ROWS ? 48 : 96;
-  const int64_t units = (int64_t)B * p.n_rt * ((max_seq_len > 0 ? max_seq_len : 1) + p.ovh);
-  int64_t G = (units + 255) / 256;  // at least 256 keys per workgroup
-  if (G > cus) G = cus;
-  if (G < 1) G = 1;
-  p.G = (int)G;
+  // bundles: balanced key ranges, each processed by n_rt workgroups (one per
+  // row tile).  The 128-row kernel keeps a bundle's workgroups on one XCD
+  // (8 * k bundles, each XCD holding k whole bundles) so that they share the
+  // keys through its L2; a few CUs idle when n_rt does not divide the CUs of
+  // an XCD.
+  const int per_xcd = cus / 8;
+  int64_t nbund = (p.rows_tile == R128_ROWS && p.n_rt <= per_xcd) ? 8 * (per_xcd / p.n_rt) : cus / p.n_rt;
+  const int64_t units = (int64_t)B * ((max_seq_len > 0 ? max_seq_len : 1) + p.ovh);  // of one row tile
+  const int64_t by_work = (units + 255) / 256;  // at least 256 keys per workgroup
+  if (nbund > by_work) nbund = by_work >= 8 ? by_work / 8 * 8 : by_work;
+  if (nbund < 1) nbund = 1;
+  p.nbund = (int)nbund;
+  p.G = p.nbund * p.n_rt;
   const size_t slot = (size_t)(p.rows_tile * D_V + 3 * p.rows_tile) * sizeof(float);
   p.prefix_off = 0;
   p.partial_off = align_up((size_t)(B + 1) * sizeof(int64_t));
@@ -1182,6 +1196,7 @@ extern "C" int mla_decode(const void* q, const void* kv_cache, const int32_t* bl
   a.lse_base = lse_base;
   a.n_rt = p.n_rt;
   a.ovh = p.ovh;
+  a.nbund = p.nbund;
   a.G = p.G;
   a.prefix = reinterpret_cast<int64_t*>(static_cast<uint8_t*>(workspace) + p.prefix_off);
   a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + p.partial_off);

@@ -89,4 +89,10 @@ __device__ __forceinline__ int range_owner(int64_t u, int64_t T, int G) {
   return (int)(((u + 1) * (int64_t)G - 1) / T);
 }
 
+// Whether range w holds any unit: with fewer units than ranges some are empty
+// (and can lie between the owners of two units).
+__device__ __forceinline__ bool range_nonempty(int w, int64_t T, int G) {
+  return (int64_t)w * T / G < (int64_t)(w + 1) * T / G;
+}
+
 }  // namespace mla

@@ -93,6 +93,26 @@ def test_tight_max_seq_len_packs_many_pieces_per_workgroup(name):
         compare(out, lse, ro, rl, f"{sp.name} r{r} tight")
 
 
+@pytest.mark.parametrize("H", [16, 128])
+def test_fewer_work_units_than_workgroups(H):
+    # a loose max_seq_len plans a full grid for requests that hold fewer work
+    # units than there are ranges: most ranges are empty, some of them between
+    # two ranges that hold keys of the same request.  The combine must read
+    # only the slots written by this call: the workspace first holds NaN bytes,
+    # then the partials of a call on longer requests.
+    msl = 1 << 20
+    small = spec(f"few_units_h{H}", 2, H, 1, True, [5, 20], global_is_null=True, seed=515)
+    big = spec(f"many_units_h{H}", 2, H, 1, True, [3000, 900], global_is_null=True, seed=516)
+    ws = torch.full((mla.mla_decode_workspace_size(2, 1, H, msl),), 0xFF, dtype=torch.uint8, device=dev())
+    for sp in (small, big, small):
+        wl = WL.build(sp)
+        say(f"{sp.name} max_seq_len {msl}")
+        out, lse = Uploaded(wl).run(0, "e", max_seq_len=msl, workspace=ws)
+        torch.cuda.synchronize()
+        ro, rl = oracle_rank(wl, 0, "e")
+        compare(out, lse, ro, rl, f"{sp.name} loose max_seq_len")
+
+
 def test_long_piece_spans_several_block_table_windows():
     # block size 1 and 270k keys: each workgroup range covers more block-table
     # entries than one LDS window holds, so a piece continues across batches;
