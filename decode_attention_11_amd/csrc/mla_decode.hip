@@ -1046,33 +1046,61 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     j0 = range_owner(pb + a.ovh, T, a.nbund);
     j1 = range_owner(pb + a.ovh + nb - 1, T, a.nbund);
   }
-  // bundle j's slot of this group: (j + b) * n_rt + rt = j * n_rt + grp; a
-  // bundle with an empty range wrote nothing
-  float M = NEG_INF;
-  for (int j = j0; j <= j1; ++j)
-    if (range_nonempty(j, T, a.nbund)) M = fmaxf(M, a.partials[((int64_t)j * a.n_rt + grp) * SLOT + ROWS * D_V + row]);
   const int64_t orow = (int64_t)b * a.R + row_idx;
   uint16_t* op = a.out + orow * D_V + col0;
   static_assert(PER % 4 == 0, "outputs are stored 4 columns at a time");
+  // bundle j's slot of this group is (j + b) * n_rt + rt = j * n_rt + grp; a
+  // bundle with an empty range wrote nothing.  The slots are merged NMAX at
+  // a time: all loads of a batch are issued before any is used.  With at
+  // most NMAX slots this is the plain two-pass merge (weights relative to
+  // the overall maximum); later batches rescale the running sums.
+  constexpr int NMAX = ROWS == M16_ROWS ? 8 : 4;
+  float M = NEG_INF, L = 0.f, Lo = 0.f;
+  float acc[PER];
+#pragma unroll
+  for (int c = 0; c < PER; ++c) acc[c] = 0.f;
+  for (int jb = j0; jb <= j1; jb += NMAX) {
+    float mw[NMAX], lw[NMAX], low[NMAX], v[NMAX][PER];
+#pragma unroll
+    for (int t = 0; t < NMAX; ++t) {
+      const int j = jb + t;
+      mw[t] = NEG_INF;
+      lw[t] = low[t] = 0.f;
+#pragma unroll
+      for (int c = 0; c < PER; ++c) v[t][c] = 0.f;
+      if (j <= j1 && range_nonempty(j, T, a.nbund)) {
+        const float* ps = a.partials + ((int64_t)j * a.n_rt + grp) * SLOT;
+        mw[t] = ps[ROWS * D_V + row];
+        lw[t] = ps[ROWS * D_V + ROWS + row];
+        low[t] = ps[ROWS * D_V + 2 * ROWS + row];
+#pragma unroll
+        for (int c = 0; c < PER; ++c) v[t][c] = ps[slot_index<ROWS>(row, col0 + c)];
+      }
+    }
+    float Mb = M;
+#pragma unroll
+    for (int t = 0; t < NMAX; ++t) Mb = fmaxf(Mb, mw[t]);
+    if (Mb == NEG_INF) continue;
+    const float sc = (M == NEG_INF) ? 0.f : fast_exp2(M - Mb);
+    L *= sc;
+    Lo *= sc;
+#pragma unroll
+    for (int c = 0; c < PER; ++c) acc[c] *= sc;
+#pragma unroll
+    for (int t = 0; t < NMAX; ++t) {
+      const float f = (mw[t] == NEG_INF) ? 0.f : fast_exp2(mw[t] - Mb);
+      L += f * lw[t];
+      Lo += f * low[t];
+#pragma unroll
+      for (int c = 0; c < PER; ++c) acc[c] += f * v[t][c];
+    }
+    M = Mb;
+  }
   if (M == NEG_INF) {
 #pragma unroll
     for (int c = 0; c < PER; c += 4) *reinterpret_cast<uint2*>(op + c) = uint2{0u, 0u};
     if (a.lse && slice == 0 && threadIdx.x < ROWS) a.lse[orow] = NEG_INF;
     return;
-  }
-  float L = 0.f, Lo = 0.f;
-  float acc[PER];
-#pragma unroll
-  for (int c = 0; c < PER; ++c) acc[c] = 0.f;
-  for (int j = j0; j <= j1; ++j) {
-    if (!range_nonempty(j, T, a.nbund)) continue;
-    const float* ps = a.partials + ((int64_t)j * a.n_rt + grp) * SLOT;
-    const float mw = ps[ROWS * D_V + row];
-    const float f = (mw == NEG_INF) ? 0.f : fast_exp2(mw - M);
-    L += f * ps[ROWS * D_V + ROWS + row];
-    Lo += f * ps[ROWS * D_V + 2 * ROWS + row];
-#pragma unroll
-    for (int c = 0; c < PER; ++c) acc[c] += f * ps[slot_index<ROWS>(row, col0 + c)];
   }
   const float inv = 1.f / Lo;
 #pragma unroll
