@@ -698,6 +698,8 @@ constexpr int R128_ROWB = ROW_BYTES;          // LDS bytes per key row (unpadded
 constexpr int R128_DMA_PER_WAVE = RING_DMA_PER_WAVE;
 constexpr int R128_STAGE = RING_STAGE;        // 36 KiB
 constexpr int R128_NS = 3;                    // ring stages
+constexpr int R128_O_BYTES = R128_ROWS * D_V * 2;                 // fp16 partial O of a slot
+constexpr int R128_SLOT_BYTES = R128_O_BYTES + 3 * R128_ROWS * 4;  // + m, l, lo per row (fp32)
 constexpr int R128_BT_WIN = 1024;             // block-table entries held in LDS per sub-piece
 constexpr int R128_QREG = 28;                 // Q^T k-steps (of 16 dims) kept in registers; the rest in LDS
 constexpr int R128_QLDS = 36 - R128_QREG;
@@ -982,29 +984,44 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
       }
       WAIT_VMCNT(0);
     }
-    // partial slot: O^T in the accumulator layout [dv/32][row][h][i] (the 16
-    // values a lane holds per 32x32 block are contiguous: 4 x 16-byte
-    // stores), then per row m, the fp32 and the bf16 sums of P
+    // partial slot: O^T / (the row's bf16 sum of P) in fp16, in the
+    // accumulator layout [dv/32][row][h][i] (the 16 values a lane holds per
+    // 32x32 block are contiguous: 2 x 16-byte stores), then per row m, the
+    // fp32 and the bf16 sums of P.  The accumulator columns span all 128
+    // rows, whose sums the owning waves publish through LDS.
     const float l_row = st.l_part + __shfl_xor(st.l_part, 32, 64);
     const float lo_row = st.l_out + __shfl_xor(st.l_out, 32, 64);
-    float* ps = a.partials + piece_slot(a, bund, bb, rt) * (R128_ROWS * D_V + 3 * R128_ROWS);
+    uint8_t* slot = reinterpret_cast<uint8_t*>(a.partials) + piece_slot(a, bund, bb, rt) * R128_SLOT_BYTES;
+    float* pm = reinterpret_cast<float*>(slot + R128_O_BYTES);
     const int r = lane & 31, h = lane >> 5;
+    __syncthreads();  // every wave is past its last read of alpha_lds
+    if (h == 0) alpha_lds[32 * wave + r] = lo_row;
+    __syncthreads();
+    float inv[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const float lo = alpha_lds[32 * rb + r];
+      inv[rb] = lo > 0.f ? 1.f / lo : 0.f;
+    }
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
-        float* pl = ps + ((4 * wave + d) * R128_ROWS + 32 * rb + r) * 32 + h * 16;
+        _Float16* pl = reinterpret_cast<_Float16*>(slot) + ((4 * wave + d) * R128_ROWS + 32 * rb + r) * 32 + h * 16;
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          *reinterpret_cast<f32x4*>(pl + 4 * c) = f32x4{st.o[4 * d + rb][4 * c], st.o[4 * d + rb][4 * c + 1],
-                                                        st.o[4 * d + rb][4 * c + 2], st.o[4 * d + rb][4 * c + 3]};
+        for (int c = 0; c < 2; ++c) {
+          f16x8 v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (_Float16)(st.o[4 * d + rb][8 * c + e] * inv[rb]);
+          *reinterpret_cast<f16x8*>(pl + 8 * c) = v;
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     if (h == 0) {
       const int prow = wave * 32 + r;
-      ps[R128_ROWS * D_V + prow] = st.m_ref;
-      ps[R128_ROWS * D_V + R128_ROWS + prow] = l_row;
-      ps[R128_ROWS * D_V + 2 * R128_ROWS + prow] = lo_row;
+      pm[prow] = st.m_ref;
+      pm[R128_ROWS + prow] = l_row;
+      pm[2 * R128_ROWS + prow] = lo_row;
     }
   });
 }
@@ -1026,11 +1043,15 @@ __device__ __forceinline__ int slot_index(int row, int dv) {
   return ((dv >> 5) * ROWS + row) * 32 + ((r32 >> 2) & 1) * 16 + (r32 >> 3) * 4 + (r32 & 3);
 }
 
+// M16 slots hold fp32 O (unnormalised); R128 slots hold fp16 O divided by
+// the row's bf16 sum of P, so its weight in the merge carries that sum.
 template <int ROWS>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   constexpr int SLICE = 64;                       // output columns per workgroup
   constexpr int PER = ROWS * SLICE / 256;         // outputs per thread
-  constexpr int SLOT = ROWS * D_V + 3 * ROWS;
+  constexpr bool F16 = ROWS == R128_ROWS;
+  constexpr int64_t SLOT_BYTES = F16 ? R128_SLOT_BYTES : (ROWS * D_V + 3 * ROWS) * 4;
+  constexpr int O_BYTES = F16 ? R128_O_BYTES : ROWS * D_V * 4;
   const int grp = blockIdx.x >> 3, slice = blockIdx.x & 7;
   const int b = grp / a.n_rt, rt = grp - b * a.n_rt;
   const int row = threadIdx.x % ROWS;
@@ -1069,12 +1090,15 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 #pragma unroll
       for (int c = 0; c < PER; ++c) v[t][c] = 0.f;
       if (j <= j1 && range_nonempty(j, T, a.nbund)) {
-        const float* ps = a.partials + ((int64_t)j * a.n_rt + grp) * SLOT;
-        mw[t] = ps[ROWS * D_V + row];
-        lw[t] = ps[ROWS * D_V + ROWS + row];
-        low[t] = ps[ROWS * D_V + 2 * ROWS + row];
+        const uint8_t* slot = reinterpret_cast<const uint8_t*>(a.partials) + ((int64_t)j * a.n_rt + grp) * SLOT_BYTES;
+        const float* pm = reinterpret_cast<const float*>(slot + O_BYTES);
+        mw[t] = pm[row];
+        lw[t] = pm[ROWS + row];
+        low[t] = pm[2 * ROWS + row];
 #pragma unroll
-        for (int c = 0; c < PER; ++c) v[t][c] = ps[slot_index<ROWS>(row, col0 + c)];
+        for (int c = 0; c < PER; ++c)
+          v[t][c] = F16 ? (float)reinterpret_cast<const _Float16*>(slot)[slot_index<ROWS>(row, col0 + c)]
+                        : reinterpret_cast<const float*>(slot)[slot_index<ROWS>(row, col0 + c)];
       }
     }
     float Mb = M;
@@ -1091,8 +1115,9 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
       const float f = (mw[t] == NEG_INF) ? 0.f : fast_exp2(mw[t] - Mb);
       L += f * lw[t];
       Lo += f * low[t];
+      const float fv = F16 ? f * low[t] : f;
 #pragma unroll
-      for (int c = 0; c < PER; ++c) acc[c] += f * v[t][c];
+      for (int c = 0; c < PER; ++c) acc[c] += fv * v[t][c];
     }
     M = Mb;
   }
@@ -1164,7 +1189,8 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool allow_r12
   if (nbund < 1) nbund = 1;
   p.nbund = (int)nbund;
   p.G = p.nbund * p.n_rt;
-  const size_t slot = (size_t)(p.rows_tile * D_V + 3 * p.rows_tile) * sizeof(float);
+  const size_t slot = p.rows_tile == R128_ROWS ? (size_t)R128_SLOT_BYTES
+                                               : (size_t)(p.rows_tile * D_V + 3 * p.rows_tile) * sizeof(float);
   p.prefix_off = 0;
   p.partial_off = align_up((size_t)(B + 1) * sizeof(int64_t));
   p.bytes = p.partial_off + align_up(((size_t)p.G + (size_t)B * p.n_rt) * slot);

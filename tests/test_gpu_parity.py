@@ -61,6 +61,9 @@ CASES = [
     # and far more pieces per workgroup range than one batch of segments holds
     spec("many_tiny_requests", 300, 16, 1, True, [(7 * i) % 5 for i in range(300)], global_is_null=True),
     spec("many_tiny_requests_h128", 40, 128, 2, True, [(3 * i) % 4 for i in range(40)], W=2),
+    # one request over every bundle: dozens of partial slots per group, merged
+    # by the combine several batches at a time
+    spec("one_request_all_bundles_h128", 1, 128, 4, True, [12000], global_is_null=True),
 ]
 
 
