@@ -26,24 +26,39 @@ struct SlotArgs {
   int64_t* slots;
 };
 
+// floor(x / d) for x >= 0, d >= 1.  Below 2^52 one correctly rounded double
+// division gives it exactly: x/d is either an integer (then representable) or
+// at least 1/d from the next integer, while the rounded quotient is within
+// 2^-53 * x/d of it, and x < 2^53 keeps that below 1/d.  Larger values take
+// the 64-bit integer division (a long instruction sequence on the GPU).
+__device__ __forceinline__ int64_t floordiv(int64_t x, int64_t d) {
+  constexpr int64_t kExact = int64_t(1) << 52;
+  if (x < kExact && d < kExact) return (int64_t)((double)x / (double)d);
+  return x / d;
+}
+
 __global__ __launch_bounds__(256) void slot_kernel(SlotArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= a.total) return;
-  const int64_t b = idx / a.n;
+  const int64_t b = floordiv(idx, a.n);
   const int64_t i = idx - b * a.n;
   const int64_t pos = a.pos[idx];
   int64_t slot = MLA_PAD_SLOT_ID;
   const bool valid = (a.num_valid == nullptr || i < (int64_t)a.num_valid[b]) && pos >= 0;
   if (valid) {
     const int64_t span = a.bs * a.W;
-    const int64_t v = pos / span;
+    const int64_t v = floordiv(pos, span);
     const int64_t off = pos - v * span;
     if (v < a.max_blocks) {
       const int64_t base = (int64_t)a.bt[b * a.max_blocks + v] * a.bs;
       if (a.W == 1) {
         slot = base + off;
-      } else if ((off / a.I) % a.W == a.rank) {
-        slot = base + (off / (a.I * a.W)) * a.I + off % a.I;
+      } else {
+        // segment of I positions inside the virtual block, its owner, and
+        // the rounds of W segments before it
+        const int64_t seg = floordiv(off, a.I);
+        const int64_t round = floordiv(seg, a.W);
+        if (seg - round * a.W == a.rank) slot = base + round * a.I + (off - seg * a.I);
       }
     }
   }

@@ -1076,6 +1076,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   // most NMAX slots this is the plain two-pass merge (weights relative to
   // the overall maximum); later batches rescale the running sums.
   constexpr int NMAX = ROWS == M16_ROWS ? 8 : 4;
+  const bool some_empty = T < a.nbund;  // with T >= nbund units every range holds one
   float M = NEG_INF, L = 0.f, Lo = 0.f;
   float acc[PER];
 #pragma unroll
@@ -1089,7 +1090,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
       lw[t] = low[t] = 0.f;
 #pragma unroll
       for (int c = 0; c < PER; ++c) v[t][c] = 0.f;
-      if (j <= j1 && range_nonempty(j, T, a.nbund)) {
+      if (j <= j1 && (!some_empty || range_nonempty(j, T, a.nbund))) {
         const uint8_t* slot = reinterpret_cast<const uint8_t*>(a.partials) + ((int64_t)j * a.n_rt + grp) * SLOT_BYTES;
         const float* pm = reinterpret_cast<const float*>(slot + O_BYTES);
         mw[t] = pm[row];

@@ -264,6 +264,24 @@ def test_slots_bit_exact_against_oracle(W, I, bs):
             np.testing.assert_array_equal(got.cpu().numpy(), exp)
 
 
+@pytest.mark.parametrize("bs,W,I", [(1 << 20, 1 << 10, 1), (1 << 20, 6, 1 << 18), (1 << 30, 1 << 23, 1)])
+def test_slots_exact_at_block_and_segment_boundaries(bs, W, I):
+    # positions on and next to virtual-block and segment edges, below 2^52
+    # (quotients through one double division) and, with a 2^53-position
+    # virtual block, above it (64-bit integer division); checked for the
+    # rank that owns each position and for the first and last rank
+    span = bs * W
+    edges = [0, 1, I - 1, I, I + 1, span - 1, span, span + 1, 2 * span + 5 * I, 2 * span + 5 * I - 1, 4 * span - 1,
+             (1 << 52) - 1, 1 << 52, (1 << 52) + 1, (1 << 53) - 1, 1 << 53, (1 << 53) + 1]
+    pos = np.array([sorted({p for p in edges if 0 <= p < 4 * span})], dtype=np.int64)
+    bt = np.array([[11, 3, 1 << 20, 9]], dtype=np.int32)
+    ranks = sorted({(int(p) % span) // I % W for p in pos[0]} | {0, W - 1})
+    for rank in ranks:
+        got = mla.cp_local_slot(i64_dev(pos), i32_dev(bt), bs, W, rank, cp_interleave=I).cpu().numpy()
+        exp = np.asarray(oracle.cp_local_slot(pos, bt, bs, W, rank, I, None), dtype=np.int64)
+        assert np.array_equal(got, exp), (rank, pos, got, exp)
+
+
 def test_slots_large_positions_int64():
     bt = np.array([[2_000_000_000, 7]], dtype=np.int32)
     pos = np.array([[0, 1, 2, 3, 130, 131]], dtype=np.int64)
