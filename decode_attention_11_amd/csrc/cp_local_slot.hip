@@ -13,8 +13,11 @@
 #include <cstdint>
 
 #include "mla_decode.h"
+#include "mla_device.h"
 
 namespace {
+
+using mla::floordiv;
 
 struct SlotArgs {
   const int64_t* pos;
@@ -25,17 +28,6 @@ struct SlotArgs {
   int64_t bs, W, rank, I;
   int64_t* slots;
 };
-
-// floor(x / d) for x >= 0, d >= 1.  Below 2^52 one correctly rounded double
-// division gives it exactly: x/d is either an integer (then representable) or
-// at least 1/d from the next integer, while the rounded quotient is within
-// 2^-53 * x/d of it, and x < 2^53 keeps that below 1/d.  Larger values take
-// the 64-bit integer division (a long instruction sequence on the GPU).
-__device__ __forceinline__ int64_t floordiv(int64_t x, int64_t d) {
-  constexpr int64_t kExact = int64_t(1) << 52;
-  if (x < kExact && d < kExact) return (int64_t)((double)x / (double)d);
-  return x / d;
-}
 
 __global__ __launch_bounds__(256) void slot_kernel(SlotArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;

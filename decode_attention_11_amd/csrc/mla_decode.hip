@@ -141,7 +141,7 @@ struct PlanLds {
   int64_t red[NT / 64];
   int64_t excl[NT];
   int nb[NT], seq[NT], tot[NT];
-  int first_last[2];
+  int first_last[2][NT / 64];  // per wave: the first and last overlapping request (or sentinels)
 };
 
 // The piece of request bb (unit offset pb, nbb keys) inside [u0, u1): the
@@ -178,7 +178,7 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int j, int r
     request_info(a, base + tid, nb2, seq2, tot2);
     T += block_sum_i64<NT>(request_units(a, nb2), pl.red);
   }
-  const int64_t u0 = (int64_t)j * T / a.nbund, u1 = (int64_t)(j + 1) * T / a.nbund;
+  const int64_t u0 = floordiv((int64_t)j * T, a.nbund), u1 = floordiv((int64_t)(j + 1) * T, a.nbund);
 
   int64_t carry = 0;
   for (int base = 0; base < a.B; base += NT) {
@@ -199,14 +199,21 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int j, int r
     pl.nb[tid] = nb;
     pl.seq[tid] = seq;
     pl.tot[tid] = tot;
-    if (tid == 0) { pl.first_last[0] = 0x7fffffff; pl.first_last[1] = -1; }
-    __syncthreads();
-    if (x > 0 && excl < u1 && incl > u0) {
-      atomicMin(&pl.first_last[0], tid);
-      atomicMax(&pl.first_last[1], tid);
+    // the requests overlapping the range are contiguous: each wave finds its
+    // first and last one by ballot, one barrier publishes them
+    const uint64_t hit = __ballot(x > 0 && excl < u1 && incl > u0);
+    const int wv = tid >> 6;
+    if ((tid & 63) == 0) {
+      pl.first_last[0][wv] = hit ? 64 * wv + __builtin_ctzll(hit) : 0x7fffffff;
+      pl.first_last[1][wv] = hit ? 64 * wv + 63 - __builtin_clzll(hit) : -1;
     }
     __syncthreads();
-    const int first = pl.first_last[0], last = pl.first_last[1];
+    int first = 0x7fffffff, last = -1;
+#pragma unroll
+    for (int v = 0; v < NT / 64; ++v) {
+      first = min(first, pl.first_last[0][v]);
+      last = max(last, pl.first_last[1][v]);
+    }
     carry += chunk_total;
 
     for (int i = first; i <= last; ++i)

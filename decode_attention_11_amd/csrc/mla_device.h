@@ -24,6 +24,17 @@ constexpr float LN2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// floor(x / d) for x >= 0, d >= 1.  Below 2^52 one correctly rounded double
+// division gives it exactly: x/d is either an integer (then representable) or
+// at least 1/d from the next integer, while the rounded quotient is within
+// 2^-53 * x/d of it, and x < 2^53 keeps that below 1/d.  Larger values take
+// the 64-bit integer division (a long instruction sequence on the GPU).
+__device__ __forceinline__ int64_t floordiv(int64_t x, int64_t d) {
+  constexpr int64_t kExact = int64_t(1) << 52;
+  if (x < kExact && d < kExact) return (int64_t)((double)x / (double)d);
+  return x / d;
+}
+
 // Two floats to packed bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ bf16x2 to_bf16x2(float a, float b) {
   f32x2 v = {a, b};
@@ -87,13 +98,13 @@ __device__ __forceinline__ int row_bound(int seq, int tot, int q_len, int j, int
 // Index of the balanced work range that holds unit u when T units are cut
 // into G ranges [floor(w*T/G), floor((w+1)*T/G)).
 __device__ __forceinline__ int range_owner(int64_t u, int64_t T, int G) {
-  return (int)(((u + 1) * (int64_t)G - 1) / T);
+  return (int)floordiv((u + 1) * (int64_t)G - 1, T);
 }
 
 // Whether range w holds any unit: with fewer units than ranges some are empty
 // (and can lie between the owners of two units).
 __device__ __forceinline__ bool range_nonempty(int w, int64_t T, int G) {
-  return (int64_t)w * T / G < (int64_t)(w + 1) * T / G;
+  return floordiv((int64_t)w * T, G) < floordiv((int64_t)(w + 1) * T, G);
 }
 
 }  // namespace mla
