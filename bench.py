@@ -100,6 +100,41 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
+# ------------------------------------------------------------------ achievable peaks
+def measured_peaks(torch, hip, stream, dev, reps=5):
+    """Achievable HBM and bf16 matrix rates on this GPU, measured with torch
+    (not this library): a 1 GiB device copy (bytes read + written) and an
+    8192^3 bf16 GEMM (hipBLASLt).  Reported beside the published peaks."""
+    out = {}
+    x = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    a_, b_ = hip.event(), hip.event()
+    y.copy_(x)
+    torch.cuda.synchronize()
+    hip.record(a_, stream)
+    for _ in range(reps):
+        y.copy_(x)
+    hip.record(b_, stream)
+    out["hbm_copy_GBps"] = round((2 << 30) * reps / (hip.elapsed_ms(a_, b_) * 1e-3) / 1e9, 1)
+    del x, y
+    n = 8192
+    g = torch.Generator(device=dev).manual_seed(0)
+    m1 = torch.randn((n, n), dtype=torch.bfloat16, device=dev, generator=g).contiguous()
+    m2 = torch.randn((n, n), dtype=torch.bfloat16, device=dev, generator=g).contiguous()
+    torch.matmul(m1, m2)
+    torch.cuda.synchronize()
+    hip.record(a_, stream)
+    for _ in range(reps):
+        torch.matmul(m1, m2)
+    hip.record(b_, stream)
+    out["bf16_gemm_TFLOPs"] = round(2.0 * n ** 3 * reps / (hip.elapsed_ms(a_, b_) * 1e-3) / 1e12, 1)
+    del m1, m2
+    hip.destroy(a_)
+    hip.destroy(b_)
+    torch.cuda.synchronize()
+    return out
+
+
 # ------------------------------------------------------------------ CPU baseline (oracle)
 def cpu_baseline(wl, ranks, unit, budget_s=20.0):
     import numpy as np
@@ -272,6 +307,10 @@ def main():
         if t.get("source_hash") == source_hash():
             traffic = t.get("bytes_per_launch")
     roof["traffic"] = traffic
+    log("achievable peaks: 1 GiB copy, 8192^3 bf16 GEMM (torch)")
+    peaks = measured_peaks(torch, hip, stream, dev)
+    meas = peaks["hbm_copy_GBps"] if mem_bound else peaks["bf16_gemm_TFLOPs"]
+    roof["frac_of_measured_peak"] = round(roof["achieved"] / meas, 4) if meas > 0 else None
 
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
@@ -282,7 +321,7 @@ def main():
         "tflops": round(tflops, 3), "kv_gbps": round(kv_gbps, 1),
         "alg_bytes_per_step": int(step_alg_bytes), "flops_per_step": int(step_flops),
         "attention_kernel_ms": round(avg_attn_ms, 5), "source_hash": source_hash(),
-        "roofline": roof,
+        "roofline": roof, "measured_peaks": peaks,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a bounded sample")
