@@ -135,6 +135,43 @@ def measured_peaks(torch, hip, stream, dev, reps=5):
     return out
 
 
+# ------------------------------------------------------------------ KV write
+def kv_write_rates(torch, mla, hip, stream, dev, step_job, reps=20, bulk_rows=1 << 18):
+    """Times mla_kv_write twice: storing the step's new-token rows at their
+    slots (the rows already there, so the cache is unchanged), and a bulk
+    scatter of bulk_rows random rows to a permutation of a scratch cache's
+    rows (bytes = rows x 1152 read + rows x 1152 written + 8 per slot)."""
+    rows, slots, cache = step_job
+    a_, b_ = hip.event(), hip.event()
+    mla.kv_write(rows, slots, cache)
+    torch.cuda.synchronize()
+    step_us = 0.0
+    for _ in range(reps):  # one launch between each event pair: the host enqueues slower than it runs
+        hip.record(a_, stream)
+        mla.kv_write(rows, slots, cache)
+        hip.record(b_, stream)
+        step_us += hip.elapsed_ms(a_, b_) * 1e3 / reps
+    g = torch.Generator(device=dev).manual_seed(1)
+    big_rows = torch.randint(-32768, 32767, (bulk_rows, 576), dtype=torch.int16, device=dev,
+                             generator=g).view(torch.bfloat16)
+    big_cache = torch.empty((bulk_rows // 64, 64, 576), dtype=torch.bfloat16, device=dev)
+    big_slots = torch.randperm(bulk_rows, device=dev, generator=g)
+    mla.kv_write(big_rows, big_slots, big_cache)
+    torch.cuda.synchronize()
+    hip.record(a_, stream)
+    for _ in range(5):
+        mla.kv_write(big_rows, big_slots, big_cache)
+    hip.record(b_, stream)
+    bulk_us = hip.elapsed_ms(a_, b_) * 1e3 / 5
+    nbytes = bulk_rows * (2 * 1152 + 8)
+    hip.destroy(a_)
+    hip.destroy(b_)
+    del big_rows, big_cache, big_slots
+    gbps = nbytes / (bulk_us * 1e-6) / 1e9
+    return {"step_rows": int(rows.numel() // 576), "step_us": round(step_us, 2), "bulk_rows": bulk_rows,
+            "bulk_us": round(bulk_us, 1), "bulk_GBps": round(gbps, 1), "bulk_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
 # ------------------------------------------------------------------ CPU baseline (oracle)
 def cpu_baseline(wl, ranks, unit, budget_s=20.0):
     import numpy as np
@@ -307,6 +344,18 @@ def main():
         if t.get("source_hash") == source_hash():
             traffic = t.get("bytes_per_launch")
     roof["traffic"] = traffic
+    log("kv write: the step's new-token rows, and a bulk scatter")
+    r0 = ranks[0]
+    pos0, nv0 = slot_jobs[0]
+    slots0 = mla.cp_local_slot(pos0, bt, s.block_size, s.W, r0, nv0)
+    pos_np = pos0.cpu().numpy()
+    rows_np = np.zeros(pos_np.shape + (576,), dtype=np.uint16)  # rows of positions other ranks own stay zero
+    for b in range(s.B):
+        for i, p in enumerate(pos_np[b]):
+            if p >= 0 and p % s.W == r0 and p // s.W < len(wl.shards[r0][b]):
+                rows_np[b, i] = wl.shards[r0][b][p // s.W]
+    rows0 = bf16(rows_np)
+    kvw = kv_write_rates(torch, mla, hip, stream, dev, (rows0, slots0, pools[r0][0]))
     log("achievable peaks: 1 GiB copy, 8192^3 bf16 GEMM (torch)")
     peaks = measured_peaks(torch, hip, stream, dev)
     meas = peaks["hbm_copy_GBps"] if mem_bound else peaks["bf16_gemm_TFLOPs"]
@@ -321,7 +370,7 @@ def main():
         "tflops": round(tflops, 3), "kv_gbps": round(kv_gbps, 1),
         "alg_bytes_per_step": int(step_alg_bytes), "flops_per_step": int(step_flops),
         "attention_kernel_ms": round(avg_attn_ms, 5), "source_hash": source_hash(),
-        "roofline": roof, "measured_peaks": peaks,
+        "roofline": roof, "measured_peaks": peaks, "kv_write": kvw,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a bounded sample")

@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "D_QK", "D_V", "PAD_SLOT_ID", "LSE_BASE_E", "LSE_BASE_2", "MLAError",
     "library_path", "load_library", "exported_symbols",
-    "mla_decode", "mla_decode_workspace_size", "mla_merge_lse", "cp_local_slot",
+    "mla_decode", "mla_decode_workspace_size", "mla_merge_lse", "cp_local_slot", "kv_write",
     "profile_attention_events",
 ]
 
@@ -48,6 +48,7 @@ _SIGNATURES = [
     ("mla_merge_lse", _I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
     ("cp_local_slot", _I, [_P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, _P]),
     ("mla_profile_attention_events", _I, [_P, _P]),
+    ("mla_kv_write", _I, [_P, _P, ctypes.c_int64, _P, _I, _I, _P]),
 ]
 
 
@@ -238,3 +239,22 @@ def cp_local_slot(positions: torch.Tensor, block_table: torch.Tensor, block_size
                              int(block_size), int(cp_world), int(cp_rank), int(cp_interleave),
                              out.data_ptr(), _stream(positions.device)))
     return out
+
+
+def kv_write(kv_new: torch.Tensor, slots: torch.Tensor, kv_cache: torch.Tensor) -> torch.Tensor:
+    """Store new KV rows [..., 576] bf16 at their slots [...] int64 in kv_cache
+    [num_blocks, block_size, 576] bf16 (in place); pad and out-of-range slots
+    write nothing.  Returns kv_cache."""
+    lib = load_library()
+    _need(kv_new, "kv_new", torch.bfloat16)
+    _need(slots, "slots", torch.int64)
+    _need(kv_cache, "kv_cache", torch.bfloat16, 3)
+    if kv_new.shape[-1] != D_QK or kv_cache.shape[2] != D_QK:
+        raise ValueError(f"rows must be {D_QK} wide")
+    n = kv_new.numel() // D_QK
+    if slots.numel() != n or tuple(slots.shape) != tuple(kv_new.shape[:-1]):
+        raise ValueError("slots must have one entry per row of kv_new")
+    _check(lib.mla_kv_write(kv_new.data_ptr(), slots.data_ptr(), int(n), kv_cache.data_ptr(),
+                            int(kv_cache.shape[0]), int(kv_cache.shape[1]), _stream(kv_cache.device)))
+    return kv_cache
+

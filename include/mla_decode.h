@@ -172,6 +172,28 @@ int cp_local_slot(const int64_t* positions, const int32_t* num_valid, int B, int
                   int cp_world, int cp_rank, int cp_interleave, int64_t* slots,
                   hipStream_t stream);
 
+/*
+ * Store new latent KV rows in a rank's paged cache at their rank-local slots
+ * (PR #52188 page, key source snippets, cp_local_slot: a rank writes the
+ * draft's KV only at the slots it owns and gets the pad slot for the others,
+ * so that it never overwrites another rank's rows; implementation
+ * breakdown: the DFlash input preparation applies the slot mapping to the
+ * draft's context and query KV).  For every i < n_rows:
+ *   if 0 <= slots[i] < num_blocks*block_size:
+ *     kv_cache[slots[i] / block_size][slots[i] % block_size][:] = kv_new[i][:]
+ *   otherwise (MLA_PAD_SLOT_ID, any negative slot, a slot past the cache)
+ *   nothing is written for row i.
+ * kv_new: [n_rows, 576] bf16; slots: [n_rows] int64 (as cp_local_slot
+ * returns them); kv_cache: [num_blocks, block_size, 576] bf16, updated in
+ * place.  If two rows carry the same slot, one of them is stored, which one
+ * is unspecified (cp_local_slot never maps two positions to one slot).
+ * Errors: MLA_ERR_INVALID_ARG for null pointers (when n_rows > 0),
+ * kv_new or kv_cache not 16-byte aligned, n_rows < 0, num_blocks < 1 or
+ * block_size < 1; MLA_ERR_HIP if the launch fails.
+ */
+int mla_kv_write(const void* kv_new, const int64_t* slots, int64_t n_rows, void* kv_cache,
+                 int num_blocks, int block_size, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

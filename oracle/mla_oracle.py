@@ -224,3 +224,31 @@ def cp_local_slot(positions: np.ndarray, block_table: np.ndarray, block_size: in
             local = (off // (interleave * W)) * interleave + off % interleave
             out[b, i] = blk * block_size + local
     return out
+
+
+def kv_write(cache_bits: np.ndarray, rows_bits: np.ndarray, slots: np.ndarray) -> np.ndarray:
+    """A copy of the paged cache with each new KV row stored at its slot.
+
+    PR #52188 page, key source snippets (cp_local_slot) and risks: the draft's
+    KV is written at the rank-local slot of its position, and a position the
+    rank does not own gets the pad slot so that nothing is written for it
+    (writing there would overwrite another rank's data).  Slot s names row
+    s % block_size of block s // block_size of the cache.  Reading: a slot
+    that is negative (the pad slot) or past the cache's rows writes nothing.
+
+    cache_bits [num_blocks, block_size, 576] and rows_bits [n, 576] are bf16
+    bit patterns; slots [n] int64.  Rows are stored one after another in
+    index order, so of several rows with one slot the last one stays (the
+    GPU kernel leaves that case unspecified; cp_local_slot never gives two
+    positions one slot).
+    """
+    out = np.array(cache_bits, copy=True)
+    num_blocks, block_size = out.shape[0], out.shape[1]
+    rows_bits = np.asarray(rows_bits)
+    for i, s in enumerate(np.asarray(slots).reshape(-1)):
+        s = int(s)
+        if s < 0 or s >= num_blocks * block_size:
+            continue
+        out[s // block_size, s % block_size, :] = rows_bits[i]
+    return out
+

@@ -21,7 +21,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["mla_status_string", "mla_decode_workspace_size", "mla_decode",
-                                           "mla_merge_lse", "cp_local_slot", "mla_profile_attention_events"])
+                                           "mla_merge_lse", "cp_local_slot", "mla_profile_attention_events",
+                                           "mla_kv_write"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -116,3 +117,21 @@ def test_profile_events_need_both_or_neither():
     assert lib.mla_profile_attention_events(1, None) == 1
     assert lib.mla_profile_attention_events(None, 1) == 1
     assert lib.mla_profile_attention_events(None, None) == 0
+
+
+def _kv_write(**kw):
+    lib = mla.load_library()
+    a = dict(rows=256, slots=256, n=4, cache=256, nblk=4, bs=64, stream=None)
+    a.update(kw)
+    return lib.mla_kv_write(a["rows"], a["slots"], a["n"], a["cache"], a["nblk"], a["bs"], a["stream"])
+
+
+@pytest.mark.parametrize("bad", [dict(n=-1), dict(nblk=0), dict(bs=0), dict(rows=None), dict(slots=None),
+                                 dict(cache=None), dict(rows=258), dict(cache=264)])
+def test_kv_write_rejects_bad_arguments(bad):
+    assert _kv_write(**bad) == 1
+
+
+def test_kv_write_empty_is_a_noop():
+    assert _kv_write(n=0, rows=None, slots=None, cache=None) == 0
+

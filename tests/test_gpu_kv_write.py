@@ -1,0 +1,97 @@
+"""GPU parity of the paged KV write (mla_kv_write) against the oracle, and a
+write-then-attend pass: the new tokens' KV rows are stored through
+cp_local_slot's slots, then every rank decodes and the merged result is
+compared with the oracle's attention over the contiguous global KV."""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_11_amd as mla
+import oracle
+import workloads as WL
+from tests.gpu_util import Uploaded, compare, say, bf16_dev, i32_dev, i64_dev, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("n,P,bs", [(1, 2, 64), (300, 16, 64), (4099, 80, 64), (77, 9, 16), (50, 200, 1)])
+def test_kv_write_matches_oracle(n, P, bs):
+    rng = np.random.default_rng(n * 7 + bs)
+    cache = rng.integers(0, 1 << 16, size=(P, bs, oracle.D_QK), dtype=np.uint16)
+    rows = rng.integers(0, 1 << 16, size=(n, oracle.D_QK), dtype=np.uint16)
+    # distinct in-range slots for most rows; pad, negative and past-the-end ones mixed in
+    assert n <= P * bs
+    slots = rng.permutation(P * bs)[:n].astype(np.int64)
+    kinds = rng.integers(0, 10, n)
+    slots = np.where(kinds == 0, oracle.PAD_SLOT_ID, slots)
+    slots = np.where(kinds == 1, -(1 << 40), slots)
+    slots = np.where(kinds == 2, P * bs + rng.integers(0, 1 << 20, n), slots)
+    slots = slots.astype(np.int64)
+    exp = oracle.kv_write(cache, rows, slots)
+    c = bf16_dev(cache)
+    say(f"kv_write n={n} P={P} bs={bs}")
+    mla.kv_write(bf16_dev(rows), i64_dev(slots), c)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(c), exp)
+
+
+@pytest.mark.parametrize("H,Q,W,causal", [(16, 4, 2, True), (128, 4, 4, True), (16, 16, 2, False)])
+def test_write_new_tokens_then_attend(H, Q, W, causal):
+    spec = WL.Spec(name=f"write_then_attend_h{H}_w{W}", B=3, H=H, Q=Q, causal=causal, seed=808 + H + W,
+                   lengths=[Q + 1, 700, 2500], W=W, ranks=tuple(range(W)))
+    wl = WL.build(spec)
+    up = Uploaded(wl)
+    bt = i32_dev(wl.block_table)
+    bs = spec.block_size
+    new_pos = (wl.tot[:, None] - Q + np.arange(Q)[None, :]).astype(np.int64)  # the step's new tokens
+    new_rows = np.stack([wl.global_rows(b, new_pos[b]) for b in range(spec.B)])  # [B, Q, 576]
+    for r in range(W):
+        # the cache before the step: the new tokens' rows hold garbage
+        pool = wl.pools[r].copy()
+        for b in range(spec.B):
+            for p in new_pos[b]:
+                if p % W == r:
+                    t = int(p) // W
+                    pool[wl.block_table[b, t // bs], t % bs] = 0x7FC0
+        up.pools[r] = bf16_dev(pool)
+        say(f"{spec.name} rank {r}: slots and write of {spec.B}x{Q} new rows")
+        slots = mla.cp_local_slot(i64_dev(new_pos), bt, bs, W, r)
+        mla.kv_write(bf16_dev(new_rows), slots, up.pools[r])
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(up.pools[r]), wl.pools[r]), f"rank {r} pool after the write"
+    outs, lses = [], []
+    for r in range(W):
+        o, l = up.run(r, "e")
+        outs.append(o)
+        lses.append(l)
+    mo, ml = mla.mla_merge_lse(outs, lses, "e")
+    torch.cuda.synchronize()
+    ro, rl = oracle.mla_decode(wl.q_bits, wl.global_rows, wl.tot.astype(np.int32), wl.tot, 1, 0, causal,
+                               spec.scale, "e")
+    compare(mo, ml, ro, rl, f"{spec.name} merged after the write")
+
+
+def test_rejected_context_suffix_is_not_written():
+    # the draft's context window: its rejected suffix maps to the pad slot,
+    # so those rows leave the cache untouched on every rank
+    spec = WL.Spec(name="draft_ctx_write", B=4, H=16, Q=16, causal=False, seed=919, lengths=[200, 333, 64, 1000],
+                   W=2, ranks=(0, 1))
+    wl = WL.build(spec)
+    si = WL.draft_slot_inputs(wl)
+    pos, nv = si["ctx_positions"], si["ctx_num_valid"]
+    rng = np.random.default_rng(3)
+    rows = rng.integers(0, 1 << 16, size=pos.shape + (oracle.D_QK,), dtype=np.uint16)
+    bt = i32_dev(wl.block_table)
+    for r in range(2):
+        slots = mla.cp_local_slot(i64_dev(pos), bt, spec.block_size, 2, r, i32_dev(nv))
+        exp_slots = oracle.cp_local_slot(pos, wl.block_table, spec.block_size, 2, r, 1, nv)
+        assert np.array_equal(slots.cpu().numpy(), exp_slots)
+        c = bf16_dev(wl.pools[r])
+        mla.kv_write(bf16_dev(rows), slots, c)
+        torch.cuda.synchronize()
+        exp = oracle.kv_write(wl.pools[r], rows.reshape(-1, oracle.D_QK), np.asarray(exp_slots).reshape(-1))
+        assert np.array_equal(bits(c), exp), f"rank {r}"

@@ -331,6 +331,50 @@ def test_paged_pool_holds_the_shards():
                 np.testing.assert_array_equal(wl.pools[r][wl.block_table[b, t // bs], t % bs], wl.shards[r][b][t])
 
 
+# ---------------------------------------------------------------- KV write
+
+def test_kv_write_rebuilds_every_rank_pool_from_the_global_kv():
+    """Writing each global position's row at the slot cp_local_slot gives it,
+    for every rank, rebuilds the rank pools the generator laid out by its own
+    paging code (the rows requests use; the others keep their filler)."""
+    wl = tiny(B=3, H=2, Q=2, W=3, causal=True, lengths=(1, 70, 131), seed=63)
+    bs, W = wl.spec.block_size, wl.spec.W
+    for r in range(W):
+        cache = wl.pools[r].copy()
+        used = np.zeros(cache.shape[:2], dtype=bool)
+        for b in range(wl.spec.B):
+            n = int(wl.seq_lens[r][b])
+            for t in range(n):
+                used[wl.block_table[b, t // bs], t % bs] = True
+        cache[used] = 0xFFFF  # forget what the generator put there
+        for b in range(wl.spec.B):
+            L = int(wl.tot[b])
+            pos = np.arange(L, dtype=np.int64)[None, :]
+            slots = oracle.cp_local_slot(pos, wl.block_table[b:b + 1], bs, W, r)
+            cache = oracle.kv_write(cache, wl.global_kv(b), slots[0])
+        np.testing.assert_array_equal(cache, wl.pools[r])
+
+
+def test_kv_write_scatter_invariants():
+    """Distinct in-range slots: the cache row at each slot is the row written
+    there and every other row is unchanged; pad, negative and past-the-end
+    slots write nothing; of two rows with one slot the later one stays."""
+    rng = np.random.default_rng(5)
+    P, bs, n = 5, 4, 9
+    cache = rng.integers(0, 1 << 16, size=(P, bs, oracle.D_QK), dtype=np.uint16)
+    rows = rng.integers(0, 1 << 16, size=(n, oracle.D_QK), dtype=np.uint16)
+    slots = np.array([7, oracle.PAD_SLOT_ID, 0, 19, -5, 20, 1 << 40, 3, 12], dtype=np.int64)
+    got = oracle.kv_write(cache, rows, slots)
+    expect = cache.copy().reshape(P * bs, oracle.D_QK)
+    for i, s in enumerate(slots):
+        if 0 <= s < P * bs:
+            expect[s] = rows[i]
+    np.testing.assert_array_equal(got.reshape(P * bs, -1), expect)
+    assert np.array_equal(cache, oracle.kv_write(cache, rows[:0], slots[:0]))  # nothing to write
+    dup = oracle.kv_write(cache, rows[:2], np.array([6, 6], dtype=np.int64))
+    np.testing.assert_array_equal(dup[1, 2], rows[1])
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 def test_mutations_are_caught(monkeypatch):
