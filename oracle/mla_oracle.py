@@ -55,25 +55,35 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def held_positions(seq_len: int, W: int, r: int) -> np.ndarray:
-    """Global positions of the local rows a rank holds: t*W + r for t < seq_len.
-
-    Round-robin placement with interleave 1 (PR #52188 page, key source
-    snippets, cp_local_slot: segment index modulo the CP size picks the rank).
-    """
-    return np.arange(int(seq_len), dtype=np.int64) * W + r
+def owns(p: np.ndarray, W: int, r: int, interleave: int = 1) -> np.ndarray:
+    """Whether rank r holds global position p: positions are dealt to the
+    ranks in segments of `interleave`, segment k going to rank k mod W
+    (PR #52188 page, key source snippets, cp_local_slot)."""
+    return (np.asarray(p) // interleave) % W == r
 
 
-def local_count(g: int, W: int, r: int) -> int:
+def held_positions(seq_len: int, W: int, r: int, interleave: int = 1) -> np.ndarray:
+    """Global positions of the local rows a rank holds, in order: the first
+    seq_len positions it owns (local row t is the t-th of them).  By
+    enumeration; with interleave 1 these are t*W + r."""
+    n = int(seq_len)
+    if n <= 0:
+        return np.zeros(0, dtype=np.int64)
+    span = (n // interleave + 2) * interleave * W  # enough positions to hold n owned ones
+    p = np.arange(span, dtype=np.int64)
+    return p[owns(p, W, r, interleave)][:n]
+
+
+def local_count(g: int, W: int, r: int, interleave: int = 1) -> int:
     """How many of the global positions 0..g-1 rank r holds, by enumeration."""
     if g <= 0:
         return 0
     p = np.arange(int(g), dtype=np.int64)
-    return int(np.count_nonzero(p % W == r))
+    return int(np.count_nonzero(owns(p, W, r, interleave)))
 
 
 def visible_positions(seq_len: int, tot: Optional[int], q_len: int, j: int,
-                      W: int, r: int, causal: bool) -> np.ndarray:
+                      W: int, r: int, causal: bool, interleave: int = 1) -> np.ndarray:
     """Global positions row j of a request attends to on rank r.
 
     Causal: the row is the token at global position tot - q_len + j, so it
@@ -83,7 +93,7 @@ def visible_positions(seq_len: int, tot: Optional[int], q_len: int, j: int,
     sees the ones it holds.  Non-causal: every held position (the draft block
     repeats the same context length for each row).
     """
-    held = held_positions(seq_len, W, r)
+    held = held_positions(seq_len, W, r, interleave)
     if not causal:
         return held
     g = max(int(tot) - (q_len - 1 - j), 0)
@@ -117,7 +127,7 @@ def attend(q_rows: np.ndarray, kv_rows: np.ndarray, scale: float, base: str = "e
 def mla_decode(q_bits: np.ndarray, kv_rows: Callable[[int, np.ndarray], np.ndarray],
                seq_lens: Sequence[int], tot: Optional[Sequence[int]], W: int, r: int,
                causal: bool, scale: float, base: str = "e",
-               rows: Optional[Sequence[Tuple[int, int, int]]] = None):
+               rows: Optional[Sequence[Tuple[int, int, int]]] = None, interleave: int = 1):
     """Oracle for one rank's decode call.
 
     q_bits:   [B, Q, H, 576] bf16 bits.
@@ -126,6 +136,8 @@ def mla_decode(q_bits: np.ndarray, kv_rows: Callable[[int, np.ndarray], np.ndarr
     seq_lens: rank-local lengths; tot: global causal lengths (None: equal to
               seq_lens, the single-rank case).
     rows:     optional list of (b, j, h) to compute; default all.
+    interleave: the rank holds positions in segments of this many (1: every
+              W-th position).
     Returns (out [B*Q, H, 512], lse [B*Q, H]) as float64; rows not asked for
     are NaN.
     """
@@ -146,7 +158,7 @@ def mla_decode(q_bits: np.ndarray, kv_rows: Callable[[int, np.ndarray], np.ndarr
         t = None if tot is None else int(tot[b])
         if t is None:
             t = int(seq_lens[b])
-        pos = visible_positions(int(seq_lens[b]), t, Q, j, W, r, causal)
+        pos = visible_positions(int(seq_lens[b]), t, Q, j, W, r, causal, interleave)
         key = (b, pos.size, int(pos[-1]) if pos.size else -1)
         if key not in cache:
             cache.clear()

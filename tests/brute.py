@@ -12,11 +12,14 @@ def bf16_to_float(bits: int) -> float:
     return struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0]
 
 
-def is_visible(p, j, q_len, tot, seq_len, W, r, causal):
+def is_visible(p, j, q_len, tot, seq_len, W, r, causal, interleave=1):
     """Global position p is visible to query row j of the request on rank r."""
-    if p % W != r:           # rank r holds only positions congruent to r
+    I = interleave
+    if (p // I) % W != r:    # rank r holds the segments of I positions dealt to it
         return False
-    if p // W >= seq_len:    # ... and only its first seq_len of them
+    # ... and only its first seq_len positions: p is its local row
+    # (whole rounds of W segments before p) * I + offset inside the segment
+    if (p // (I * W)) * I + p % I >= seq_len:
         return False
     if causal:
         query_pos = tot - q_len + j   # the row's own global position

@@ -33,7 +33,8 @@ def tiny(B=2, H=3, Q=3, W=2, causal=True, lengths=(9, 14), seed=11, ranks=None, 
 def oracle_rank(wl, r, base="e", causal=None):
     s = wl.spec
     causal = s.causal if causal is None else causal
-    return oracle.mla_decode(wl.q_bits, wl.global_rows, wl.seq_lens[r], wl.tot, s.W, r, causal, s.scale, base)
+    return oracle.mla_decode(wl.q_bits, wl.global_rows, wl.seq_lens[r], wl.tot, s.W, r, causal, s.scale, base,
+                             interleave=s.interleave)
 
 
 # ---------------------------------------------------------------- lengths
@@ -62,6 +63,41 @@ def test_page_formula_with_interleave_matches_enumeration():
                 for G in range(0, 300):
                     enum = sum(1 for p in range(G) if (p // I) % W == r)
                     assert enum == page_local_len(G, W, r, I)
+
+
+def test_held_positions_with_interleave_match_the_slot_ownership():
+    # the positions a rank holds, in order, are the positions cp_local_slot
+    # gives it a slot for, and local row t of them gets the t-th slot of the
+    # rank's paging (table entry t // bs, offset t % bs)
+    bs = 8
+    for I in (1, 2, 4, 8):
+        for W in (1, 2, 3, 4):
+            for r in range(W):
+                L = 157
+                held = oracle.held_positions(oracle.local_count(L, W, r, I), W, r, I)
+                pos = np.arange(L, dtype=np.int64)[None, :]
+                bt = np.arange(100, dtype=np.int32)[None, :] * 3 + 1
+                slots = oracle.cp_local_slot(pos, bt, bs, W, r, I)[0]
+                owned = np.nonzero(slots != oracle.PAD_SLOT_ID)[0]
+                assert owned.tolist() == held.tolist(), (I, W, r)
+                t = np.arange(held.size)
+                assert slots[owned].tolist() == (bt[0, t // bs].astype(np.int64) * bs + t % bs).tolist()
+
+
+def test_visible_positions_with_interleave_match_bruteforce_predicate():
+    for I in (2, 4):
+        for W in (2, 3):
+            for r in range(W):
+                for tot in range(0, 60, 5):
+                    seq = oracle.local_count(tot, W, r, I)
+                    assert seq == page_local_len(tot, W, r, I)
+                    for Q in (1, 4):
+                        for j in range(Q):
+                            for causal in (True, False):
+                                got = oracle.visible_positions(seq, tot, Q, j, W, r, causal, I).tolist()
+                                exp = [p for p in range(tot + W * I)
+                                       if brute.is_visible(p, j, Q, tot, seq, W, r, causal, I)]
+                                assert got == exp, (I, W, r, tot, Q, j, causal)
 
 
 def test_visible_count_textbook_causal_w1():
@@ -213,9 +249,11 @@ def test_single_rank_equals_non_dcp():
     np.testing.assert_array_equal(l1, l0)
 
 
-@pytest.mark.parametrize("W,causal,base", [(2, True, "e"), (8, True, "e"), (3, False, "2"), (8, True, "2")])
-def test_sharded_then_merged_equals_unsharded(W, causal, base):
-    wl = tiny(B=3, H=2, Q=4, W=W, causal=causal, lengths=(5, 29, 40), seed=41 + W)
+@pytest.mark.parametrize("W,causal,base,I", [(2, True, "e", 1), (8, True, "e", 1), (3, False, "2", 1),
+                                           (8, True, "2", 1), (2, True, "e", 4), (3, True, "2", 2),
+                                           (4, False, "e", 2)])
+def test_sharded_then_merged_equals_unsharded(W, causal, base, I):
+    wl = tiny(B=3, H=2, Q=4, W=W, causal=causal, lengths=(5, 29, 40), seed=41 + W + I, interleave=I)
     parts = [oracle_rank(wl, r, base) for r in range(W)]
     mo, ml = oracle.merge_lse([p[0] for p in parts], [p[1] for p in parts], base)
     un = WL.unsharded(wl)
@@ -333,11 +371,12 @@ def test_paged_pool_holds_the_shards():
 
 # ---------------------------------------------------------------- KV write
 
-def test_kv_write_rebuilds_every_rank_pool_from_the_global_kv():
+@pytest.mark.parametrize("I", [1, 2, 4])
+def test_kv_write_rebuilds_every_rank_pool_from_the_global_kv(I):
     """Writing each global position's row at the slot cp_local_slot gives it,
     for every rank, rebuilds the rank pools the generator laid out by its own
     paging code (the rows requests use; the others keep their filler)."""
-    wl = tiny(B=3, H=2, Q=2, W=3, causal=True, lengths=(1, 70, 131), seed=63)
+    wl = tiny(B=3, H=2, Q=2, W=3, causal=True, lengths=(1, 70, 131), seed=63, interleave=I)
     bs, W = wl.spec.block_size, wl.spec.W
     for r in range(W):
         cache = wl.pools[r].copy()
@@ -350,7 +389,7 @@ def test_kv_write_rebuilds_every_rank_pool_from_the_global_kv():
         for b in range(wl.spec.B):
             L = int(wl.tot[b])
             pos = np.arange(L, dtype=np.int64)[None, :]
-            slots = oracle.cp_local_slot(pos, wl.block_table[b:b + 1], bs, W, r)
+            slots = oracle.cp_local_slot(pos, wl.block_table[b:b + 1], bs, W, r, I)
             cache = oracle.kv_write(cache, wl.global_kv(b), slots[0])
         np.testing.assert_array_equal(cache, wl.pools[r])
 
@@ -408,9 +447,10 @@ def test_mutations_are_caught(monkeypatch):
         monkeypatch.setattr(O, "attend", real_attend)
 
     vis_muts = {
-        "causal offset off by one": lambda s, t, Q, j, W, r, c: real_vis(s, t + 1, Q, j, W, r, c),
-        "wrong rank": lambda s, t, Q, j, W, r, c: real_vis(s, t, Q, j, W, (r + 1) % W, c),
-        "end-aligned local mask": lambda s, t, Q, j, W, r, c: real_vis(s, t, Q, j, W, r, False)[: max(s - (Q - 1 - j), 0)],
+        "causal offset off by one": lambda s, t, Q, j, W, r, c, i=1: real_vis(s, t + 1, Q, j, W, r, c, i),
+        "wrong rank": lambda s, t, Q, j, W, r, c, i=1: real_vis(s, t, Q, j, W, (r + 1) % W, c, i),
+        "end-aligned local mask": lambda s, t, Q, j, W, r, c, i=1: real_vis(s, t, Q, j, W, r, False, i)[
+            : max(s - (Q - 1 - j), 0)],
     }
     for name, fn in vis_muts.items():
         monkeypatch.setattr(O, "visible_positions", fn)

@@ -73,6 +73,7 @@ class Spec:
     lengths: object  # ("uniform", lo, hi) or explicit list of global lengths
     W: int = 1
     ranks: Sequence[int] = (0,)
+    interleave: int = 1   # ranks hold segments of this many consecutive positions
     block_size: int = 64
     scale: float = DEFAULT_SCALE
     lse_base: str = "e"
@@ -101,24 +102,33 @@ class Workload:
 
     def global_rows(self, b: int, positions: np.ndarray) -> np.ndarray:
         """bf16 rows of request b at the given global positions (contiguous global view)."""
-        W = self.spec.W
+        W, I = self.spec.W, self.spec.interleave
         positions = np.asarray(positions, dtype=np.int64)
         out = np.empty((positions.size, D_QK), dtype=np.uint16)
-        for r in np.unique(positions % W) if positions.size else []:
-            sel = (positions % W) == r
+        owner = (positions // I) % W
+        local = (positions // (I * W)) * I + positions % I
+        for r in np.unique(owner) if positions.size else []:
+            sel = owner == r
             if int(r) not in self.shards:
                 raise KeyError(f"rank {int(r)} shard of request {b} was not generated")
-            out[sel] = self.shards[int(r)][b][positions[sel] // W]
+            out[sel] = self.shards[int(r)][b][local[sel]]
         return out
 
     def global_kv(self, b: int) -> np.ndarray:
         """Whole contiguous global KV of request b (every rank's shard interleaved)."""
-        W = self.spec.W
+        W, I = self.spec.W, self.spec.interleave
         L = int(self.tot[b])
         g = np.empty((L, D_QK), dtype=np.uint16)
         for r in range(W):
-            g[r::W] = self.shards[r][b]
+            g[_owned(L, W, r, I)] = self.shards[r][b]
         return g
+
+
+def _owned(L: int, W: int, r: int, I: int) -> np.ndarray:
+    """The global positions 0..L-1 that rank r holds, in order: positions go
+    to the ranks in segments of I, segment k to rank k mod W."""
+    p = np.arange(int(L), dtype=np.int64)
+    return p[(p // I) % W == r]
 
 
 def _lengths(spec: Spec) -> np.ndarray:
@@ -155,17 +165,19 @@ def build(spec: Spec, ranks: Optional[Sequence[int]] = None) -> Workload:
         with ThreadPoolExecutor(_THREADS) as ex:
             q_bits = np.stack(list(ex.map(mkq, range(B))))
 
-    # rank shards: rank r holds the positions r, r+W, r+2W, ... of each request
+    # rank shards: rank r holds the positions of the segments dealt to it
+    # (with interleave 1: r, r+W, r+2W, ...) of each request, in order
+    I = spec.interleave
     shards: Dict[int, List[np.ndarray]] = {}
     seq_lens: Dict[int, np.ndarray] = {}
     for r in ranks:
-        counts = [len(range(r, int(tot[b]), W)) for b in range(B)]
+        counts = [len(_owned(int(tot[b]), W, r, I)) for b in range(B)]
         with ThreadPoolExecutor(_THREADS) as ex:
             shards[r] = list(ex.map(lambda b: _normal_bits([spec.seed, b, r, 0], (counts[b], D_QK)), range(B)))
         seq_lens[r] = np.asarray(counts, dtype=np.int32)
 
     # one block table shared by all ranks; sized for rank 0's (largest) shard
-    need = [max(1, -(-len(range(0, int(tot[b]), W)) // bs)) for b in range(B)]
+    need = [max(1, -(-len(_owned(int(tot[b]), W, 0, I)) // bs)) for b in range(B)]
     used = int(sum(need))
     P = spec.pool_blocks if spec.pool_blocks is not None else max(used + 1, int(math.ceil(spec.pool_factor * used)))
     assert P >= used
