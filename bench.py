@@ -67,12 +67,14 @@ class Hip:
 
 
 # ------------------------------------------------------------------ algorithmic work
-def row_keys(seq, tot, Q, j, W, r, causal):
-    """Rank-local visible keys of row j (the same bound the kernel applies)."""
+def row_keys(seq, tot, Q, j, W, r, causal, I=1):
+    """Rank-local visible keys of row j (the same bound the kernel applies):
+    of the global prefix g, rank r holds the positions of the segments of I
+    dealt to it."""
     if not causal:
         return seq
-    g = tot - (Q - 1 - j)
-    return min(seq, -(-max(g - r, 0) // W))
+    g = max(tot - (Q - 1 - j), 0)
+    return min(seq, g // (I * W) * I + min(max(g % (I * W) - r * I, 0), I))
 
 
 def rank_work(wl, r):
@@ -83,11 +85,11 @@ def rank_work(wl, r):
     for b in range(s.B):
         seq = int(wl.seq_lens[r][b])
         tot = int(wl.tot[b]) if not s.global_is_null else seq
-        nmax = row_keys(seq, tot, s.Q, s.Q - 1, s.W, r, s.causal)
+        nmax = row_keys(seq, tot, s.Q, s.Q - 1, s.W, r, s.causal, s.interleave)
         kv += nmax * KV_ROW_BYTES
         bt += -(-nmax // s.block_size) * 4
         for j in range(s.Q):
-            flops += row_keys(seq, tot, s.Q, j, s.W, r, s.causal) * s.H * FLOP_PER_KEY_ROW
+            flops += row_keys(seq, tot, s.Q, j, s.W, r, s.causal, s.interleave) * s.H * FLOP_PER_KEY_ROW
     rows = s.B * s.Q * s.H
     return dict(flops=flops, kv_bytes=kv, q_bytes=rows * KV_ROW_BYTES, bt_bytes=bt,
                 out_bytes=rows * 512 * 2, lse_bytes=rows * 4)
@@ -189,11 +191,13 @@ def cpu_baseline(wl, ranks, unit, budget_s=20.0):
             seq = wl.seq_lens[r]
             tot = None if (s.global_is_null and s.W == 1) else wl.tot
             rows = [(b, j, h) for j in range(s.Q) for h in range(s.H)]
-            oracle.mla_decode(wl.q_bits, wl.global_rows, seq, tot, s.W, r, s.causal, s.scale, s.lse_base, rows=rows)
+            oracle.mla_decode(wl.q_bits, wl.global_rows, seq, tot, s.W, r, s.causal, s.scale, s.lse_base, rows=rows,
+                              interleave=s.interleave)
             sq = int(seq[b])
             tt = int(wl.tot[b]) if tot is not None else sq
-            kv += row_keys(sq, tt, s.Q, s.Q - 1, s.W, r, s.causal) * KV_ROW_BYTES
-            flops += sum(row_keys(sq, tt, s.Q, j, s.W, r, s.causal) for j in range(s.Q)) * s.H * FLOP_PER_KEY_ROW
+            kv += row_keys(sq, tt, s.Q, s.Q - 1, s.W, r, s.causal, s.interleave) * KV_ROW_BYTES
+            flops += sum(row_keys(sq, tt, s.Q, j, s.W, r, s.causal, s.interleave)
+                         for j in range(s.Q)) * s.H * FLOP_PER_KEY_ROW
         done_b += 1
         if time.perf_counter() - t0 > budget_s:
             break
@@ -212,6 +216,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--replicas", type=int, default=0, help="KV replicas rotated per step (0: auto)")
+    ap.add_argument("--interleave", type=int, default=1,
+                    help="DCP interleave: ranks hold segments of this many positions (sharded workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
     args = ap.parse_args()
@@ -237,7 +243,7 @@ def main():
     dev = torch.device("cuda:0")
     hip = Hip()
 
-    spec = WL.config(args.config)
+    spec = WL.config(args.config, interleave=args.interleave)
     log(f"workload {spec.name}: generating inputs")
     t0 = time.perf_counter()
     wl = WL.build(spec)
@@ -279,12 +285,13 @@ def main():
         rep = i % replicas
         for r in ranks:
             for pos, nv in slot_jobs:
-                mla.cp_local_slot(pos, bt, s.block_size, s.W, r, nv)
+                mla.cp_local_slot(pos, bt, s.block_size, s.W, r, nv, cp_interleave=s.interleave)
             if evs is not None:
                 a, b_ = evs.pop()
                 mla.profile_attention_events(a, b_)
             mla.mla_decode(q, pools[r][rep], bt, seq[r], glob_arg, s.W, r, None, s.causal, s.scale, s.lse_base,
-                           max_seq_len=max_seq[r], out=outs[r], lse=lses[r], workspace=ws[r])
+                           max_seq_len=max_seq[r], out=outs[r], lse=lses[r], workspace=ws[r],
+                           cp_interleave=s.interleave)
         if evs is not None:
             mla.profile_attention_events(None, None)
         if s.W > 1 and len(ranks) == s.W:
@@ -347,13 +354,15 @@ def main():
     log("kv write: the step's new-token rows, and a bulk scatter")
     r0 = ranks[0]
     pos0, nv0 = slot_jobs[0]
-    slots0 = mla.cp_local_slot(pos0, bt, s.block_size, s.W, r0, nv0)
+    slots0 = mla.cp_local_slot(pos0, bt, s.block_size, s.W, r0, nv0, cp_interleave=s.interleave)
     pos_np = pos0.cpu().numpy()
     rows_np = np.zeros(pos_np.shape + (576,), dtype=np.uint16)  # rows of positions other ranks own stay zero
     for b in range(s.B):
         for i, p in enumerate(pos_np[b]):
-            if p >= 0 and p % s.W == r0 and p // s.W < len(wl.shards[r0][b]):
-                rows_np[b, i] = wl.shards[r0][b][p // s.W]
+            I = s.interleave
+            t = (p // (I * s.W)) * I + p % I  # the rank's local row of p
+            if p >= 0 and (p // I) % s.W == r0 and t < len(wl.shards[r0][b]):
+                rows_np[b, i] = wl.shards[r0][b][t]
     rows0 = bf16(rows_np)
     kvw = kv_write_rates(torch, mla, hip, stream, dev, (rows0, slots0, pools[r0][0]))
     log("achievable peaks: 1 GiB copy, 8192^3 bf16 GEMM (torch)")
@@ -366,7 +375,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": spec.name, "batch": s.B, "heads": s.H, "q_len": s.Q, "causal": s.causal,
-                   "cp_world": s.W, "ranks": ranks, "block_size": s.block_size, "kv_replicas": replicas},
+                   "cp_world": s.W, "cp_interleave": s.interleave, "ranks": ranks, "block_size": s.block_size,
+                   "kv_replicas": replicas},
         "tflops": round(tflops, 3), "kv_gbps": round(kv_gbps, 1),
         "alg_bytes_per_step": int(step_alg_bytes), "flops_per_step": int(step_flops),
         "attention_kernel_ms": round(avg_attn_ms, 5), "source_hash": source_hash(),

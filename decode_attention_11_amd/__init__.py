@@ -49,6 +49,8 @@ _SIGNATURES = [
     ("cp_local_slot", _I, [_P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, _P]),
     ("mla_profile_attention_events", _I, [_P, _P]),
     ("mla_kv_write", _I, [_P, _P, ctypes.c_int64, _P, _I, _I, _P]),
+    ("mla_decode_interleaved", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                                    ctypes.c_float, _I, _P, _P, _P, ctypes.c_size_t, _P]),
 ]
 
 
@@ -122,7 +124,7 @@ def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
                q_len: Optional[int] = None, causal: bool = True, scale: Optional[float] = None,
                lse_base: str = "e", *, max_seq_len: Optional[int] = None,
                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-               workspace: Optional[torch.Tensor] = None, return_lse: bool = True
+               workspace: Optional[torch.Tensor] = None, return_lse: bool = True, cp_interleave: int = 1
                ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """One rank's paged MLA decode.  q: [B, q_len, H, 576] (or [B*q_len, H, 576]
     with q_len given) bf16; kv_cache: [num_blocks, block_size, 576] bf16.
@@ -177,13 +179,16 @@ def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
     ws_bytes = int(lib.mla_decode_workspace_size(B, Q, H, int(max_seq_len)))
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
-    _check(lib.mla_decode(
-        q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(),
-        causal_seqlens_global.data_ptr() if causal_seqlens_global is not None else None,
-        B, Q, H, num_blocks, bs, max_blocks, int(max_seq_len), int(cp_world), int(cp_rank),
-        1 if causal else 0, float(scale), base, out.data_ptr(),
-        lse.data_ptr() if (return_lse and lse is not None) else None,
-        workspace.data_ptr(), int(workspace.numel()), _stream(dev)))
+    head = (q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(),
+            causal_seqlens_global.data_ptr() if causal_seqlens_global is not None else None,
+            B, Q, H, num_blocks, bs, max_blocks, int(max_seq_len), int(cp_world), int(cp_rank))
+    tail = (1 if causal else 0, float(scale), base, out.data_ptr(),
+            lse.data_ptr() if (return_lse and lse is not None) else None,
+            workspace.data_ptr(), int(workspace.numel()), _stream(dev))
+    if cp_interleave == 1:
+        _check(lib.mla_decode(*head, *tail))
+    else:
+        _check(lib.mla_decode_interleaved(*head, int(cp_interleave), *tail))
     return out, (lse if return_lse else None)
 
 

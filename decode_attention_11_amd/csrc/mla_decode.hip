@@ -54,6 +54,7 @@ struct DecodeArgs {
   int num_blocks, bs, max_blocks;
   int bs_shift;            // log2(bs) when bs is a power of two, else -1
   int W, rank, causal;
+  int I;                   // cp_interleave: positions go to ranks in segments of I
   float scale_log2;        // softmax scale times log2(e)
   int lse_base;
   int n_rt;                // row tiles per request
@@ -87,7 +88,7 @@ __device__ __forceinline__ void request_info(const DecodeArgs& a, int b, int& nb
   if (b < a.B) {
     seq = gload_i32(a.seq_lens + b);
     tot = a.glob ? gload_i32(a.glob + b) : seq;
-    nb = row_bound(seq, tot, a.Q, a.Q - 1, a.W, a.rank, a.causal);
+    nb = row_bound(seq, tot, a.Q, a.Q - 1, a.W, a.rank, a.I, a.causal);
   }
 }
 
@@ -623,7 +624,7 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
         for (int kk = 0; kk < M16_KSTEPS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 128 * kk);
         ring_issue_all(nxt, wave, sel_off);
         const int my_row = cc.d.rt * M16_ROWS + li;
-        nrow = my_row < a.R ? row_bound(cc.d.seq, cc.d.tot, a.Q, my_row / a.H, a.W, a.rank, a.causal) : 0;
+        nrow = my_row < a.R ? row_bound(cc.d.seq, cc.d.tot, a.Q, my_row / a.H, a.W, a.rank, a.I, a.causal) : 0;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) st.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         st.m_ref = NEG_INF;
@@ -934,7 +935,7 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
     const int32_t* btr = a.bt + (int64_t)bb * a.max_blocks;
     const int my_row = rt * R128_ROWS + wave * 32 + (lane & 31);
     const bool row_ok = my_row < a.R;
-    const int nrow = row_ok ? row_bound(seq, tot, a.Q, my_row / a.H, a.W, a.rank, a.causal) : 0;
+    const int nrow = row_ok ? row_bound(seq, tot, a.Q, my_row / a.H, a.W, a.rank, a.I, a.causal) : 0;
     // the smallest bound over the wave's rows: tiles below it are unmasked
     int nmin = nrow;
 #pragma unroll
@@ -1225,14 +1226,15 @@ extern "C" size_t mla_decode_workspace_size(int B, int q_len, int H, int max_seq
   return a > b ? a : b;
 }
 
-extern "C" int mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
-                          const int32_t* seq_lens, const int32_t* causal_seqlens_global,
-                          int B, int q_len, int H, int num_blocks, int block_size, int max_blocks,
-                          int max_seq_len, int cp_world, int cp_rank, int causal, float scale,
-                          int lse_base, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                          hipStream_t stream) {
+namespace {
+
+int decode(const void* q, const void* kv_cache, const int32_t* block_table, const int32_t* seq_lens,
+           const int32_t* causal_seqlens_global, int B, int q_len, int H, int num_blocks, int block_size,
+           int max_blocks, int max_seq_len, int cp_world, int cp_rank, int cp_interleave, int causal, float scale,
+           int lse_base, void* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (B < 0 || q_len < 1 || H < 1 || num_blocks < 1 || block_size < 1 || max_blocks < 1 ||
-      max_seq_len < 0 || cp_world < 1 || cp_rank < 0 || cp_rank >= cp_world ||
+      max_seq_len < 0 || cp_world < 1 || cp_rank < 0 || cp_rank >= cp_world || cp_interleave < 1 ||
+      (int64_t)cp_interleave * cp_world > (1 << 30) ||
       (causal != 0 && causal != 1) || (lse_base != MLA_LSE_BASE_E && lse_base != MLA_LSE_BASE_2) ||
       !std::isfinite(scale))
     return MLA_ERR_INVALID_ARG;
@@ -1254,6 +1256,7 @@ extern "C" int mla_decode(const void* q, const void* kv_cache, const int32_t* bl
   a.num_blocks = num_blocks; a.bs = block_size; a.max_blocks = max_blocks;
   a.bs_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
   a.W = cp_world; a.rank = cp_rank; a.causal = causal;
+  a.I = cp_interleave;
   a.scale_log2 = scale * LOG2E;
   a.lse_base = lse_base;
   a.n_rt = p.n_rt;
@@ -1277,4 +1280,28 @@ extern "C" int mla_decode(const void* q, const void* kv_cache, const int32_t* bl
     hipLaunchKernelGGL(combine_kernel<R128_ROWS>, dim3(B * p.n_rt * 8), dim3(256), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" int mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
+                          const int32_t* seq_lens, const int32_t* causal_seqlens_global,
+                          int B, int q_len, int H, int num_blocks, int block_size, int max_blocks,
+                          int max_seq_len, int cp_world, int cp_rank, int causal, float scale,
+                          int lse_base, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  return decode(q, kv_cache, block_table, seq_lens, causal_seqlens_global, B, q_len, H, num_blocks, block_size,
+                max_blocks, max_seq_len, cp_world, cp_rank, 1, causal, scale, lse_base, out, lse, workspace,
+                workspace_bytes, stream);
+}
+
+extern "C" int mla_decode_interleaved(const void* q, const void* kv_cache, const int32_t* block_table,
+                                      const int32_t* seq_lens, const int32_t* causal_seqlens_global,
+                                      int B, int q_len, int H, int num_blocks, int block_size, int max_blocks,
+                                      int max_seq_len, int cp_world, int cp_rank, int cp_interleave, int causal,
+                                      float scale, int lse_base, void* out, float* lse, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  return decode(q, kv_cache, block_table, seq_lens, causal_seqlens_global, B, q_len, H, num_blocks, block_size,
+                max_blocks, max_seq_len, cp_world, cp_rank, cp_interleave, causal, scale, lse_base, out, lse,
+                workspace, workspace_bytes, stream);
 }

@@ -81,17 +81,23 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
   return z;
 }
 
-// Rank-local visible key count of query row j of a request (interleave 1):
-// causal rows see the global prefix tot - (q_len-1-j) of which rank r holds
-// ceil(max(prefix - r, 0) / W) positions, capped by the rank's local length;
-// non-causal rows see the whole local length.
-__device__ __forceinline__ int row_bound(int seq, int tot, int q_len, int j, int W, int r, int causal) {
+// Rank-local visible key count of query row j of a request: causal rows see
+// the global prefix G = tot - (q_len-1-j); positions go to the ranks in
+// segments of I (segment k to rank k mod W), so rank r holds
+// (G / (I*W))*I + min(max(G % (I*W) - r*I, 0), I) of them (with I = 1:
+// ceil(max(G - r, 0) / W)), capped by its local length (PR #52188 page, key
+// source snippets: the per-row prefix and the rank-local length).
+// Non-causal rows see the whole local length.
+__device__ __forceinline__ int row_bound(int seq, int tot, int q_len, int j, int W, int r, int I, int causal) {
   if (seq < 0) seq = 0;
   if (!causal) return seq;
   int64_t g = (int64_t)tot - (q_len - 1 - j);
-  int64_t x = g - r;
-  if (x < 0) x = 0;
-  int64_t n = (x + W - 1) / W;
+  if (g < 0) g = 0;
+  const int64_t span = (int64_t)I * W;
+  const int64_t rounds = floordiv(g, span);
+  int64_t rem = g - rounds * span - (int64_t)r * I;
+  rem = rem < 0 ? 0 : (rem > I ? I : rem);
+  const int64_t n = rounds * I + rem;
   return n < seq ? (int)n : seq;
 }
 

@@ -117,6 +117,29 @@ int mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
                hipStream_t stream);
 
 /*
+ * mla_decode for ranks that hold their keys in segments of cp_interleave
+ * positions: segment k of a request's global positions (positions
+ * k*cp_interleave .. k*cp_interleave + cp_interleave - 1) belongs to rank
+ * k % cp_world, and the rank's local key t is the t-th position it owns
+ * (PR #52188 page, key source snippets, cp_local_slot, and the rank-local
+ * length it prints for an interleave).  The causal bound of row j becomes
+ *   G = max(tot_b - (q_len-1-j), 0),
+ *   n(b,j) = min(seq_lens[b], (G / (I*W))*I + min(max(G % (I*W) - r*I, 0), I))
+ * with I = cp_interleave, W = cp_world, r = cp_rank; everything else is as in
+ * mla_decode, which is this call with cp_interleave = 1.  (The native CP
+ * mask of the PR #54012 page supports interleave 1 only; this is the
+ * generalisation the slot mapping already describes.)
+ * Errors: those of mla_decode, and MLA_ERR_INVALID_ARG for cp_interleave < 1
+ * or cp_interleave*cp_world > 2^30.
+ */
+int mla_decode_interleaved(const void* q, const void* kv_cache, const int32_t* block_table,
+                           const int32_t* seq_lens, const int32_t* causal_seqlens_global,
+                           int B, int q_len, int H, int num_blocks, int block_size, int max_blocks,
+                           int max_seq_len, int cp_world, int cp_rank, int cp_interleave, int causal,
+                           float scale, int lse_base, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Profiling aid (not part of the computation): for the calling host thread,
  * record `start` just before and `stop` just after the split-KV attention
  * kernel of each following mla_decode call, on that call's stream.  Pass two

@@ -49,7 +49,7 @@ class Uploaded:
         gnull = s.global_is_null if global_null is None else global_null
         g = None if gnull else self.tot
         return mla.mla_decode(self.q, self.pools[r], self.bt, self.seq[r], g, cp_world=s.W, cp_rank=r,
-                              causal=causal, scale=s.scale, lse_base=base, **kw)
+                              causal=causal, scale=s.scale, lse_base=base, cp_interleave=s.interleave, **kw)
 
 
 def compare(out, lse, ro, rl, label="", rows=None):

@@ -22,7 +22,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["mla_status_string", "mla_decode_workspace_size", "mla_decode",
                                            "mla_merge_lse", "cp_local_slot", "mla_profile_attention_events",
-                                           "mla_kv_write"])
+                                           "mla_kv_write", "mla_decode_interleaved"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -134,4 +134,21 @@ def test_kv_write_rejects_bad_arguments(bad):
 
 def test_kv_write_empty_is_a_noop():
     assert _kv_write(n=0, rows=None, slots=None, cache=None) == 0
+
+
+def _decode_il(I, **kw):
+    lib = mla.load_library()
+    a = dict(q=1, kv=1, bt=1, sl=1, gl=1, B=2, Q=1, H=16, nblk=4, bs=64, maxb=2, maxlen=128, W=2, r=1,
+             causal=1, scale=0.1, base=0, out=1, lse=1, ws=1, wsb=0, stream=None)
+    a.update(kw)
+    return lib.mla_decode_interleaved(a["q"], a["kv"], a["bt"], a["sl"], a["gl"], a["B"], a["Q"], a["H"], a["nblk"],
+                                      a["bs"], a["maxb"], a["maxlen"], a["W"], a["r"], I, a["causal"],
+                                      ctypes.c_float(a["scale"]), a["base"], a["out"], a["lse"], a["ws"], a["wsb"],
+                                      a["stream"])
+
+
+@pytest.mark.parametrize("I,kw", [(0, {}), (-2, {}), (1 << 29, dict(W=4, r=1)), (2, dict(r=2)), (2, dict(gl=None))])
+def test_interleaved_decode_rejects_bad_arguments(I, kw):
+    # every case fails a host check (the last ones also have a zero-size workspace)
+    assert _decode_il(I, **kw) == 1
 

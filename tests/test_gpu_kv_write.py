@@ -39,10 +39,11 @@ def test_kv_write_matches_oracle(n, P, bs):
     assert np.array_equal(bits(c), exp)
 
 
-@pytest.mark.parametrize("H,Q,W,causal", [(16, 4, 2, True), (128, 4, 4, True), (16, 16, 2, False)])
-def test_write_new_tokens_then_attend(H, Q, W, causal):
-    spec = WL.Spec(name=f"write_then_attend_h{H}_w{W}", B=3, H=H, Q=Q, causal=causal, seed=808 + H + W,
-                   lengths=[Q + 1, 700, 2500], W=W, ranks=tuple(range(W)))
+@pytest.mark.parametrize("H,Q,W,causal,I", [(16, 4, 2, True, 1), (128, 4, 4, True, 1), (16, 16, 2, False, 1),
+                                             (16, 4, 2, True, 8), (128, 4, 4, True, 2)])
+def test_write_new_tokens_then_attend(H, Q, W, causal, I):
+    spec = WL.Spec(name=f"write_then_attend_h{H}_w{W}_i{I}", B=3, H=H, Q=Q, causal=causal, seed=808 + H + W + I,
+                   lengths=[Q + 1, 700, 2500], W=W, ranks=tuple(range(W)), interleave=I)
     wl = WL.build(spec)
     up = Uploaded(wl)
     bt = i32_dev(wl.block_table)
@@ -54,12 +55,13 @@ def test_write_new_tokens_then_attend(H, Q, W, causal):
         pool = wl.pools[r].copy()
         for b in range(spec.B):
             for p in new_pos[b]:
-                if p % W == r:
-                    t = int(p) // W
+                p = int(p)
+                if (p // I) % W == r:
+                    t = (p // (I * W)) * I + p % I  # the rank's local row of p
                     pool[wl.block_table[b, t // bs], t % bs] = 0x7FC0
         up.pools[r] = bf16_dev(pool)
         say(f"{spec.name} rank {r}: slots and write of {spec.B}x{Q} new rows")
-        slots = mla.cp_local_slot(i64_dev(new_pos), bt, bs, W, r)
+        slots = mla.cp_local_slot(i64_dev(new_pos), bt, bs, W, r, cp_interleave=I)
         mla.kv_write(bf16_dev(new_rows), slots, up.pools[r])
         torch.cuda.synchronize()
         assert np.array_equal(bits(up.pools[r]), wl.pools[r]), f"rank {r} pool after the write"

@@ -28,7 +28,8 @@ def oracle_rank(wl, r, base="e", causal=None):
     s = wl.spec
     causal = s.causal if causal is None else causal
     tot = None if (s.global_is_null and s.W == 1) else wl.tot
-    return oracle.mla_decode(wl.q_bits, wl.global_rows, wl.seq_lens[r], tot, s.W, r, causal, s.scale, base)
+    return oracle.mla_decode(wl.q_bits, wl.global_rows, wl.seq_lens[r], tot, s.W, r, causal, s.scale, base,
+                             interleave=s.interleave)
 
 
 def spec(name, B, H, Q, causal, lengths, W=1, ranks=None, bs=64, seed=None, **kw):
@@ -64,6 +65,11 @@ CASES = [
     # one request over every bundle: dozens of partial slots per group, merged
     # by the combine several batches at a time
     spec("one_request_all_bundles_h128", 1, 128, 4, True, [12000], global_is_null=True),
+    # ranks holding segments of several positions (interleave > 1)
+    spec("h16_q4_dcp2_interleave4", 3, 16, 4, True, [5, 333, 2049], W=2, interleave=4),
+    spec("h128_q4_dcp4_interleave16", 2, 128, 4, True, [70, 1500], W=4, interleave=16, bs=64),
+    spec("h16_q16_noncausal_dcp3_interleave2", 2, 16, 16, False, [100, 900], W=3, interleave=2),
+    spec("h24_q3_dcp8_interleave8_bs128", 2, 24, 3, True, [200, 1111], W=8, interleave=8, bs=128),
 ]
 
 
@@ -205,9 +211,9 @@ def test_end_aligned_mask_is_not_what_the_kernel_does():
     np.testing.assert_allclose(lse.cpu().numpy(), math.log(4.0), atol=1e-5)
 
 
-@pytest.mark.parametrize("W,base", [(2, "e"), (8, "e"), (8, "2"), (3, "2")])
-def test_sharded_then_merged_equals_unsharded(W, base):
-    sp = spec(f"shard_merge_w{W}", 3, 128 if W == 8 else 16, 4, True, [7, 800, 2600], W=W)
+@pytest.mark.parametrize("W,base,I", [(2, "e", 1), (8, "e", 1), (8, "2", 1), (3, "2", 1), (2, "e", 16), (8, "e", 4)])
+def test_sharded_then_merged_equals_unsharded(W, base, I):
+    sp = spec(f"shard_merge_w{W}_i{I}", 3, 128 if W == 8 else 16, 4, True, [7, 800, 2600], W=W, interleave=I)
     wl = WL.build(sp)
     up = Uploaded(wl)
     parts = [up.run(r, base) for r in range(W)]
