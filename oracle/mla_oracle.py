@@ -171,6 +171,37 @@ def mla_decode(q_bits: np.ndarray, kv_rows: Callable[[int, np.ndarray], np.ndarr
     return out, lse
 
 
+def mla_decode_varlen(q_tok: np.ndarray, query_start_loc: Sequence[int],
+                      kv_rows: Callable[[int, np.ndarray], np.ndarray],
+                      seq_lens: Sequence[int], tot: Optional[Sequence[int]], W: int, r: int,
+                      causal: bool, scale: float, base: str = "e", interleave: int = 1):
+    """Oracle for one rank's decode call with a query length per request.
+
+    q_tok:  [T, H, 576] bf16 bits, the query tokens of all requests packed;
+            request b owns tokens query_start_loc[b] .. query_start_loc[b+1]-1.
+    Reading (PR #52188 page, key source snippets: the per-row causal prefix
+    tot - (query_len - 1 - j); summary: the builder declares support for
+    batches of different query lengths): each request applies the per-row
+    prefix with its own query length; a request with no tokens has no rows.
+    Returns (out [T, H, 512], lse [T, H]) as float64.
+    """
+    T, H, D = q_tok.shape
+    assert D == D_QK
+    qsl = [int(x) for x in query_start_loc]
+    out = np.full((T, H, D_V), np.nan)
+    lse = np.full((T, H), np.nan)
+    for b in range(len(qsl) - 1):
+        q_len = qsl[b + 1] - qsl[b]
+        t = int(seq_lens[b]) if tot is None else int(tot[b])
+        for j in range(q_len):
+            pos = visible_positions(int(seq_lens[b]), t, q_len, j, W, r, causal, interleave)
+            kv = bf16_bits_to_f64(kv_rows(b, pos))
+            o, l = attend(bf16_bits_to_f64(q_tok[qsl[b] + j]), kv, scale, base)
+            out[qsl[b] + j] = o
+            lse[qsl[b] + j] = l
+    return out, lse
+
+
 def merge_lse(outs: List[np.ndarray], lses: List[np.ndarray], base: str = "e"
               ) -> Tuple[np.ndarray, np.ndarray]:
     """Combine partial (out, lse) pairs of disjoint key sets into the full result.

@@ -27,12 +27,12 @@ def is_visible(p, j, q_len, tot, seq_len, W, r, causal, interleave=1):
     return True
 
 
-def attend_row(q, kv_global, j, q_len, tot, seq_len, W, r, causal, scale, base="e"):
+def attend_row(q, kv_global, j, q_len, tot, seq_len, W, r, causal, scale, base="e", interleave=1):
     """q: list of 576 floats; kv_global: list of rows (list of 576 floats) indexed by global position."""
     weights = []
     vals = []
     for p in range(len(kv_global)):
-        if not is_visible(p, j, q_len, tot, seq_len, W, r, causal):
+        if not is_visible(p, j, q_len, tot, seq_len, W, r, causal, interleave):
             continue
         s = scale * math.fsum(q[d] * kv_global[p][d] for d in range(576))
         weights.append(math.exp(s))

@@ -197,6 +197,65 @@ def test_oracle_matches_pure_python_bruteforce():
                         np.testing.assert_allclose(o[b * s.Q + j, h], bo, rtol=0, atol=1e-12)
 
 
+# ---------------------------------------------------------------- varlen
+
+def tiny_varlen(q_lens, W=2, causal=True, lengths=(9, 14, 6), seed=17, I=1):
+    spec = WL.Spec(name="tiny_varlen", B=len(q_lens), H=2, Q=max(q_lens), causal=causal, seed=seed,
+                   lengths=list(lengths), W=W, ranks=tuple(range(W)), block_size=4, interleave=I, q_lens=list(q_lens))
+    return WL.build(spec)
+
+
+def varlen_rank(wl, r, base="e"):
+    s = wl.spec
+    return oracle.mla_decode_varlen(wl.q_tok, wl.query_start_loc, wl.global_rows, wl.seq_lens[r], wl.tot, s.W, r,
+                                    s.causal, s.scale, base, interleave=s.interleave)
+
+
+@pytest.mark.parametrize("causal,I", [(True, 1), (False, 1), (True, 2)])
+def test_varlen_oracle_matches_pure_python_bruteforce(causal, I):
+    wl = tiny_varlen([3, 0, 1], W=2, causal=causal, lengths=(9, 5, 12), I=I)
+    s, qsl = wl.spec, wl.query_start_loc
+    for r in range(2):
+        o, l = varlen_rank(wl, r)
+        for b in range(s.B):
+            kv = [[brute.bf16_to_float(x) for x in row] for row in wl.global_kv(b)]
+            ql = int(qsl[b + 1] - qsl[b])
+            for j in range(ql):
+                for h in range(s.H):
+                    q = [brute.bf16_to_float(x) for x in wl.q_tok[qsl[b] + j, h]]
+                    bo, bl = brute.attend_row(q, kv, j, ql, int(wl.tot[b]), int(wl.seq_lens[r][b]), s.W, r, causal,
+                                              s.scale, "e", I)
+                    got = l[qsl[b] + j, h]
+                    assert abs(got - bl) <= 1e-12 or (bl == -math.inf and got == -math.inf)
+                    np.testing.assert_allclose(o[qsl[b] + j, h], bo, rtol=0, atol=1e-12)
+
+
+def test_varlen_equals_one_uniform_call_per_request():
+    # each request alone is a uniform call with its own query length
+    wl = tiny_varlen([4, 1, 2], W=3, lengths=(17, 8, 23))
+    s, qsl = wl.spec, wl.query_start_loc
+    for r in range(3):
+        o, l = varlen_rank(wl, r)
+        for b in range(s.B):
+            ql = int(qsl[b + 1] - qsl[b])
+            q1 = wl.q_tok[qsl[b]:qsl[b + 1]][None]  # [1, ql, H, 576]
+            uo, ul = oracle.mla_decode(q1, lambda _b, pos: wl.global_rows(b, pos), wl.seq_lens[r][b:b + 1],
+                                       wl.tot[b:b + 1], s.W, r, True, s.scale, "e")
+            np.testing.assert_array_equal(o[qsl[b]:qsl[b + 1]], uo)
+            np.testing.assert_array_equal(l[qsl[b]:qsl[b + 1]], ul)
+
+
+def test_varlen_with_equal_lengths_is_the_uniform_call():
+    wl = tiny_varlen([3, 3, 3], W=2, lengths=(9, 14, 6))
+    s = wl.spec
+    for r in range(2):
+        o, l = varlen_rank(wl, r)
+        q = wl.q_tok.reshape(s.B, 3, s.H, oracle.D_QK)
+        uo, ul = oracle.mla_decode(q, wl.global_rows, wl.seq_lens[r], wl.tot, s.W, r, True, s.scale, "e")
+        np.testing.assert_array_equal(o, uo)
+        np.testing.assert_array_equal(l, ul)
+
+
 def test_zero_query_gives_uniform_mean_and_log_count():
     # q = 0: every visible score is 0, softmax is uniform: lse = ln(count), out = mean of V
     wl = tiny(B=2, H=2, Q=4, W=3, causal=True, lengths=(17, 30), seed=9, q_zero=True)

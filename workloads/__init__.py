@@ -74,6 +74,7 @@ class Spec:
     W: int = 1
     ranks: Sequence[int] = (0,)
     interleave: int = 1   # ranks hold segments of this many consecutive positions
+    q_lens: Optional[Sequence[int]] = None  # per-request query lengths (varlen); Q is then their maximum
     block_size: int = 64
     scale: float = DEFAULT_SCALE
     lse_base: str = "e"
@@ -95,6 +96,8 @@ class Workload:
     block_table: np.ndarray             # [B, max_blocks] int32
     pools: Dict[int, np.ndarray]        # rank -> [P, bs, 576] uint16
     slot_inputs: Optional[dict] = None
+    q_tok: Optional[np.ndarray] = None  # varlen: [T, H, 576] uint16, requests' tokens packed
+    query_start_loc: Optional[np.ndarray] = None  # varlen: [B+1] int32
 
     @property
     def max_blocks(self) -> int:
@@ -155,7 +158,17 @@ def build(spec: Spec, ranks: Optional[Sequence[int]] = None) -> Workload:
     B, H, Q, W, bs = spec.B, spec.H, spec.Q, spec.W, spec.block_size
     tot = _lengths(spec)
 
-    # query
+    # query (varlen: request b's q_lens[b] tokens, packed)
+    q_tok = qsl = None
+    if spec.q_lens is not None:
+        ql = [int(x) for x in spec.q_lens]
+        assert len(ql) == B and max(ql) == Q, "Q must be the largest per-request query length"
+        qsl = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+
+        def mkq_var(b):
+            rng = np.random.default_rng([spec.seed, b, 1])
+            return bf16_bits(rng.standard_normal((ql[b], H, D_QK), dtype=np.float32) * np.float32(spec.q_mult))
+        q_tok = np.concatenate([mkq_var(b) for b in range(B)]) if qsl[-1] else np.zeros((0, H, D_QK), np.uint16)
     if spec.q_zero:
         q_bits = np.zeros((B, Q, H, D_QK), dtype=np.uint16)
     else:
@@ -210,7 +223,7 @@ def build(spec: Spec, ranks: Optional[Sequence[int]] = None) -> Workload:
         pools[r] = pool
 
     return Workload(spec=spec, tot=tot, q_bits=q_bits, seq_lens=seq_lens, shards=shards,
-                    block_table=bt, pools=pools)
+                    block_table=bt, pools=pools, q_tok=q_tok, query_start_loc=qsl)
 
 
 def unsharded(wl: Workload) -> Workload:
