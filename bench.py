@@ -77,20 +77,24 @@ def row_keys(seq, tot, Q, j, W, r, causal, I=1):
     return min(seq, g // (I * W) * I + min(max(g % (I * W) - r * I, 0), I))
 
 
+def q_lens_of(s):
+    return [int(x) for x in s.q_lens] if s.q_lens is not None else [s.Q] * s.B
+
+
 def rank_work(wl, r):
     s = wl.spec
     flops = 0
     kv = 0
     bt = 0
-    for b in range(s.B):
+    for b, ql in enumerate(q_lens_of(s)):
         seq = int(wl.seq_lens[r][b])
         tot = int(wl.tot[b]) if not s.global_is_null else seq
-        nmax = row_keys(seq, tot, s.Q, s.Q - 1, s.W, r, s.causal, s.interleave)
+        nmax = row_keys(seq, tot, ql, ql - 1, s.W, r, s.causal, s.interleave) if ql else 0
         kv += nmax * KV_ROW_BYTES
         bt += -(-nmax // s.block_size) * 4
-        for j in range(s.Q):
-            flops += row_keys(seq, tot, s.Q, j, s.W, r, s.causal, s.interleave) * s.H * FLOP_PER_KEY_ROW
-    rows = s.B * s.Q * s.H
+        for j in range(ql):
+            flops += row_keys(seq, tot, ql, j, s.W, r, s.causal, s.interleave) * s.H * FLOP_PER_KEY_ROW
+    rows = sum(q_lens_of(s)) * s.H
     return dict(flops=flops, kv_bytes=kv, q_bytes=rows * KV_ROW_BYTES, bt_bytes=bt,
                 out_bytes=rows * 512 * 2, lse_bytes=rows * 4)
 
@@ -186,25 +190,34 @@ def cpu_baseline(wl, ranks, unit, budget_s=20.0):
     s = wl.spec
     done_b, flops, kv = 0, 0, 0
     t0 = time.perf_counter()
+    qls = q_lens_of(s)
     for b in range(s.B):
         for r in ranks:
             seq = wl.seq_lens[r]
             tot = None if (s.global_is_null and s.W == 1) else wl.tot
-            rows = [(b, j, h) for j in range(s.Q) for h in range(s.H)]
-            oracle.mla_decode(wl.q_bits, wl.global_rows, seq, tot, s.W, r, s.causal, s.scale, s.lse_base, rows=rows,
-                              interleave=s.interleave)
+            ql = qls[b]
+            if s.q_lens is not None:
+                qsl = wl.query_start_loc
+                one = np.array([0, ql], dtype=np.int32)
+                oracle.mla_decode_varlen(wl.q_tok[qsl[b]:qsl[b + 1]], one, lambda _b, pos: wl.global_rows(b, pos),
+                                         seq[b:b + 1], None if tot is None else tot[b:b + 1], s.W, r, s.causal,
+                                         s.scale, s.lse_base, interleave=s.interleave)
+            else:
+                rows = [(b, j, h) for j in range(s.Q) for h in range(s.H)]
+                oracle.mla_decode(wl.q_bits, wl.global_rows, seq, tot, s.W, r, s.causal, s.scale, s.lse_base,
+                                  rows=rows, interleave=s.interleave)
             sq = int(seq[b])
             tt = int(wl.tot[b]) if tot is not None else sq
-            kv += row_keys(sq, tt, s.Q, s.Q - 1, s.W, r, s.causal, s.interleave) * KV_ROW_BYTES
-            flops += sum(row_keys(sq, tt, s.Q, j, s.W, r, s.causal, s.interleave)
-                         for j in range(s.Q)) * s.H * FLOP_PER_KEY_ROW
+            kv += (row_keys(sq, tt, ql, ql - 1, s.W, r, s.causal, s.interleave) if ql else 0) * KV_ROW_BYTES
+            flops += sum(row_keys(sq, tt, ql, j, s.W, r, s.causal, s.interleave)
+                         for j in range(ql)) * s.H * FLOP_PER_KEY_ROW
         done_b += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     value = kv / dt / 1e9 if unit == "GB/s" else flops / dt / 1e12
     return {"value": round(value, 6), "unit": unit, "cores": int(cores), "kind": "oracle",
-            "sample": f"{done_b} of {s.B} requests, all {s.Q}x{s.H} rows, ranks {list(ranks)}, "
+            "sample": f"{done_b} of {s.B} requests, all their query rows x {s.H} heads, ranks {list(ranks)}, "
                       f"float64 numpy oracle, {dt:.1f} s wall"}
 
 
@@ -216,6 +229,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--replicas", type=int, default=0, help="KV replicas rotated per step (0: auto)")
+    ap.add_argument("--varlen", action="store_true",
+                    help="per-request query lengths uniform in [1, q_len] (seeded), through mla_decode_varlen")
     ap.add_argument("--interleave", type=int, default=1,
                     help="DCP interleave: ranks hold segments of this many positions (sharded workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -244,6 +259,10 @@ def main():
     hip = Hip()
 
     spec = WL.config(args.config, interleave=args.interleave)
+    if args.varlen:
+        ql = np.random.default_rng([spec.seed, 31337]).integers(1, spec.Q, size=spec.B, endpoint=True)
+        ql[0] = spec.Q  # the largest length stays the workload's q_len
+        spec = WL.config(args.config, interleave=args.interleave, q_lens=[int(x) for x in ql])
     log(f"workload {spec.name}: generating inputs")
     t0 = time.perf_counter()
     wl = WL.build(spec)
@@ -255,7 +274,9 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
 
     replicas = args.replicas or (3 if args.config in (1, 2) else 1)
-    q = bf16(wl.q_bits)
+    q = bf16(wl.q_tok if s.q_lens is not None else wl.q_bits)
+    qsl_dev = torch.from_numpy(wl.query_start_loc).to(dev) if s.q_lens is not None else None
+    T = sum(q_lens_of(s))
     bt = torch.from_numpy(wl.block_table).to(dev)
     tot = torch.from_numpy(wl.tot.astype(np.int32)).to(dev)
     pools = {r: [bf16(wl.pools[r])] for r in ranks}
@@ -269,15 +290,17 @@ def main():
         slot_jobs = [(torch.from_numpy(si["ctx_positions"]).to(dev), torch.from_numpy(si["ctx_num_valid"]).to(dev)),
                      (torch.from_numpy(si["query_positions"]).to(dev), None)]
     else:
-        newpos = (wl.tot[:, None] - s.Q + np.arange(s.Q)[None, :]).astype(np.int64)
+        qls = np.asarray(q_lens_of(s))
+        newpos = (wl.tot[:, None] - qls[:, None] + np.arange(s.Q)[None, :]).astype(np.int64)
+        newpos[np.arange(s.Q)[None, :] >= qls[:, None]] = -1  # shorter requests: pad positions
         slot_jobs = [(torch.from_numpy(newpos).to(dev), None)]
     max_seq = {r: int(wl.seq_lens[r].max()) for r in ranks}
-    outs = {r: torch.empty((s.B * s.Q, s.H, 512), dtype=torch.bfloat16, device=dev) for r in ranks}
-    lses = {r: torch.empty((s.B * s.Q, s.H), dtype=torch.float32, device=dev) for r in ranks}
+    outs = {r: torch.empty((T, s.H, 512), dtype=torch.bfloat16, device=dev) for r in ranks}
+    lses = {r: torch.empty((T, s.H), dtype=torch.float32, device=dev) for r in ranks}
     ws = {r: torch.empty((max(mla.mla_decode_workspace_size(s.B, s.Q, s.H, max_seq[r]), 1),),
                          dtype=torch.uint8, device=dev) for r in ranks}
-    merged = (torch.empty((s.B * s.Q, s.H, 512), dtype=torch.bfloat16, device=dev),
-              torch.empty((s.B * s.Q, s.H), dtype=torch.float32, device=dev))
+    merged = (torch.empty((T, s.H, 512), dtype=torch.bfloat16, device=dev),
+              torch.empty((T, s.H), dtype=torch.float32, device=dev))
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev).cuda_stream
 
@@ -289,9 +312,14 @@ def main():
             if evs is not None:
                 a, b_ = evs.pop()
                 mla.profile_attention_events(a, b_)
-            mla.mla_decode(q, pools[r][rep], bt, seq[r], glob_arg, s.W, r, None, s.causal, s.scale, s.lse_base,
-                           max_seq_len=max_seq[r], out=outs[r], lse=lses[r], workspace=ws[r],
-                           cp_interleave=s.interleave)
+            if qsl_dev is not None:
+                mla.mla_decode_varlen(q, qsl_dev, pools[r][rep], bt, seq[r], glob_arg, s.W, r, s.causal, s.scale,
+                                      s.lse_base, max_q_len=s.Q, max_seq_len=max_seq[r], out=outs[r], lse=lses[r],
+                                      workspace=ws[r], cp_interleave=s.interleave)
+            else:
+                mla.mla_decode(q, pools[r][rep], bt, seq[r], glob_arg, s.W, r, None, s.causal, s.scale, s.lse_base,
+                               max_seq_len=max_seq[r], out=outs[r], lse=lses[r], workspace=ws[r],
+                               cp_interleave=s.interleave)
         if evs is not None:
             mla.profile_attention_events(None, None)
         if s.W > 1 and len(ranks) == s.W:
@@ -374,7 +402,8 @@ def main():
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": spec.name, "batch": s.B, "heads": s.H, "q_len": s.Q, "causal": s.causal,
+        "config": {"workload": spec.name + ("_varlen" if s.q_lens is not None else ""), "batch": s.B, "heads": s.H,
+                   "q_len": s.Q if s.q_lens is None else f"1..{s.Q} per request", "causal": s.causal,
                    "cp_world": s.W, "cp_interleave": s.interleave, "ranks": ranks, "block_size": s.block_size,
                    "kv_replicas": replicas},
         "tflops": round(tflops, 3), "kv_gbps": round(kv_gbps, 1),

@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "D_QK", "D_V", "PAD_SLOT_ID", "LSE_BASE_E", "LSE_BASE_2", "MLAError",
     "library_path", "load_library", "exported_symbols",
-    "mla_decode", "mla_decode_workspace_size", "mla_merge_lse", "cp_local_slot", "kv_write",
+    "mla_decode", "mla_decode_varlen", "mla_decode_workspace_size", "mla_merge_lse", "cp_local_slot", "kv_write",
     "profile_attention_events",
 ]
 
@@ -51,6 +51,8 @@ _SIGNATURES = [
     ("mla_kv_write", _I, [_P, _P, ctypes.c_int64, _P, _I, _I, _P]),
     ("mla_decode_interleaved", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                                     ctypes.c_float, _I, _P, _P, _P, ctypes.c_size_t, _P]),
+    ("mla_decode_varlen", _I, [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                               ctypes.c_float, _I, _P, _P, _P, ctypes.c_size_t, _P]),
 ]
 
 
@@ -262,4 +264,73 @@ def kv_write(kv_new: torch.Tensor, slots: torch.Tensor, kv_cache: torch.Tensor) 
     _check(lib.mla_kv_write(kv_new.data_ptr(), slots.data_ptr(), int(n), kv_cache.data_ptr(),
                             int(kv_cache.shape[0]), int(kv_cache.shape[1]), _stream(kv_cache.device)))
     return kv_cache
+
+
+def mla_decode_varlen(q: torch.Tensor, query_start_loc: torch.Tensor, kv_cache: torch.Tensor,
+                      block_table: torch.Tensor, seq_lens: torch.Tensor,
+                      causal_seqlens_global: Optional[torch.Tensor] = None, cp_world: int = 1, cp_rank: int = 0,
+                      causal: bool = True, scale: Optional[float] = None, lse_base: str = "e", *,
+                      max_q_len: Optional[int] = None, max_seq_len: Optional[int] = None,
+                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, return_lse: bool = True, cp_interleave: int = 1
+                      ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """One rank's decode for requests with different query lengths: q [T, H, 576] bf16 packs the
+    requests' tokens, request b owning tokens query_start_loc[b] .. query_start_loc[b+1]-1.
+    Returns out [T, H, 512] bf16 and lse [T, H] float32.  max_q_len (the largest per-request
+    length) is read from query_start_loc with a host sync when not given."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16, 3)
+    T, H, Dq = q.shape
+    if Dq != D_QK:
+        raise ValueError(f"q last dim must be {D_QK}")
+    _need(query_start_loc, "query_start_loc", torch.int32, 1)
+    B = int(query_start_loc.shape[0]) - 1
+    if B < 0:
+        raise ValueError("query_start_loc must have B+1 entries")
+    _need(kv_cache, "kv_cache", torch.bfloat16, 3)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    if block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_table and seq_lens must have B rows")
+    if causal_seqlens_global is not None:
+        _need(causal_seqlens_global, "causal_seqlens_global", torch.int32, 1)
+        if causal_seqlens_global.shape[0] != B:
+            raise ValueError("causal_seqlens_global must have B entries")
+    if max_q_len is None:
+        max_q_len = int((query_start_loc[1:] - query_start_loc[:-1]).max().item()) if B > 0 else 1
+    max_q_len = max(int(max_q_len), 1)
+    num_blocks, bs = int(kv_cache.shape[0]), int(kv_cache.shape[1])
+    max_blocks = int(block_table.shape[1])
+    if max_seq_len is None:
+        max_seq_len = max_blocks * bs
+    if scale is None:
+        scale = 1.0 / math.sqrt(192.0)
+    base = {"e": LSE_BASE_E, "2": LSE_BASE_2}.get(str(lse_base))
+    if base is None:
+        raise ValueError("lse_base must be 'e' or '2'")
+    dev = q.device
+    if out is None:
+        out = torch.empty((T, H, D_V), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", torch.bfloat16, 3)
+        if tuple(out.shape) != (T, H, D_V):
+            raise ValueError("out must be [T, H, 512]")
+    if return_lse:
+        if lse is None:
+            lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        else:
+            _need(lse, "lse", torch.float32, 2)
+            if tuple(lse.shape) != (T, H):
+                raise ValueError("lse must be [T, H]")
+    ws_bytes = int(lib.mla_decode_workspace_size(max(B, 1), max_q_len, H, int(max_seq_len)))
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+    _check(lib.mla_decode_varlen(
+        q.data_ptr(), query_start_loc.data_ptr(), max_q_len, kv_cache.data_ptr(), block_table.data_ptr(),
+        seq_lens.data_ptr(), causal_seqlens_global.data_ptr() if causal_seqlens_global is not None else None,
+        B, H, num_blocks, bs, max_blocks, int(max_seq_len), int(cp_world), int(cp_rank), int(cp_interleave),
+        1 if causal else 0, float(scale), base, out.data_ptr(),
+        lse.data_ptr() if (return_lse and lse is not None) else None,
+        workspace.data_ptr(), int(workspace.numel()), _stream(dev)))
+    return out, (lse if return_lse else None)
 

@@ -50,7 +50,8 @@ struct DecodeArgs {
   const int32_t* bt;       // [B, max_blocks]
   const int32_t* seq_lens; // [B]
   const int32_t* glob;     // [B] or null
-  int B, Q, H, R;          // R = Q*H rows per request
+  const int32_t* qsl;      // [B+1] token offsets of the requests (varlen), or null: Q tokens each
+  int B, Q, H, R;          // Q: (largest) tokens per request, R = Q*H rows
   int num_blocks, bs, max_blocks;
   int bs_shift;            // log2(bs) when bs is a power of two, else -1
   int W, rank, causal;
@@ -81,14 +82,28 @@ __device__ __forceinline__ int64_t piece_slot(const DecodeArgs& a, int j, int bb
   return ((int64_t)j + bb) * a.n_rt + rt;
 }
 
-// Key count of the largest row (row j = q_len-1 has the longest prefix),
-// local length and global length of request b; zeros past B.
+// Query tokens of request b and the index of its first one: Q each, or
+// from the token offsets of a varlen batch.
+__device__ __forceinline__ void request_tokens(const DecodeArgs& a, int b, int& q_len, int& q_base) {
+  if (a.qsl) {
+    q_base = gload_i32(a.qsl + b);
+    q_len = gload_i32(a.qsl + b + 1) - q_base;
+  } else {
+    q_base = b * a.Q;
+    q_len = a.Q;
+  }
+}
+
+// Key count of the largest row (the last query row sees the whole global
+// length, whatever the query length), local length and global length of
+// request b; zeros past B and for a request without query tokens.
 __device__ __forceinline__ void request_info(const DecodeArgs& a, int b, int& nb, int& seq, int& tot) {
   nb = seq = tot = 0;
   if (b < a.B) {
     seq = gload_i32(a.seq_lens + b);
     tot = a.glob ? gload_i32(a.glob + b) : seq;
-    nb = row_bound(seq, tot, a.Q, a.Q - 1, a.W, a.rank, a.I, a.causal);
+    nb = row_bound(seq, tot, 1, 0, a.W, a.rank, a.I, a.causal);
+    if (a.qsl && gload_i32(a.qsl + b + 1) == gload_i32(a.qsl + b)) nb = 0;
   }
 }
 
@@ -392,6 +407,7 @@ struct M16State {
 
 struct M16Seg {
   int bb, rt, ka, kb, seq, tot, e_base, flags;
+  int q_len, q_base;  // the request's query tokens and its first token's index
 };
 
 // Ring position: segment s (with its descriptor), tile j (-1: the segment's
@@ -412,6 +428,8 @@ __device__ __forceinline__ void m16_load_seg(M16Cursor& c, const M16Seg* segs, i
   c.d.tot = __builtin_amdgcn_readfirstlane(d.tot);
   c.d.e_base = __builtin_amdgcn_readfirstlane(d.e_base);
   c.d.flags = __builtin_amdgcn_readfirstlane(d.flags);
+  c.d.q_len = __builtin_amdgcn_readfirstlane(d.q_len);
+  c.d.q_base = __builtin_amdgcn_readfirstlane(d.q_base);
   c.nt = (c.d.kb - c.d.ka + M16_TILE - 1) / M16_TILE;
   c.j = (c.d.flags & M16_SEG_FIRST) ? -1 : 0;
 }
@@ -439,7 +457,7 @@ __device__ __forceinline__ RingRows m16_item_rows(const DecodeArgs& a, const int
   if (c.s < nseg) {
     if (c.j < 0) {
       const int qr = c.d.rt * M16_ROWS + r;
-      if (r < M16_ROWS && qr < a.R) rowp = a.q + ((int64_t)c.d.bb * a.R + qr) * ROW_BYTES;
+      if (r < M16_ROWS && qr < c.d.q_len * a.H) rowp = a.q + ((int64_t)c.d.q_base * a.H + qr) * ROW_BYTES;
     } else {
       const int t = c.d.ka + M16_TILE * c.j + r;
       if (t < c.d.kb) {
@@ -624,7 +642,9 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
         for (int kk = 0; kk < M16_KSTEPS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 128 * kk);
         ring_issue_all(nxt, wave, sel_off);
         const int my_row = cc.d.rt * M16_ROWS + li;
-        nrow = my_row < a.R ? row_bound(cc.d.seq, cc.d.tot, a.Q, my_row / a.H, a.W, a.rank, a.I, a.causal) : 0;
+        nrow = my_row < cc.d.q_len * a.H
+                   ? row_bound(cc.d.seq, cc.d.tot, cc.d.q_len, my_row / a.H, a.W, a.rank, a.I, a.causal)
+                   : 0;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) st.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         st.m_ref = NEG_INF;
@@ -663,7 +683,13 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
 
   for_each_piece<M16_THREADS>(a, bund, tile, plan, [&](int bb, int rt, int k0, int k1, int seq, int tot) {
     // append the piece (rows [16 rt, 16 rt + 16) of request bb, keys [k0, k1))
-    // to the batch as one or more segments
+    // to the batch as one or more segments; a row tile past the request's
+    // rows (a shorter query in a varlen batch) has nothing to compute
+    int q_len, q_base;
+    request_tokens(a, bb, q_len, q_base);
+    q_len = __builtin_amdgcn_readfirstlane(q_len);
+    q_base = __builtin_amdgcn_readfirstlane(q_base);
+    if (rt * M16_ROWS >= q_len * a.H) return;
     const int32_t* btr = a.bt + (int64_t)bb * a.max_blocks;
     int flags = M16_SEG_FIRST;
     for (int ka = k0; ka < k1;) {
@@ -674,7 +700,8 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
       const int e0 = block_of(a, ka), e1 = block_of(a, kb - 1);
       for (int e = e0 + tid; e <= e1; e += M16_THREADS)
         bt_lds[nent + e - e0] = e < a.max_blocks ? gload_i32(btr + e) : -1;
-      if (tid == 0) segs[nseg] = M16Seg{bb, rt, ka, kb, seq, tot, nent - e0, flags | (kb == k1 ? M16_SEG_LAST : 0)};
+      if (tid == 0)
+        segs[nseg] = M16Seg{bb, rt, ka, kb, seq, tot, nent - e0, flags | (kb == k1 ? M16_SEG_LAST : 0), q_len, q_base};
       ++nseg;
       nent += e1 - e0 + 1;
       ka = kb;
@@ -931,11 +958,18 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
   const R128LaneOff lane_off = r128_lane_offsets(lane, wave);
 
   for_each_piece<R128_THREADS>(a, bund, tile, plan, [&](int bb, int rt, int k0, int k1, int seq, int tot) {
-    // ---- one piece: rows [128 rt, 128 rt + 128) of request bb, keys [k0, k1)
+    // ---- one piece: rows [128 rt, 128 rt + 128) of request bb, keys [k0, k1);
+    // a row tile past the request's rows (a shorter query in a varlen
+    // batch) has nothing to compute
+    int q_len, q_base;
+    request_tokens(a, bb, q_len, q_base);
+    q_len = __builtin_amdgcn_readfirstlane(q_len);
+    q_base = __builtin_amdgcn_readfirstlane(q_base);
+    if (rt * R128_ROWS >= q_len * a.H) return;
     const int32_t* btr = a.bt + (int64_t)bb * a.max_blocks;
     const int my_row = rt * R128_ROWS + wave * 32 + (lane & 31);
-    const bool row_ok = my_row < a.R;
-    const int nrow = row_ok ? row_bound(seq, tot, a.Q, my_row / a.H, a.W, a.rank, a.I, a.causal) : 0;
+    const bool row_ok = my_row < q_len * a.H;
+    const int nrow = row_ok ? row_bound(seq, tot, q_len, my_row / a.H, a.W, a.rank, a.I, a.causal) : 0;
     // the smallest bound over the wave's rows: tiles below it are unmasked
     int nmin = nrow;
 #pragma unroll
@@ -944,7 +978,7 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
     bf16x8 qf[R128_QREG];
     uint8_t* q_tail = q_tail_lds[wave];
     {
-      const uint8_t* qrow = a.q + ((int64_t)bb * a.R + (row_ok ? my_row : 0)) * ROW_BYTES + 16 * (lane >> 5);
+      const uint8_t* qrow = a.q + ((int64_t)q_base * a.H + (row_ok ? my_row : 0)) * ROW_BYTES + 16 * (lane >> 5);
 #pragma unroll
       for (int kk = 0; kk < R128_QREG; ++kk) qf[kk] = row_ok ? gload_bf16x8(qrow + 32 * kk) : zero_bf16x8();
 #pragma unroll
@@ -1065,7 +1099,9 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int row = threadIdx.x % ROWS;
   const int col0 = slice * SLICE + (threadIdx.x / ROWS) * PER;
   const int row_idx = rt * ROWS + row;
-  if (row_idx >= a.R) return;
+  int q_len, q_base;
+  request_tokens(a, b, q_len, q_base);
+  if (row_idx >= q_len * a.H) return;
   const int64_t T = a.prefix[a.B];
   const int64_t pb = a.prefix[b], pb1 = a.prefix[b + 1];
   const int nb = pb1 > pb ? (int)(pb1 - pb - a.ovh) : 0;
@@ -1075,7 +1111,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     j0 = range_owner(pb + a.ovh, T, a.nbund);
     j1 = range_owner(pb + a.ovh + nb - 1, T, a.nbund);
   }
-  const int64_t orow = (int64_t)b * a.R + row_idx;
+  const int64_t orow = (int64_t)q_base * a.H + row_idx;
   uint16_t* op = a.out + orow * D_V + col0;
   static_assert(PER % 4 == 0, "outputs are stored 4 columns at a time");
   // bundle j's slot of this group is (j + b) * n_rt + rt = j * n_rt + grp; a
@@ -1228,8 +1264,9 @@ extern "C" size_t mla_decode_workspace_size(int B, int q_len, int H, int max_seq
 
 namespace {
 
-int decode(const void* q, const void* kv_cache, const int32_t* block_table, const int32_t* seq_lens,
-           const int32_t* causal_seqlens_global, int B, int q_len, int H, int num_blocks, int block_size,
+int decode(const void* q, const int32_t* query_start_loc, const void* kv_cache, const int32_t* block_table,
+           const int32_t* seq_lens, const int32_t* causal_seqlens_global, int B, int q_len, int H, int num_blocks,
+           int block_size,
            int max_blocks, int max_seq_len, int cp_world, int cp_rank, int cp_interleave, int causal, float scale,
            int lse_base, void* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (B < 0 || q_len < 1 || H < 1 || num_blocks < 1 || block_size < 1 || max_blocks < 1 ||
@@ -1252,6 +1289,7 @@ int decode(const void* q, const void* kv_cache, const int32_t* block_table, cons
   a.bt = block_table;
   a.seq_lens = seq_lens;
   a.glob = causal_seqlens_global;
+  a.qsl = query_start_loc;
   a.B = B; a.Q = q_len; a.H = H; a.R = q_len * H;
   a.num_blocks = num_blocks; a.bs = block_size; a.max_blocks = max_blocks;
   a.bs_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
@@ -1290,9 +1328,9 @@ extern "C" int mla_decode(const void* q, const void* kv_cache, const int32_t* bl
                           int max_seq_len, int cp_world, int cp_rank, int causal, float scale,
                           int lse_base, void* out, float* lse, void* workspace, size_t workspace_bytes,
                           hipStream_t stream) {
-  return decode(q, kv_cache, block_table, seq_lens, causal_seqlens_global, B, q_len, H, num_blocks, block_size,
-                max_blocks, max_seq_len, cp_world, cp_rank, 1, causal, scale, lse_base, out, lse, workspace,
-                workspace_bytes, stream);
+  return decode(q, nullptr, kv_cache, block_table, seq_lens, causal_seqlens_global, B, q_len, H, num_blocks,
+                block_size, max_blocks, max_seq_len, cp_world, cp_rank, 1, causal, scale, lse_base, out, lse,
+                workspace, workspace_bytes, stream);
 }
 
 extern "C" int mla_decode_interleaved(const void* q, const void* kv_cache, const int32_t* block_table,
@@ -1301,7 +1339,19 @@ extern "C" int mla_decode_interleaved(const void* q, const void* kv_cache, const
                                       int max_seq_len, int cp_world, int cp_rank, int cp_interleave, int causal,
                                       float scale, int lse_base, void* out, float* lse, void* workspace,
                                       size_t workspace_bytes, hipStream_t stream) {
-  return decode(q, kv_cache, block_table, seq_lens, causal_seqlens_global, B, q_len, H, num_blocks, block_size,
-                max_blocks, max_seq_len, cp_world, cp_rank, cp_interleave, causal, scale, lse_base, out, lse,
-                workspace, workspace_bytes, stream);
+  return decode(q, nullptr, kv_cache, block_table, seq_lens, causal_seqlens_global, B, q_len, H, num_blocks,
+                block_size, max_blocks, max_seq_len, cp_world, cp_rank, cp_interleave, causal, scale, lse_base, out,
+                lse, workspace, workspace_bytes, stream);
+}
+
+extern "C" int mla_decode_varlen(const void* q, const int32_t* query_start_loc, int max_q_len, const void* kv_cache,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 const int32_t* causal_seqlens_global, int B, int H, int num_blocks, int block_size,
+                                 int max_blocks, int max_seq_len, int cp_world, int cp_rank, int cp_interleave,
+                                 int causal, float scale, int lse_base, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  if (B > 0 && query_start_loc == nullptr) return MLA_ERR_INVALID_ARG;
+  return decode(q, query_start_loc, kv_cache, block_table, seq_lens, causal_seqlens_global, B, max_q_len, H,
+                num_blocks, block_size, max_blocks, max_seq_len, cp_world, cp_rank, cp_interleave, causal, scale,
+                lse_base, out, lse, workspace, workspace_bytes, stream);
 }

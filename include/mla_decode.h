@@ -140,6 +140,34 @@ int mla_decode_interleaved(const void* q, const void* kv_cache, const int32_t* b
                            size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * mla_decode for a batch whose requests have different query lengths
+ * (varlen).  The query tokens of all requests are packed: request b owns
+ * tokens query_start_loc[b] .. query_start_loc[b+1]-1 of q, so its query
+ * length is q_len_b = query_start_loc[b+1] - query_start_loc[b] (0 allowed).
+ * Row j < q_len_b of request b applies the causal prefix with its own length
+ * (PR #52188 page, key source snippets: tot - (query_len - 1 - j); summary:
+ * the backends declare support for batches of different query lengths,
+ * supports_dcp_with_varlen):
+ *   G = max(tot_b - (q_len_b-1-j), 0) and the bound of mla_decode_interleaved;
+ * non-causal rows see seq_lens[b].  Outputs follow the tokens:
+ *   out[(query_start_loc[b]+j)*H + h, :], lse[(query_start_loc[b]+j)*H + h].
+ * Layouts: q [T, H, 576] bf16 and out [T, H, 512] bf16, lse [T, H] float32
+ * (T = query_start_loc[B]); query_start_loc [B+1] int32 in device memory,
+ * non-decreasing, starting at 0.  max_q_len (host) must be at least every
+ * q_len_b; it sizes the work split and the workspace:
+ *   mla_decode_workspace_size(B, max_q_len, H, max_seq_len).
+ * Device-side precondition (not checked): q_len_b <= max_q_len; rows of a
+ * longer request past max_q_len*H are left unwritten.
+ * Errors: those of mla_decode_interleaved (with q_len = max_q_len), and
+ * MLA_ERR_INVALID_ARG for a NULL query_start_loc when B > 0.
+ */
+int mla_decode_varlen(const void* q, const int32_t* query_start_loc, int max_q_len, const void* kv_cache,
+                      const int32_t* block_table, const int32_t* seq_lens, const int32_t* causal_seqlens_global,
+                      int B, int H, int num_blocks, int block_size, int max_blocks, int max_seq_len,
+                      int cp_world, int cp_rank, int cp_interleave, int causal, float scale, int lse_base,
+                      void* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Profiling aid (not part of the computation): for the calling host thread,
  * record `start` just before and `stop` just after the split-KV attention
  * kernel of each following mla_decode call, on that call's stream.  Pass two

@@ -22,7 +22,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["mla_status_string", "mla_decode_workspace_size", "mla_decode",
                                            "mla_merge_lse", "cp_local_slot", "mla_profile_attention_events",
-                                           "mla_kv_write", "mla_decode_interleaved"])
+                                           "mla_kv_write", "mla_decode_interleaved", "mla_decode_varlen"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -151,4 +151,13 @@ def _decode_il(I, **kw):
 def test_interleaved_decode_rejects_bad_arguments(I, kw):
     # every case fails a host check (the last ones also have a zero-size workspace)
     assert _decode_il(I, **kw) == 1
+
+
+def test_varlen_decode_needs_token_offsets():
+    lib = mla.load_library()
+    args = [1, None, 4, 1, 1, 1, None, 2, 16, 4, 64, 2, 128, 1, 0, 1, 1, ctypes.c_float(0.1), 0, 1, 1, 1, 1 << 40, None]
+    assert lib.mla_decode_varlen(*args) == 1          # no query_start_loc
+    args[1] = 1
+    args[2] = 0
+    assert lib.mla_decode_varlen(*args) == 1          # max_q_len < 1
 
