@@ -62,6 +62,20 @@ def owns(p: np.ndarray, W: int, r: int, interleave: int = 1) -> np.ndarray:
     return (np.asarray(p) // interleave) % W == r
 
 
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Decode 8-bit floats with 1 sign, 4 exponent (bias 7) and 3 mantissa bits
+    (the OCP E4M3 format, no infinities): exponent 0 is subnormal
+    (m/8 * 2^-6), the code with all exponent and mantissa bits set is NaN,
+    the largest value is 448."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    out = sign * mag
+    return np.where((e == 15) & ((c & 7) == 7), np.nan, out)
+
+
 def held_positions(seq_len: int, W: int, r: int, interleave: int = 1) -> np.ndarray:
     """Global positions of the local rows a rank holds, in order: the first
     seq_len positions it owns (local row t is the t-th of them).  By
@@ -127,7 +141,8 @@ def attend(q_rows: np.ndarray, kv_rows: np.ndarray, scale: float, base: str = "e
 def mla_decode(q_bits: np.ndarray, kv_rows: Callable[[int, np.ndarray], np.ndarray],
                seq_lens: Sequence[int], tot: Optional[Sequence[int]], W: int, r: int,
                causal: bool, scale: float, base: str = "e",
-               rows: Optional[Sequence[Tuple[int, int, int]]] = None, interleave: int = 1):
+               rows: Optional[Sequence[Tuple[int, int, int]]] = None, interleave: int = 1,
+               kv_scale: Optional[float] = None):
     """Oracle for one rank's decode call.
 
     q_bits:   [B, Q, H, 576] bf16 bits.
@@ -138,6 +153,10 @@ def mla_decode(q_bits: np.ndarray, kv_rows: Callable[[int, np.ndarray], np.ndarr
     rows:     optional list of (b, j, h) to compute; default all.
     interleave: the rank holds positions in segments of this many (1: every
               W-th position).
+    kv_scale: None for a bf16 cache; otherwise kv_rows returns 8-bit E4M3
+              codes and the key/value rows are their values times kv_scale
+              (one dequantisation scale for the latent cache, which is both
+              key and value).
     Returns (out [B*Q, H, 512], lse [B*Q, H]) as float64; rows not asked for
     are NaN.
     """
@@ -162,7 +181,8 @@ def mla_decode(q_bits: np.ndarray, kv_rows: Callable[[int, np.ndarray], np.ndarr
         key = (b, pos.size, int(pos[-1]) if pos.size else -1)
         if key not in cache:
             cache.clear()
-            cache[key] = bf16_bits_to_f64(kv_rows(b, pos))
+            raw = kv_rows(b, pos)
+            cache[key] = bf16_bits_to_f64(raw) if kv_scale is None else e4m3_to_f64(raw) * float(kv_scale)
         kv = cache[key]
         qr = bf16_bits_to_f64(q_bits[b, j, heads, :])
         o, l = attend(qr, kv, scale, base)

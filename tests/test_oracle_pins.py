@@ -197,6 +197,38 @@ def test_oracle_matches_pure_python_bruteforce():
                         np.testing.assert_allclose(o[b * s.Q + j, h], bo, rtol=0, atol=1e-12)
 
 
+# ---------------------------------------------------------------- FP8 cache
+
+def test_e4m3_decode_matches_torch_and_closed_forms():
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+    assert got[0x38] == 1.0 and got[0xB8] == -1.0 and got[0x7E] == 448.0
+    assert got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6 and np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+
+
+@pytest.mark.parametrize("kv_scale", [1.0, 0.25, 3.0])
+def test_fp8_cache_is_the_bf16_path_on_its_values(kv_scale):
+    # the oracle's FP8 branch equals its bf16 branch on the cache's values
+    # (torch decodes the codes; values times kv_scale are exact in bf16 for
+    # these scales), which pins the decoding and where the scale applies
+    wl8 = tiny(B=2, H=3, Q=3, W=2, causal=True, lengths=(9, 14), seed=23, kv_dtype="fp8", kv_scale=kv_scale)
+    s = wl8.spec
+
+    def rows_bf16(b, pos):
+        v = torch.from_numpy(wl8.global_rows(b, pos)).view(torch.float8_e4m3fn).float() * kv_scale
+        return v.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+    for r in range(2):
+        o8, l8 = oracle.mla_decode(wl8.q_bits, wl8.global_rows, wl8.seq_lens[r], wl8.tot, s.W, r, True, s.scale,
+                                   "e", kv_scale=kv_scale)
+        ob, lb = oracle.mla_decode(wl8.q_bits, rows_bf16, wl8.seq_lens[r], wl8.tot, s.W, r, True, s.scale, "e")
+        np.testing.assert_array_equal(o8, ob)
+        np.testing.assert_array_equal(l8, lb)
+
+
 # ---------------------------------------------------------------- varlen
 
 def tiny_varlen(q_lens, W=2, causal=True, lengths=(9, 14, 6), seed=17, I=1):

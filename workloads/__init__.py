@@ -56,6 +56,31 @@ def _normal_bits(seed_key: Sequence[int], shape) -> np.ndarray:
     return bf16_bits(rng.standard_normal(shape, dtype=np.float32))
 
 
+# the 127 non-negative finite values of the 8-bit E4M3 format (codes 0..126)
+_E4M3_POS = np.array([(m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+                      for e in range(16) for m in range(8)][:127])
+
+
+def e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """Round float values to 8-bit E4M3 codes: nearest value, ties to the even
+    code, magnitudes past 448 saturate to 448."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a), 1, 126)
+    lo = hi - 1
+    dlo, dhi = a - _E4M3_POS[lo], _E4M3_POS[hi] - a
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    return (pick | np.where(x < 0, 0x80, 0)).astype(np.uint8)
+
+
+def _normal_kv(spec, seed_key: Sequence[int], shape) -> np.ndarray:
+    """N(0,1) latent rows: bf16 bits, or E4M3 codes of value / kv_scale."""
+    if spec.kv_dtype == "fp8":
+        rng = np.random.default_rng(list(seed_key))
+        return e4m3_codes(rng.standard_normal(shape, dtype=np.float32) / spec.kv_scale)
+    return _normal_bits(seed_key, shape)
+
+
 @dataclass
 class Spec:
     """A synthetic workload.
@@ -75,6 +100,8 @@ class Spec:
     ranks: Sequence[int] = (0,)
     interleave: int = 1   # ranks hold segments of this many consecutive positions
     q_lens: Optional[Sequence[int]] = None  # per-request query lengths (varlen); Q is then their maximum
+    kv_dtype: str = "bf16"  # "bf16" or "fp8" (8-bit E4M3 codes of value / kv_scale)
+    kv_scale: float = 1.0
     block_size: int = 64
     scale: float = DEFAULT_SCALE
     lse_base: str = "e"
@@ -107,7 +134,7 @@ class Workload:
         """bf16 rows of request b at the given global positions (contiguous global view)."""
         W, I = self.spec.W, self.spec.interleave
         positions = np.asarray(positions, dtype=np.int64)
-        out = np.empty((positions.size, D_QK), dtype=np.uint16)
+        out = np.empty((positions.size, D_QK), dtype=np.uint8 if self.spec.kv_dtype == "fp8" else np.uint16)
         owner = (positions // I) % W
         local = (positions // (I * W)) * I + positions % I
         for r in np.unique(owner) if positions.size else []:
@@ -121,7 +148,7 @@ class Workload:
         """Whole contiguous global KV of request b (every rank's shard interleaved)."""
         W, I = self.spec.W, self.spec.interleave
         L = int(self.tot[b])
-        g = np.empty((L, D_QK), dtype=np.uint16)
+        g = np.empty((L, D_QK), dtype=np.uint8 if self.spec.kv_dtype == "fp8" else np.uint16)
         for r in range(W):
             g[_owned(L, W, r, I)] = self.shards[r][b]
         return g
@@ -146,9 +173,11 @@ def _lengths(spec: Spec) -> np.ndarray:
 
 def _fill_rows(spec: Spec, r: int, n_rows: int) -> np.ndarray:
     if spec.fill == "nan":
+        if spec.kv_dtype == "fp8":
+            return np.full((n_rows, D_QK), 0x7F, dtype=np.uint8)
         return np.full((n_rows, D_QK), BF16_NAN, dtype=np.uint16)
     # a fixed random pattern, tiled: N(0,1)-distributed filler for unused rows
-    pat = _normal_bits([spec.seed, 7777, r], (min(n_rows, 4096), D_QK))
+    pat = _normal_kv(spec, [spec.seed, 7777, r], (min(n_rows, 4096), D_QK))
     reps = -(-n_rows // pat.shape[0])
     return np.ascontiguousarray(np.tile(pat, (reps, 1))[:n_rows])
 
@@ -186,7 +215,7 @@ def build(spec: Spec, ranks: Optional[Sequence[int]] = None) -> Workload:
     for r in ranks:
         counts = [len(_owned(int(tot[b]), W, r, I)) for b in range(B)]
         with ThreadPoolExecutor(_THREADS) as ex:
-            shards[r] = list(ex.map(lambda b: _normal_bits([spec.seed, b, r, 0], (counts[b], D_QK)), range(B)))
+            shards[r] = list(ex.map(lambda b: _normal_kv(spec, [spec.seed, b, r, 0], (counts[b], D_QK)), range(B)))
         seq_lens[r] = np.asarray(counts, dtype=np.int32)
 
     # one block table shared by all ranks; sized for rank 0's (largest) shard
