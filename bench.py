@@ -32,6 +32,11 @@ HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2516.6    # 256 CU x 4096 flop/clk x 2.4 GHz, dense bf16
 FLOP_PER_KEY_ROW = 2 * 576 + 2 * 512   # QK^T (576-wide) + PV (512-wide) per (row, key)
 KV_ROW_BYTES = 576 * 2
+FP8_KV_SCALE = 1.0 / 64           # --fp8: codes of N(0,1) values / this scale (|value| < 7 stays below 448)
+
+
+def kv_row_bytes(s):
+    return 576 if s.kv_dtype == "fp8" else KV_ROW_BYTES
 
 
 def log(*a):
@@ -90,7 +95,7 @@ def rank_work(wl, r):
         seq = int(wl.seq_lens[r][b])
         tot = int(wl.tot[b]) if not s.global_is_null else seq
         nmax = row_keys(seq, tot, ql, ql - 1, s.W, r, s.causal, s.interleave) if ql else 0
-        kv += nmax * KV_ROW_BYTES
+        kv += nmax * kv_row_bytes(s)
         bt += -(-nmax // s.block_size) * 4
         for j in range(ql):
             flops += row_keys(seq, tot, ql, j, s.W, r, s.causal, s.interleave) * s.H * FLOP_PER_KEY_ROW
@@ -191,6 +196,7 @@ def cpu_baseline(wl, ranks, unit, budget_s=20.0):
     done_b, flops, kv = 0, 0, 0
     t0 = time.perf_counter()
     qls = q_lens_of(s)
+    kvs = s.kv_scale if s.kv_dtype == "fp8" else None
     for b in range(s.B):
         for r in ranks:
             seq = wl.seq_lens[r]
@@ -201,14 +207,14 @@ def cpu_baseline(wl, ranks, unit, budget_s=20.0):
                 one = np.array([0, ql], dtype=np.int32)
                 oracle.mla_decode_varlen(wl.q_tok[qsl[b]:qsl[b + 1]], one, lambda _b, pos: wl.global_rows(b, pos),
                                          seq[b:b + 1], None if tot is None else tot[b:b + 1], s.W, r, s.causal,
-                                         s.scale, s.lse_base, interleave=s.interleave)
+                                         s.scale, s.lse_base, interleave=s.interleave, kv_scale=kvs)
             else:
                 rows = [(b, j, h) for j in range(s.Q) for h in range(s.H)]
                 oracle.mla_decode(wl.q_bits, wl.global_rows, seq, tot, s.W, r, s.causal, s.scale, s.lse_base,
-                                  rows=rows, interleave=s.interleave)
+                                  rows=rows, interleave=s.interleave, kv_scale=kvs)
             sq = int(seq[b])
             tt = int(wl.tot[b]) if tot is not None else sq
-            kv += (row_keys(sq, tt, ql, ql - 1, s.W, r, s.causal, s.interleave) if ql else 0) * KV_ROW_BYTES
+            kv += (row_keys(sq, tt, ql, ql - 1, s.W, r, s.causal, s.interleave) if ql else 0) * kv_row_bytes(s)
             flops += sum(row_keys(sq, tt, ql, j, s.W, r, s.causal, s.interleave)
                          for j in range(ql)) * s.H * FLOP_PER_KEY_ROW
         done_b += 1
@@ -233,6 +239,8 @@ def main():
                     help="per-request query lengths uniform in [1, q_len] (seeded), through mla_decode_varlen")
     ap.add_argument("--interleave", type=int, default=1,
                     help="DCP interleave: ranks hold segments of this many positions (sharded workloads)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="FP8 (E4M3) latent cache with one dequantisation scale, through mla_decode_fp8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
     args = ap.parse_args()
@@ -258,7 +266,11 @@ def main():
     dev = torch.device("cuda:0")
     hip = Hip()
 
-    spec = WL.config(args.config, interleave=args.interleave)
+    if args.fp8 and args.varlen:
+        print("--fp8 and --varlen are separate entry points; pick one", file=sys.stderr)
+        sys.exit(2)
+    kv_kw = dict(kv_dtype="fp8", kv_scale=FP8_KV_SCALE) if args.fp8 else {}
+    spec = WL.config(args.config, interleave=args.interleave, **kv_kw)
     if args.varlen:
         ql = np.random.default_rng([spec.seed, 31337]).integers(1, spec.Q, size=spec.B, endpoint=True)
         ql[0] = spec.Q  # the largest length stays the workload's q_len
@@ -279,7 +291,13 @@ def main():
     T = sum(q_lens_of(s))
     bt = torch.from_numpy(wl.block_table).to(dev)
     tot = torch.from_numpy(wl.tot.astype(np.int32)).to(dev)
-    pools = {r: [bf16(wl.pools[r])] for r in ranks}
+    def kv_dev(pool):
+        if pool.dtype == np.uint8:  # E4M3 codes
+            return torch.from_numpy(np.ascontiguousarray(pool)).to(dev)
+        return bf16(pool)
+
+    fp8_kw = dict(kv_scale=s.kv_scale) if s.kv_dtype == "fp8" else {}
+    pools = {r: [kv_dev(wl.pools[r])] for r in ranks}
     for r in ranks:
         for _ in range(replicas - 1):
             pools[r].append(pools[r][0].clone())
@@ -319,7 +337,7 @@ def main():
             else:
                 mla.mla_decode(q, pools[r][rep], bt, seq[r], glob_arg, s.W, r, None, s.causal, s.scale, s.lse_base,
                                max_seq_len=max_seq[r], out=outs[r], lse=lses[r], workspace=ws[r],
-                               cp_interleave=s.interleave)
+                               cp_interleave=s.interleave, **fp8_kw)
         if evs is not None:
             mla.profile_attention_events(None, None)
         if s.W > 1 and len(ranks) == s.W:
@@ -373,7 +391,7 @@ def main():
         unit, value = "TFLOP/s", tflops
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     traffic = None
-    tfile = os.path.join(ROOT, "profiles", f"traffic_config{args.config}.json")
+    tfile = os.path.join(ROOT, "profiles", f"traffic_config{args.config}{'_fp8' if args.fp8 else ''}.json")
     if os.path.exists(tfile):
         t = json.load(open(tfile))
         if t.get("source_hash") == source_hash():
@@ -391,8 +409,10 @@ def main():
             t = (p // (I * s.W)) * I + p % I  # the rank's local row of p
             if p >= 0 and (p // I) % s.W == r0 and t < len(wl.shards[r0][b]):
                 rows_np[b, i] = wl.shards[r0][b][t]
-    rows0 = bf16(rows_np)
-    kvw = kv_write_rates(torch, mla, hip, stream, dev, (rows0, slots0, pools[r0][0]))
+    if s.kv_dtype == "fp8":
+        kvw = None  # mla_kv_write stores bf16 rows; an FP8 cache is written by a quantising store, not built
+    else:
+        kvw = kv_write_rates(torch, mla, hip, stream, dev, (bf16(rows_np), slots0, pools[r0][0]))
     log("achievable peaks: 1 GiB copy, 8192^3 bf16 GEMM (torch)")
     peaks = measured_peaks(torch, hip, stream, dev)
     meas = peaks["hbm_copy_GBps"] if mem_bound else peaks["bf16_gemm_TFLOPs"]
@@ -402,10 +422,11 @@ def main():
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": spec.name + ("_varlen" if s.q_lens is not None else ""), "batch": s.B, "heads": s.H,
+        "config": {"workload": spec.name + ("_varlen" if s.q_lens is not None else "")
+                   + ("_fp8kv" if s.kv_dtype == "fp8" else ""), "batch": s.B, "heads": s.H,
                    "q_len": s.Q if s.q_lens is None else f"1..{s.Q} per request", "causal": s.causal,
                    "cp_world": s.W, "cp_interleave": s.interleave, "ranks": ranks, "block_size": s.block_size,
-                   "kv_replicas": replicas},
+                   "kv_replicas": replicas, "kv_cache": "fp8_e4m3" if s.kv_dtype == "fp8" else "bf16"},
         "tflops": round(tflops, 3), "kv_gbps": round(kv_gbps, 1),
         "alg_bytes_per_step": int(step_alg_bytes), "flops_per_step": int(step_flops),
         "attention_kernel_ms": round(avg_attn_ms, 5), "source_hash": source_hash(),

@@ -53,7 +53,12 @@ _SIGNATURES = [
                                     ctypes.c_float, _I, _P, _P, _P, ctypes.c_size_t, _P]),
     ("mla_decode_varlen", _I, [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                                ctypes.c_float, _I, _P, _P, _P, ctypes.c_size_t, _P]),
+    ("mla_decode_fp8", _I, [_P, _P, ctypes.c_float, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                            ctypes.c_float, _I, _P, _P, _P, ctypes.c_size_t, _P]),
 ]
+
+# dtypes accepted for an FP8 (E4M3) cache: torch's OCP E4M3 type or raw codes
+_FP8_KV_DTYPES = tuple(t for t in (getattr(torch, "float8_e4m3fn", None), torch.uint8) if t is not None)
 
 
 class MLAError(RuntimeError):
@@ -126,11 +131,13 @@ def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
                q_len: Optional[int] = None, causal: bool = True, scale: Optional[float] = None,
                lse_base: str = "e", *, max_seq_len: Optional[int] = None,
                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-               workspace: Optional[torch.Tensor] = None, return_lse: bool = True, cp_interleave: int = 1
-               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+               workspace: Optional[torch.Tensor] = None, return_lse: bool = True, cp_interleave: int = 1,
+               kv_scale: Optional[float] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """One rank's paged MLA decode.  q: [B, q_len, H, 576] (or [B*q_len, H, 576]
-    with q_len given) bf16; kv_cache: [num_blocks, block_size, 576] bf16.
-    Returns out [B*q_len, H, 512] bf16 and lse [B*q_len, H] float32."""
+    with q_len given) bf16; kv_cache: [num_blocks, block_size, 576] bf16, or
+    E4M3 codes (float8_e4m3fn or uint8) with kv_scale, the one dequantisation
+    factor of the whole cache.  Returns out [B*q_len, H, 512] bf16 and lse
+    [B*q_len, H] float32."""
     lib = load_library()
     if q.dim() == 3:
         if q_len is None:
@@ -144,7 +151,13 @@ def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
         raise ValueError(f"q_len={q_len} does not match q.shape[1]={Q}")
     if Dq != D_QK:
         raise ValueError(f"q last dim must be {D_QK}")
-    _need(kv_cache, "kv_cache", torch.bfloat16, 3)
+    fp8 = kv_scale is not None
+    if fp8:
+        if kv_cache.dtype not in _FP8_KV_DTYPES:
+            raise ValueError("an FP8 cache (kv_scale given) must be float8_e4m3fn or uint8 codes")
+        _need(kv_cache, "kv_cache", kv_cache.dtype, 3)
+    else:
+        _need(kv_cache, "kv_cache", torch.bfloat16, 3)
     if kv_cache.shape[2] != D_QK:
         raise ValueError(f"kv_cache last dim must be {D_QK}")
     _need(block_table, "block_table", torch.int32, 2)
@@ -187,7 +200,9 @@ def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
     tail = (1 if causal else 0, float(scale), base, out.data_ptr(),
             lse.data_ptr() if (return_lse and lse is not None) else None,
             workspace.data_ptr(), int(workspace.numel()), _stream(dev))
-    if cp_interleave == 1:
+    if fp8:
+        _check(lib.mla_decode_fp8(head[0], head[1], float(kv_scale), *head[2:], int(cp_interleave), *tail))
+    elif cp_interleave == 1:
         _check(lib.mla_decode(*head, *tail))
     else:
         _check(lib.mla_decode_interleaved(*head, int(cp_interleave), *tail))

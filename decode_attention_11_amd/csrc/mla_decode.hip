@@ -56,7 +56,9 @@ struct DecodeArgs {
   int bs_shift;            // log2(bs) when bs is a power of two, else -1
   int W, rank, causal;
   int I;                   // cp_interleave: positions go to ranks in segments of I
-  float scale_log2;        // softmax scale times log2(e)
+  float scale_log2;        // softmax scale (times the FP8 cache scale) times log2(e)
+  float out_scale;         // output factor: the FP8 cache scale, 1 for bf16
+  int kv_fp8;              // KV rows are 576 E4M3 bytes instead of 576 bf16
   int lse_base;
   int n_rt;                // row tiles per request
   int ovh;                 // work units charged per piece on top of its keys
@@ -391,6 +393,11 @@ constexpr int M16_HALF = 16 * ROW_BYTES;           // bytes of a 16-key half of 
 constexpr int M16_STAGE = RING_STAGE;              // 36 KiB
 constexpr int M16_NS = 4;                          // ring stages
 constexpr int M16_DMA_PER_WAVE = RING_DMA_PER_WAVE;
+// FP8 cache: a ring item is 18 KiB (32 keys x 576 E4M3 bytes, or the 16
+// bf16 query rows), 18 one-KiB loads: waves 0, 1 issue 5, waves 2, 3 issue 4
+constexpr int M16F8_RAW = 18 * 1024;
+constexpr int M16F8_NS = 5;
+constexpr int M16F8_ROW = D_QK;  // bytes of an E4M3 row
 constexpr int M16_KSTEPS = 9;                      // 32-dim MFMA steps per wave (half of 576)
 constexpr int M16_BT_WIN = 1024;                   // block-table entries held in LDS per batch
 constexpr int M16_MAXSEG = 16;                     // segments per batch
@@ -473,9 +480,10 @@ __device__ __forceinline__ RingRows m16_item_rows(const DecodeArgs& a, const int
 // One 32-key tile: this wave's quarter of S^T, the exchange of the partial
 // tiles, online softmax with a lazily moved reference max, then this wave's
 // quarter of O^T += V^T P^T.  qf holds the wave's 9 k-steps of Q^T.
+template <class Issue>
 __device__ __forceinline__ void m16_compute(M16State& st, const bf16x8 (&qf)[M16_KSTEPS], const uint8_t* stage,
                                             uint8_t* xchg, float scale_log2, int ts, int k1, int nrow, int lane,
-                                            int wave, const RingRows& nxt, const int (&sel_off)[RING_DMA_PER_WAVE]) {
+                                            int wave, Issue&& issue) {
   const int li = lane & 15, g = lane >> 4;
   // S^T[key][row] of half wave%2: lane (li, g) gets keys 4g+e for row li;
   // the K fragment of k-step kk = 2k + wave/2 is logical chunk 4kk + g of key
@@ -492,7 +500,7 @@ __device__ __forceinline__ void m16_compute(M16State& st, const bf16x8 (&qf)[M16
   // barrier would stall the waves behind the address unit)
 #pragma unroll
   for (int kk = 0; kk < M16_KSTEPS; ++kk) {
-    ring_issue_one(nxt, kk, wave, sel_off);
+    issue(kk);
     if (kk & 1)
       sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[kk], sb, 0, 0, 0);
     else
@@ -576,8 +584,86 @@ __device__ __forceinline__ void m16_compute(M16State& st, const bf16x8 (&qf)[M16
   }
 }
 
+// ---- FP8 cache: ring items land as raw bytes and K items are widened to
+// bf16 (exactly: every E4M3 value is a bf16 value) into the swizzled layout
+// the computation reads.
+// What ring item c is, for the per-lane addresses of its 18 loads: a Q item
+// (q points at its first query row, qrows rows are real), a key tile (keys
+// ts .. ts+31, real below kb), or past the end (zero rows).
+struct F8Item {
+  const uint8_t* q;
+  int qrows;
+  int ts, kb, e_base;
+  int kind;  // 0 past the end, 1 query rows, 2 key tile
+  uint32_t stage_lds;
+};
+
+__device__ __forceinline__ F8Item m16f8_item(const DecodeArgs& a, int nseg, const M16Cursor& c, uint32_t stage_lds) {
+  F8Item d{nullptr, 0, 0, 0, 0, 0, stage_lds};
+  if (c.s < nseg) {
+    if (c.j < 0) {
+      d.kind = 1;
+      d.q = a.q + ((int64_t)c.d.q_base * a.H + c.d.rt * M16_ROWS) * ROW_BYTES;
+      d.qrows = min(M16_ROWS, c.d.q_len * a.H - c.d.rt * M16_ROWS);
+    } else {
+      d.kind = 2;
+      d.ts = c.d.ka + M16_TILE * c.j;
+      d.kb = c.d.kb;
+      d.e_base = c.d.e_base;
+    }
+  }
+  return d;
+}
+
+// Load g (0..17) of item d: lane l fills item byte 1024 g + 16 l (a key row
+// is 576 bytes, a query row 1152; 16-byte chunks never straddle rows).
+__device__ __forceinline__ void m16f8_issue(const DecodeArgs& a, const int* bt_lds, const F8Item& d, int g,
+                                            int lane) {
+  const int b = 1024 * g + 16 * lane;
+  const uint8_t* zero = reinterpret_cast<const uint8_t*>(kZeroRow);
+  const uint8_t* p = zero + (b % M16F8_ROW);
+  if (d.kind == 2) {
+    const int row = b / M16F8_ROW, off = b - row * M16F8_ROW;
+    const int t = d.ts + row;
+    if (t < d.kb) {
+      const int vb = block_of(a, t);
+      const int blk = bt_lds[d.e_base + vb];
+      if ((unsigned)blk < (unsigned)a.num_blocks)
+        p = a.kv + ((int64_t)blk * a.bs + (t - vb * a.bs)) * M16F8_ROW + off;
+    }
+  } else if (d.kind == 1) {
+    const int row = b / ROW_BYTES, off = b - row * ROW_BYTES;
+    if (row < d.qrows) p = d.q + (int64_t)row * ROW_BYTES + off;
+  }
+  asm volatile("" : "+v"(p));
+  dma16(p, d.stage_lds + 1024 * g);
+}
+
+// Widen a key tile: bf16 chunk k (8 values) of row r comes from E4M3 bytes
+// 576 r + 8 k of the raw item and goes to chunk k of row r of the swizzled
+// stage layout; consecutive threads take consecutive chunks, so both the
+// 8-byte reads and the 16-byte writes are free of bank conflicts.
+__device__ __forceinline__ void m16f8_widen(const uint8_t* raw, uint8_t* stage, int tid) {
+#pragma unroll
+  for (int i = 0; i < (RING_TILE * D_QK / 8) / M16_THREADS; ++i) {
+    const int c = tid + M16_THREADS * i;
+    const int row = c / (D_QK / 8), k = c - (D_QK / 8) * row;
+    const uint2 v = *reinterpret_cast<const uint2*>(raw + M16F8_ROW * row + 8 * k);
+    const uint4 o = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true))};
+    *reinterpret_cast<uint4*>(stage + ROW_BYTES * row + 16 * ((k & ~7) | ((k ^ ring_swz(row)) & 7))) = o;
+  }
+}
+
+template <bool F8>
 __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[M16_NS * M16_STAGE];
+  // bf16 cache: NS stages of 36 KiB.  FP8 cache: NS_F8 raw stages of 18 KiB
+  // and one bf16 stage the computation reads.
+  constexpr int NS = F8 ? M16F8_NS : M16_NS;
+  constexpr int RAW = F8 ? M16F8_RAW : M16_STAGE;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * RAW + (F8 ? M16_STAGE : 0)];
   __shared__ __attribute__((aligned(16))) uint8_t xchg[4 * 1024];
   __shared__ int bt_lds[M16_BT_WIN];
   __shared__ M16Seg segs[M16_MAXSEG];
@@ -591,7 +677,18 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
   const int bund = blockIdx.x / a.n_rt, tile = blockIdx.x - bund * a.n_rt;
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
   int sel_off[RING_DMA_PER_WAVE];  // per-lane constants of this wave's ring loads
-  ring_dma_offsets(sel_off, wave, lane);
+  if constexpr (!F8) ring_dma_offsets(sel_off, wave, lane);
+  uint8_t* const cstage = ring + NS * RAW;  // FP8: the widened tile
+  // FP8: load g of an item is issued by wave g % 4 (waves 0, 1: 5 loads,
+  // waves 2, 3: 4), at its m-th issue slot for g = wave + 4 m
+  auto f8_issue = [&](const F8Item& d, int m) __attribute__((always_inline)) {
+    const int gl = wave + 4 * m;
+    if (gl < M16F8_RAW / 1024) m16f8_issue(a, bt_lds, d, gl, lane);
+  };
+  auto f8_issue_all = [&](const F8Item& d) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < 5; ++m) f8_issue(d, m);
+  };
 
   // state of the group being computed; it survives batch boundaries
   bf16x8 qf[M16_KSTEPS];
@@ -619,28 +716,48 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
     }
     M16Cursor cc = ci;
 #pragma unroll
-    for (int p = 0; p < M16_NS - 1; ++p) {
-      ring_issue_all(m16_item_rows(a, bt_lds, nseg, ci, ring_lds + p * M16_STAGE, wave, lane), wave, sel_off);
+    for (int p = 0; p < NS - 1; ++p) {
+      if constexpr (F8)
+        f8_issue_all(m16f8_item(a, nseg, ci, ring_lds + p * RAW));
+      else
+        ring_issue_all(m16_item_rows(a, bt_lds, nseg, ci, ring_lds + p * RAW, wave, lane), wave, sel_off);
       m16_advance(ci, segs, nseg);
     }
     for (int it = 0; it < n_items; ++it) {
       // item it landed (items it+1 .. it+NS-2 may still be in flight), and
       // after the barrier every wave is done with item it-1 ...
-      WAIT_VMCNT(M16_DMA_PER_WAVE * (M16_NS - 2));
+      if constexpr (F8) {
+        if (wave < 2)
+          WAIT_VMCNT(5 * (NS - 2));
+        else
+          WAIT_VMCNT(4 * (NS - 2));
+      } else {
+        WAIT_VMCNT(M16_DMA_PER_WAVE * (NS - 2));
+      }
       __syncthreads();
       // ... so its stage can take item it+NS-1
-      const RingRows nxt =
-          m16_item_rows(a, bt_lds, nseg, ci, ring_lds + ((it + M16_NS - 1) % M16_NS) * M16_STAGE, wave, lane);
+      const uint32_t nxt_lds = ring_lds + ((it + NS - 1) % NS) * RAW;
+      RingRows nxt;
+      F8Item nxt8;
+      if constexpr (F8)
+        nxt8 = m16f8_item(a, nseg, ci, nxt_lds);
+      else
+        nxt = m16_item_rows(a, bt_lds, nseg, ci, nxt_lds, wave, lane);
       m16_advance(ci, segs, nseg);
-      const uint8_t* stage = ring + (it % M16_NS) * M16_STAGE;
+      const uint8_t* stage = ring + (it % NS) * RAW;
       if (cc.j < 0) {
         // Q item: this wave's k-steps of Q^T (lane (li, g): dims
         // 32kk + 8g .. +7 of row li, kk = 2k + wave/2; stored like key rows
-        // 0..15) into registers, and a fresh state
-        const uint8_t* qp = stage + ROW_BYTES * li + 16 * ((4 * (wave >> 1) + g) ^ ring_swz(li));
+        // 0..15, or plainly row after row for an FP8 cache) into registers,
+        // and a fresh state
+        const uint8_t* qp = F8 ? stage + ROW_BYTES * li + 16 * (4 * (wave >> 1) + g)
+                               : stage + ROW_BYTES * li + 16 * ((4 * (wave >> 1) + g) ^ ring_swz(li));
 #pragma unroll
         for (int kk = 0; kk < M16_KSTEPS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 128 * kk);
-        ring_issue_all(nxt, wave, sel_off);
+        if constexpr (F8)
+          f8_issue_all(nxt8);
+        else
+          ring_issue_all(nxt, wave, sel_off);
         const int my_row = cc.d.rt * M16_ROWS + li;
         nrow = my_row < cc.d.q_len * a.H
                    ? row_bound(cc.d.seq, cc.d.tot, cc.d.q_len, my_row / a.H, a.W, a.rank, a.I, a.causal)
@@ -651,8 +768,19 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
         st.l_part = 0.f;
         st.l_out = 0.f;
       } else {
-        m16_compute(st, qf, stage, xchg, a.scale_log2, cc.d.ka + M16_TILE * cc.j, cc.d.kb, nrow, lane, wave, nxt,
-                    sel_off);
+        if constexpr (F8) {
+          // widen the tile; the barrier at the top of this iteration ended
+          // every read of the previous one
+          m16f8_widen(stage, cstage, tid);
+          __syncthreads();
+          m16_compute(st, qf, cstage, xchg, a.scale_log2, cc.d.ka + M16_TILE * cc.j, cc.d.kb, nrow, lane, wave,
+                      [&](int kk) __attribute__((always_inline)) {
+                        if (kk < 5) f8_issue(nxt8, kk);
+                      });
+        } else {
+          m16_compute(st, qf, stage, xchg, a.scale_log2, cc.d.ka + M16_TILE * cc.j, cc.d.kb, nrow, lane, wave,
+                      [&](int kk) __attribute__((always_inline)) { ring_issue_one(nxt, kk, wave, sel_off); });
+        }
         if (cc.j == cc.nt - 1 && (cc.d.flags & M16_SEG_LAST)) {
           // partial slot: wave w's O^T tiles T = 8w + mt in the accumulator
           // layout [T][lane][4] (one 16-byte store per lane and tile), then
@@ -1172,7 +1300,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     if (a.lse && slice == 0 && threadIdx.x < ROWS) a.lse[orow] = NEG_INF;
     return;
   }
-  const float inv = 1.f / Lo;
+  const float inv = a.out_scale / Lo;  // the FP8 cache scale of V (1 for bf16)
 #pragma unroll
   for (int c0 = 0; c0 < PER; c0 += 4)
     *reinterpret_cast<bf16x4*>(op + c0) = to_bf16x4(acc[c0] * inv, acc[c0 + 1] * inv, acc[c0 + 2] * inv,
@@ -1268,19 +1396,21 @@ int decode(const void* q, const int32_t* query_start_loc, const void* kv_cache, 
            const int32_t* seq_lens, const int32_t* causal_seqlens_global, int B, int q_len, int H, int num_blocks,
            int block_size,
            int max_blocks, int max_seq_len, int cp_world, int cp_rank, int cp_interleave, int causal, float scale,
-           int lse_base, void* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+           int lse_base, int kv_fp8, float kv_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+           hipStream_t stream) {
   if (B < 0 || q_len < 1 || H < 1 || num_blocks < 1 || block_size < 1 || max_blocks < 1 ||
       max_seq_len < 0 || cp_world < 1 || cp_rank < 0 || cp_rank >= cp_world || cp_interleave < 1 ||
       (int64_t)cp_interleave * cp_world > (1 << 30) ||
       (causal != 0 && causal != 1) || (lse_base != MLA_LSE_BASE_E && lse_base != MLA_LSE_BASE_2) ||
-      !std::isfinite(scale))
+      !std::isfinite(scale) || !(std::isfinite(kv_scale) && kv_scale > 0.f))
     return MLA_ERR_INVALID_ARG;
   if ((int64_t)q_len * H > (1 << 24)) return MLA_ERR_INVALID_ARG;
   if (causal && cp_world > 1 && causal_seqlens_global == nullptr) return MLA_ERR_INVALID_ARG;
   if (B == 0) return MLA_OK;
   if (!q || !kv_cache || !block_table || !seq_lens || !out) return MLA_ERR_INVALID_ARG;
   const bool pow2_bs = (block_size & (block_size - 1)) == 0;
-  const Plan p = make_plan(B, q_len, H, max_seq_len, device_cu_count(), pow2_bs);
+  // an FP8 cache runs on the 16-row kernel only (row tiles of any count)
+  const Plan p = make_plan(B, q_len, H, max_seq_len, device_cu_count(), pow2_bs && !kv_fp8);
   if (workspace_bytes < p.bytes || workspace == nullptr) return MLA_ERR_INVALID_ARG;
 
   DecodeArgs a{};
@@ -1295,7 +1425,9 @@ int decode(const void* q, const int32_t* query_start_loc, const void* kv_cache, 
   a.bs_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
   a.W = cp_world; a.rank = cp_rank; a.causal = causal;
   a.I = cp_interleave;
-  a.scale_log2 = scale * LOG2E;
+  a.scale_log2 = scale * kv_scale * LOG2E;
+  a.out_scale = kv_scale;
+  a.kv_fp8 = kv_fp8;
   a.lse_base = lse_base;
   a.n_rt = p.n_rt;
   a.ovh = p.ovh;
@@ -1307,8 +1439,10 @@ int decode(const void* q, const int32_t* query_start_loc, const void* kv_cache, 
   a.lse = lse;
 
   if (tl_prof_start) (void)hipEventRecord(tl_prof_start, stream);
-  if (p.rows_tile == M16_ROWS)
-    hipLaunchKernelGGL(attn_m16_kernel, dim3(p.G), dim3(M16_THREADS), 0, stream, a);
+  if (kv_fp8)
+    hipLaunchKernelGGL(attn_m16_kernel<true>, dim3(p.G), dim3(M16_THREADS), 0, stream, a);
+  else if (p.rows_tile == M16_ROWS)
+    hipLaunchKernelGGL(attn_m16_kernel<false>, dim3(p.G), dim3(M16_THREADS), 0, stream, a);
   else
     hipLaunchKernelGGL(attn_r128_kernel, dim3(p.G), dim3(R128_THREADS), 0, stream, a);
   if (tl_prof_stop) (void)hipEventRecord(tl_prof_stop, stream);
@@ -1329,8 +1463,8 @@ extern "C" int mla_decode(const void* q, const void* kv_cache, const int32_t* bl
                           int lse_base, void* out, float* lse, void* workspace, size_t workspace_bytes,
                           hipStream_t stream) {
   return decode(q, nullptr, kv_cache, block_table, seq_lens, causal_seqlens_global, B, q_len, H, num_blocks,
-                block_size, max_blocks, max_seq_len, cp_world, cp_rank, 1, causal, scale, lse_base, out, lse,
-                workspace, workspace_bytes, stream);
+                block_size, max_blocks, max_seq_len, cp_world, cp_rank, 1, causal, scale, lse_base, 0, 1.f, out,
+                lse, workspace, workspace_bytes, stream);
 }
 
 extern "C" int mla_decode_interleaved(const void* q, const void* kv_cache, const int32_t* block_table,
@@ -1340,8 +1474,8 @@ extern "C" int mla_decode_interleaved(const void* q, const void* kv_cache, const
                                       float scale, int lse_base, void* out, float* lse, void* workspace,
                                       size_t workspace_bytes, hipStream_t stream) {
   return decode(q, nullptr, kv_cache, block_table, seq_lens, causal_seqlens_global, B, q_len, H, num_blocks,
-                block_size, max_blocks, max_seq_len, cp_world, cp_rank, cp_interleave, causal, scale, lse_base, out,
-                lse, workspace, workspace_bytes, stream);
+                block_size, max_blocks, max_seq_len, cp_world, cp_rank, cp_interleave, causal, scale, lse_base, 0,
+                1.f, out, lse, workspace, workspace_bytes, stream);
 }
 
 extern "C" int mla_decode_varlen(const void* q, const int32_t* query_start_loc, int max_q_len, const void* kv_cache,
@@ -1353,5 +1487,15 @@ extern "C" int mla_decode_varlen(const void* q, const int32_t* query_start_loc, 
   if (B > 0 && query_start_loc == nullptr) return MLA_ERR_INVALID_ARG;
   return decode(q, query_start_loc, kv_cache, block_table, seq_lens, causal_seqlens_global, B, max_q_len, H,
                 num_blocks, block_size, max_blocks, max_seq_len, cp_world, cp_rank, cp_interleave, causal, scale,
-                lse_base, out, lse, workspace, workspace_bytes, stream);
+                lse_base, 0, 1.f, out, lse, workspace, workspace_bytes, stream);
+}
+
+extern "C" int mla_decode_fp8(const void* q, const void* kv_cache, float kv_scale, const int32_t* block_table,
+                              const int32_t* seq_lens, const int32_t* causal_seqlens_global, int B, int q_len, int H,
+                              int num_blocks, int block_size, int max_blocks, int max_seq_len, int cp_world,
+                              int cp_rank, int cp_interleave, int causal, float scale, int lse_base, void* out,
+                              float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode(q, nullptr, kv_cache, block_table, seq_lens, causal_seqlens_global, B, q_len, H, num_blocks,
+                block_size, max_blocks, max_seq_len, cp_world, cp_rank, cp_interleave, causal, scale, lse_base, 1,
+                kv_scale, out, lse, workspace, workspace_bytes, stream);
 }

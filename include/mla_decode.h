@@ -168,6 +168,27 @@ int mla_decode_varlen(const void* q, const int32_t* query_start_loc, int max_q_l
                       void* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * mla_decode_interleaved over an FP8 latent cache (PR #54012 page, key
+ * source snippets: the backend's cache dtype and its bmm1/bmm2 scales, and
+ * the output scale handed to the decode kernel).  kv_cache holds
+ * [num_blocks, block_size, 576] bytes, each an E4M3 code (OCP 8-bit float:
+ * 1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, 0x7f
+ * and 0xff are NaN, largest value 448); the key/value row is each code's
+ * value times kv_scale, one factor for the whole cache.  Scores are
+ * scale * q . (kv_scale * code), the output is the softmax-weighted sum of
+ * the dequantised value rows, and the LSE is that of the scaled scores.  The
+ * query, output, LSE, workspace and every other argument are those of
+ * mla_decode_interleaved (its workspace size query applies unchanged).
+ * Errors: those of mla_decode_interleaved, and MLA_ERR_INVALID_ARG for a
+ * kv_scale that is not finite and positive.
+ */
+int mla_decode_fp8(const void* q, const void* kv_cache, float kv_scale, const int32_t* block_table,
+                   const int32_t* seq_lens, const int32_t* causal_seqlens_global, int B, int q_len, int H,
+                   int num_blocks, int block_size, int max_blocks, int max_seq_len, int cp_world, int cp_rank,
+                   int cp_interleave, int causal, float scale, int lse_base, void* out, float* lse,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Profiling aid (not part of the computation): for the calling host thread,
  * record `start` just before and `stop` just after the split-KV attention
  * kernel of each following mla_decode call, on that call's stream.  Pass two

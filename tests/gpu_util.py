@@ -24,6 +24,15 @@ def bf16_dev(bits: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev()).view(torch.bfloat16)
 
 
+def u8_dev(codes: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).to(dev())
+
+
+def kv_dev(pool: np.ndarray) -> torch.Tensor:
+    """A cache pool: bf16 bits (uint16) or E4M3 codes (uint8)."""
+    return u8_dev(pool) if pool.dtype == np.uint8 else bf16_dev(pool)
+
+
 def i32_dev(x) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(np.asarray(x, dtype=np.int32))).to(dev())
 
@@ -40,7 +49,7 @@ class Uploaded:
         self.q = bf16_dev(wl.q_bits)
         self.bt = i32_dev(wl.block_table)
         self.tot = i32_dev(wl.tot)
-        self.pools = {r: bf16_dev(p) for r, p in wl.pools.items()}
+        self.pools = {r: kv_dev(p) for r, p in wl.pools.items()}
         self.seq = {r: i32_dev(s) for r, s in wl.seq_lens.items()}
 
     def run(self, r, base="e", causal=None, global_null=None, **kw):
@@ -48,6 +57,8 @@ class Uploaded:
         causal = s.causal if causal is None else causal
         gnull = s.global_is_null if global_null is None else global_null
         g = None if gnull else self.tot
+        if s.kv_dtype == "fp8":
+            kw.setdefault("kv_scale", s.kv_scale)
         return mla.mla_decode(self.q, self.pools[r], self.bt, self.seq[r], g, cp_world=s.W, cp_rank=r,
                               causal=causal, scale=s.scale, lse_base=base, cp_interleave=s.interleave, **kw)
 

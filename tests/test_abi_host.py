@@ -22,7 +22,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["mla_status_string", "mla_decode_workspace_size", "mla_decode",
                                            "mla_merge_lse", "cp_local_slot", "mla_profile_attention_events",
-                                           "mla_kv_write", "mla_decode_interleaved", "mla_decode_varlen"])
+                                           "mla_kv_write", "mla_decode_interleaved", "mla_decode_varlen",
+                                           "mla_decode_fp8"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -161,3 +162,26 @@ def test_varlen_decode_needs_token_offsets():
     args[2] = 0
     assert lib.mla_decode_varlen(*args) == 1          # max_q_len < 1
 
+
+
+def _decode_fp8(kv_scale, **kw):
+    lib = mla.load_library()
+    a = dict(q=1, kv=1, bt=1, sl=1, gl=None, B=2, Q=1, H=16, nblk=4, bs=64, maxb=2, maxlen=128, W=1, r=0, I=1,
+             causal=1, scale=0.1, base=0, out=1, lse=1, ws=1, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.mla_decode_fp8(a["q"], a["kv"], ctypes.c_float(kv_scale), a["bt"], a["sl"], a["gl"], a["B"], a["Q"],
+                              a["H"], a["nblk"], a["bs"], a["maxb"], a["maxlen"], a["W"], a["r"], a["I"], a["causal"],
+                              ctypes.c_float(a["scale"]), a["base"], a["out"], a["lse"], a["ws"], a["wsb"],
+                              a["stream"])
+
+
+@pytest.mark.parametrize("kv_scale,kw", [
+    (0.0, {}), (-1.0, {}), (float("nan"), {}), (float("inf"), {}), (1e-3, dict(I=0)), (1e-3, dict(Q=0)),
+    (1e-3, dict(kv=None)), (1e-3, dict(wsb=0)),
+])
+def test_fp8_decode_rejects_bad_arguments(kv_scale, kw):
+    assert _decode_fp8(kv_scale, **kw) == 1
+
+
+def test_fp8_decode_empty_batch_is_a_noop():
+    assert _decode_fp8(0.5, B=0, q=None, kv=None, out=None) == 0

@@ -1,0 +1,138 @@
+"""GPU parity of the FP8 (E4M3) latent cache path (mla_decode_fp8) against the
+oracle: every E4M3 code's conversion, small seeded workloads over the shapes
+the bf16 tests cover, a full-size sampled check, and bitwise agreement with
+the bf16 path on a cache holding the same values.  Bar as for bf16: output
+max-abs <= 2e-2 and mean-abs <= 2e-3 against float64, LSE within 1e-3.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_11_amd as mla
+import oracle
+import workloads as WL
+from tests.gpu_util import Uploaded, compare, say, bf16_dev, u8_dev, i32_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def spec(name, B, H, Q, causal, lengths, W=1, ranks=None, bs=64, kv_scale=1.0 / 64, **kw):
+    return WL.Spec(name=name, B=B, H=H, Q=Q, causal=causal, seed=zlib.crc32(name.encode()) % 10000,
+                   lengths=list(lengths), W=W, ranks=tuple(range(W)) if ranks is None else tuple(ranks),
+                   block_size=bs, kv_dtype="fp8", kv_scale=kv_scale, **kw)
+
+
+CASES = [
+    spec("fp8_h16_q1_ragged", 5, 16, 1, True, [1, 63, 64, 65, 3000], global_is_null=True),
+    spec("fp8_h16_q1_scale1", 3, 16, 1, True, [40, 700, 2100], global_is_null=True, kv_scale=1.0),
+    spec("fp8_h8_q2", 3, 8, 2, True, [2, 700, 1290], global_is_null=True, kv_scale=0.0123),
+    spec("fp8_h16_q4_dcp2", 3, 16, 4, True, [5, 333, 2049], W=2),
+    spec("fp8_h24_q3_dcp8_bs128", 2, 24, 3, True, [200, 1111], W=8, bs=128),
+    spec("fp8_h128_q4_causal", 2, 128, 4, True, [4, 900], global_is_null=True),
+    spec("fp8_h128_q16_noncausal_dcp2_rank1", 2, 128, 16, False, [64, 1000], W=2, ranks=[1]),
+    spec("fp8_bs1", 2, 16, 1, True, [17, 90], bs=1, global_is_null=True),
+    spec("fp8_bs16_dcp4", 3, 16, 2, True, [9, 130, 515], W=4, bs=16),
+    spec("fp8_nan_fill", 3, 16, 4, True, [70, 130, 1000], W=2, fill="nan"),
+    spec("fp8_peaky", 3, 16, 1, True, [100, 1500, 4000], q_mult=8.0, global_is_null=True),
+    spec("fp8_h16_q4_dcp2_interleave4", 3, 16, 4, True, [5, 333, 2049], W=2, interleave=4),
+    spec("fp8_many_tiny_requests", 300, 16, 1, True, [(7 * i) % 5 for i in range(300)], global_is_null=True),
+]
+
+
+def oracle_rank(wl, r):
+    s = wl.spec
+    tot = None if (s.global_is_null and s.W == 1) else wl.tot
+    return oracle.mla_decode(wl.q_bits, wl.global_rows, wl.seq_lens[r], tot, s.W, r, s.causal, s.scale, s.lse_base,
+                             interleave=s.interleave, kv_scale=s.kv_scale)
+
+
+@pytest.mark.parametrize("sp", CASES, ids=[c.name for c in CASES])
+def test_fp8_decode_matches_oracle(sp):
+    wl = WL.build(sp)
+    up = Uploaded(wl)
+    for r in sorted(wl.pools):
+        say(f"{sp.name} rank {r}")
+        out, lse = up.run(r)
+        torch.cuda.synchronize()
+        ro, rl = oracle_rank(wl, r)
+        compare(out, lse, ro, rl, f"{sp.name} r{r}")
+
+
+@pytest.mark.parametrize("kv_scale", [1.0, 0.25])
+def test_every_e4m3_code_converts_exactly(kv_scale):
+    """One visible key per request, so the output is that key's value row,
+    which is exactly representable in bf16: every finite code is compared
+    bit for bit with the oracle's decoding."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)  # the two NaN codes
+    B, H, bs, D = 4, 16, 16, oracle.D_QK
+    rows = np.zeros((B, D), dtype=np.uint8)
+    for b in range(B):
+        # every finite code lands in the value columns of two requests, at
+        # different columns
+        rows[b, :512] = np.roll(np.resize(codes, 512), 37 * b)
+        rows[b, 512:] = codes[(np.arange(64) * 5 + b) % codes.size]
+    pool = np.zeros((B, bs, D), dtype=np.uint8)
+    pool[:, 0, :] = rows
+    bt = np.arange(B, dtype=np.int32).reshape(B, 1)
+    seq = np.ones(B, dtype=np.int32)
+    q = torch.zeros((B, 1, H, D), dtype=torch.bfloat16, device="cuda:0")
+    say(f"all codes, kv_scale {kv_scale}")
+    out, lse = mla.mla_decode(q, u8_dev(pool), i32_dev(bt), i32_dev(seq), None, kv_scale=kv_scale)
+    torch.cuda.synchronize()
+    want = oracle.e4m3_to_f64(rows[:, :512]) * kv_scale  # exactly representable in bf16
+    got = out.float().cpu().numpy().astype(np.float64)
+    for b in range(B):
+        assert np.array_equal(got[b], np.broadcast_to(want[b], (H, 512))), f"request {b}"
+    assert np.all(lse.cpu().numpy() == 0.0)  # a zero query: one key with score 0
+
+
+def test_fp8_equals_bf16_path_on_the_same_values_bitwise():
+    """With kv_scale 1 the bf16 cache of the decoded codes holds the same
+    values, and the 16-row kernel gives identical results on both."""
+    sp = spec("fp8_vs_bf16", 4, 16, 1, True, [30, 500, 1500, 4100], global_is_null=True, kv_scale=1.0)
+    wl = WL.build(sp)
+    up = Uploaded(wl)
+    codes = wl.pools[0]
+    vals = oracle.e4m3_to_f64(codes).astype(np.float32)  # exact: E4M3 values fit in bf16
+    bf = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(oracle.bf16_bits_to_f64(bf), oracle.e4m3_to_f64(codes))
+    o8, l8 = up.run(0)
+    o16, l16 = mla.mla_decode(up.q, bf16_dev(bf), up.bt, up.seq[0], None, scale=sp.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o8, o16)
+    assert torch.equal(l8, l16)
+
+
+def test_fp8_cache_scale_scales_scores_and_values():
+    """Codes c with scale s against codes c with scale 2s: the second equals
+    the first with the query doubled (scores) and the output doubled."""
+    sp = spec("fp8_scale_rel", 3, 16, 1, True, [100, 900, 2500], global_is_null=True, kv_scale=1.0 / 32)
+    wl = WL.build(sp)
+    up = Uploaded(wl)
+    o1, l1 = up.run(0)
+    o2, l2 = up.run(0, kv_scale=2.0 / 32)
+    q2 = (up.q.float() * 2).to(torch.bfloat16)  # exact: doubling a bf16 value
+    o3, l3 = mla.mla_decode(q2, up.pools[0], up.bt, up.seq[0], None, scale=sp.scale, kv_scale=1.0 / 32)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.float(), (o3.float() * 2))
+    assert torch.equal(l2, l3)
+    assert not torch.equal(l1, l2)
+
+
+def test_fp8_full_size_decode_on_sampled_rows():
+    sp = WL.config(2, kv_dtype="fp8", kv_scale=1.0 / 64)
+    say(f"{sp.name} fp8: generating")
+    wl = WL.build(sp)
+    up = Uploaded(wl)
+    out, lse = up.run(0, max_seq_len=int(wl.seq_lens[0].max()))
+    torch.cuda.synchronize()
+    o = out.float()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    rng = np.random.default_rng(2002)
+    rows = sorted({(int(rng.integers(sp.B)), 0, int(rng.integers(sp.H))) for _ in range(24)}
+                  | {(int(np.argmax(wl.tot)), 0, sp.H - 1), (int(np.argmin(wl.tot)), 0, 0)})
+    ro, rl = oracle.mla_decode(wl.q_bits, wl.global_rows, wl.seq_lens[0], None, 1, 0, True, sp.scale, "e",
+                               rows=rows, kv_scale=sp.kv_scale)
+    compare(out, lse, ro, rl, f"{sp.name} fp8", rows=[(b, h) for (b, _, h) in rows])
