@@ -396,7 +396,9 @@ constexpr int M16_DMA_PER_WAVE = RING_DMA_PER_WAVE;
 // FP8 cache: a ring item is 18 KiB (32 keys x 576 E4M3 bytes, or the 16
 // bf16 query rows), 18 one-KiB loads: waves 0, 1 issue 5, waves 2, 3 issue 4
 constexpr int M16F8_RAW = 18 * 1024;
-constexpr int M16F8_NS = 5;
+constexpr int M16F8_NS = 3;
+constexpr int M16F8_WG_PER_CU = 2;  // two workgroups per CU hide each other's latency chains
+constexpr int M16F8_LOADS = M16F8_RAW / 1024;
 constexpr int M16F8_ROW = D_QK;  // bytes of an E4M3 row
 constexpr int M16_KSTEPS = 9;                      // 32-dim MFMA steps per wave (half of 576)
 constexpr int M16_BT_WIN = 1024;                   // block-table entries held in LDS per batch
@@ -477,10 +479,87 @@ __device__ __forceinline__ RingRows m16_item_rows(const DecodeArgs& a, const int
   return ring_rows(rowp, stage_lds);
 }
 
+// ---- FP8 cache.  A key item holds 32 rows of 576 E4M3 bytes, row r at byte
+// 576 r, unconverted; the computation widens its fragments to bf16 in
+// registers (exactly: every E4M3 value is a bf16 value).  Rows are 144
+// dwords apart (16 mod 32 banks), so the 16-byte chunks of each row are
+// rotated: value chunk c < 32 of row r sits at (c + rot(r)) mod 32, rope
+// chunk c >= 32 at 32 + (c + rot(r)) mod 4, with rot(r) = (r/2) mod 4 +
+// 2 [r >= 16].  Then the 8 key rows of a transposed value read (keys 4g..4g+3
+// and 16+4g..16+4g+3, one chunk) land on 8 different 16-byte bank groups,
+// and the 16 key rows of a score read on every group twice.  The ring loads
+// place the chunks: lane l of load g fills item chunk 64 g + l, and takes
+// its bytes from whichever source chunk belongs there.
+__device__ __forceinline__ int f8_rot(int r) { return ((r >> 1) & 3) + 2 * ((r >> 4) & 1); }
+__device__ __forceinline__ int f8_pos(int r, int c) {
+  return c < 32 ? (c + f8_rot(r)) & 31 : 32 + ((c + f8_rot(r)) & 3);
+}
+__device__ __forceinline__ int f8_chunk_at(int r, int q) {
+  return q < 32 ? (q - f8_rot(r)) & 31 : 32 + ((q - f8_rot(r)) & 3);
+}
+
+// 8 E4M3 bytes to 8 bf16 values, byte e to element e
+__device__ __forceinline__ bf16x8 f8x8_to_bf16(uint32_t x, uint32_t y) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y, 1.0f, true);
+  const bf16x4 lo = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const bf16x4 hi = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Source addresses of this wave's loads of ring item c (load g = wave + 4m
+// for m < 5 while g < 18), all resolved before the first is issued.  A Q
+// item holds the group's 16 bf16 query rows in the swizzled layout of the
+// bf16 ring; items past the end load zeros.
+struct F8Loads {
+  const uint8_t* p[5];
+  uint32_t lds;
+};
+
+__device__ __forceinline__ F8Loads m16f8_loads(const DecodeArgs& a, const int* bt_lds, int nseg, const M16Cursor& c,
+                                               uint32_t stage_lds, int wave, int lane) {
+  F8Loads L;
+  L.lds = stage_lds;
+  const uint8_t* zero = reinterpret_cast<const uint8_t*>(kZeroRow);
+#pragma unroll
+  for (int m = 0; m < 5; ++m) {
+    const int P = 64 * (wave + 4 * m) + lane;  // item chunk this lane fills
+    const uint8_t* p = zero;
+    asm volatile("" : "+v"(p));
+    if (wave + 4 * m < M16F8_LOADS && c.s < nseg) {
+      if (c.j < 0) {
+        const int r = P / (ROW_BYTES / 16), q = P - (ROW_BYTES / 16) * r;
+        const int ch = (q & ~7) | ((q ^ ring_swz(r)) & 7);
+        const int qr = c.d.rt * M16_ROWS + r;
+        p = (qr < c.d.q_len * a.H ? a.q + ((int64_t)c.d.q_base * a.H + qr) * ROW_BYTES : zero) + 16 * ch;
+      } else {
+        const int r = P / (M16F8_ROW / 16), q = P - (M16F8_ROW / 16) * r;
+        const int ch = f8_chunk_at(r, q);
+        const int t = c.d.ka + M16_TILE * c.j + r;
+        p = zero + 16 * ch;
+        if (t < c.d.kb) {
+          const int vb = block_of(a, t);
+          const int blk = bt_lds[c.d.e_base + vb];
+          if ((unsigned)blk < (unsigned)a.num_blocks)
+            p = a.kv + ((int64_t)blk * a.bs + (t - vb * a.bs)) * M16F8_ROW + 16 * ch;
+        }
+      }
+    }
+    L.p[m] = p;
+  }
+  return L;
+}
+
+__device__ __forceinline__ void m16f8_issue(const F8Loads& L, int m, int wave) {
+  if (wave + 4 * m < M16F8_LOADS) dma16(L.p[m], L.lds + 1024 * (wave + 4 * m));
+}
+
 // One 32-key tile: this wave's quarter of S^T, the exchange of the partial
 // tiles, online softmax with a lazily moved reference max, then this wave's
 // quarter of O^T += V^T P^T.  qf holds the wave's 9 k-steps of Q^T.
-template <class Issue>
+template <bool F8, class Issue>
 __device__ __forceinline__ void m16_compute(M16State& st, const bf16x8 (&qf)[M16_KSTEPS], const uint8_t* stage,
                                             uint8_t* xchg, float scale_log2, int ts, int k1, int nrow, int lane,
                                             int wave, Issue&& issue) {
@@ -489,13 +568,26 @@ __device__ __forceinline__ void m16_compute(M16State& st, const bf16x8 (&qf)[M16
   // the K fragment of k-step kk = 2k + wave/2 is logical chunk 4kk + g of key
   // row li, i.e. physical byte 128k + 16*((4*(wave/2) + g) ^ f(row))
   const int kr = 16 * (wave & 1) + li;
-  const uint8_t* kp = stage + ROW_BYTES * kr + 16 * ((4 * (wave >> 1) + g) ^ ring_swz(kr));
   f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
   bf16x8 kf[M16_KSTEPS];
   // all nine reads first, then the MFMAs in two chains (one chain of nine
   // dependent MFMAs would wait out the MFMA latency at every step)
+  if constexpr (F8) {
+    // dims 64kk + 32(wave/2) + 8g .. +7 are E4M3 bytes 8(g%2) .. +7 of
+    // chunk 4kk + 2(wave/2) + g/2
+    const uint8_t* kp = stage + M16F8_ROW * kr + 8 * (g & 1);
+    const int c0 = 2 * (wave >> 1) + (g >> 1);
+    uint2 raw[M16_KSTEPS];
 #pragma unroll
-  for (int kk = 0; kk < M16_KSTEPS; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(kp + 128 * kk);
+    for (int kk = 0; kk < M16_KSTEPS; ++kk)
+      raw[kk] = *reinterpret_cast<const uint2*>(kp + 16 * f8_pos(kr, 4 * kk + c0));
+#pragma unroll
+    for (int kk = 0; kk < M16_KSTEPS; ++kk) kf[kk] = f8x8_to_bf16(raw[kk].x, raw[kk].y);
+  } else {
+    const uint8_t* kp = stage + ROW_BYTES * kr + 16 * ((4 * (wave >> 1) + g) ^ ring_swz(kr));
+#pragma unroll
+    for (int kk = 0; kk < M16_KSTEPS; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(kp + 128 * kk);
+  }
   // one ring load of a later item per MFMA step (a burst of 36 after the
   // barrier would stall the waves behind the address unit)
 #pragma unroll
@@ -563,107 +655,54 @@ __device__ __forceinline__ void m16_compute(M16State& st, const bf16x8 (&qf)[M16
   // 16h + 4g + li/4, value columns 16T + 4(li%4) .. +3 (logical chunk
   // 2T + (li/2)%2, byte 8(li%2)) and receives column 16T + li of the 4 rows;
   // T = 8*wave + mt, so the chunk is 8(2*wave + mt/4) + 2(mt%4) + (li/2)%2
-  const int vr = 4 * g + (li >> 2);
-  const int vsw = ring_swz(vr);  // equal for rows vr and 16 + vr
-  const uint8_t* vrow = stage + ROW_BYTES * vr + 256 * wave + 8 * (li & 1);
-  const uint8_t* vp[4];
+  if constexpr (F8) {
+    // an 8-bit transposed read: in each 16-lane group, lanes 2e and 2e+1
+    // address the two halves of block row e (key 4g+e, or 16+4g+e-4 for
+    // e >= 4, as in P^T) of value chunk T = 8 wave + mt, and lane li receives
+    // byte column li of the 8 rows
+    const int e = li >> 1;
+    const int key = e < 4 ? 4 * g + e : 12 + 4 * g + e;
+    const uint8_t* vrow = stage + M16F8_ROW * key + 8 * (li & 1);
+    const int vrot = f8_rot(key) + 8 * wave;
+    i32x2 v[8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) vp[q] = vrow + 16 * ((2 * q + ((li >> 1) & 1)) ^ vsw);
-  i16x4 v[8][2];
+    for (int mt = 0; mt < 8; ++mt)
+      v[mt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vrow + 16 * ((vrot + mt) & 31)));
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    v[mt][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp[mt & 3] + 128 * (mt >> 2)));
-    v[mt][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp[mt & 3] + M16_HALF + 128 * (mt >> 2)));
-  }
+    for (int mt = 0; mt < 8; ++mt)
+      st.o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f8x8_to_bf16((uint32_t)v[mt].x, (uint32_t)v[mt].y), pf,
+                                                         st.o[mt], 0, 0, 0);
+  } else {
+    const int vr = 4 * g + (li >> 2);
+    const int vsw = ring_swz(vr);  // equal for rows vr and 16 + vr
+    const uint8_t* vrow = stage + ROW_BYTES * vr + 256 * wave + 8 * (li & 1);
+    const uint8_t* vp[4];
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    const bf16x4 a0 = __builtin_bit_cast(bf16x4, v[mt][0]);
-    const bf16x4 a1 = __builtin_bit_cast(bf16x4, v[mt][1]);
-    st.o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                       pf, st.o[mt], 0, 0, 0);
-  }
-}
-
-// ---- FP8 cache: ring items land as raw bytes and K items are widened to
-// bf16 (exactly: every E4M3 value is a bf16 value) into the swizzled layout
-// the computation reads.
-// What ring item c is, for the per-lane addresses of its 18 loads: a Q item
-// (q points at its first query row, qrows rows are real), a key tile (keys
-// ts .. ts+31, real below kb), or past the end (zero rows).
-struct F8Item {
-  const uint8_t* q;
-  int qrows;
-  int ts, kb, e_base;
-  int kind;  // 0 past the end, 1 query rows, 2 key tile
-  uint32_t stage_lds;
-};
-
-__device__ __forceinline__ F8Item m16f8_item(const DecodeArgs& a, int nseg, const M16Cursor& c, uint32_t stage_lds) {
-  F8Item d{nullptr, 0, 0, 0, 0, 0, stage_lds};
-  if (c.s < nseg) {
-    if (c.j < 0) {
-      d.kind = 1;
-      d.q = a.q + ((int64_t)c.d.q_base * a.H + c.d.rt * M16_ROWS) * ROW_BYTES;
-      d.qrows = min(M16_ROWS, c.d.q_len * a.H - c.d.rt * M16_ROWS);
-    } else {
-      d.kind = 2;
-      d.ts = c.d.ka + M16_TILE * c.j;
-      d.kb = c.d.kb;
-      d.e_base = c.d.e_base;
+    for (int q = 0; q < 4; ++q) vp[q] = vrow + 16 * ((2 * q + ((li >> 1) & 1)) ^ vsw);
+    i16x4 v[8][2];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      v[mt][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp[mt & 3] + 128 * (mt >> 2)));
+      v[mt][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp[mt & 3] + M16_HALF + 128 * (mt >> 2)));
     }
-  }
-  return d;
-}
-
-// Load g (0..17) of item d: lane l fills item byte 1024 g + 16 l (a key row
-// is 576 bytes, a query row 1152; 16-byte chunks never straddle rows).
-__device__ __forceinline__ void m16f8_issue(const DecodeArgs& a, const int* bt_lds, const F8Item& d, int g,
-                                            int lane) {
-  const int b = 1024 * g + 16 * lane;
-  const uint8_t* zero = reinterpret_cast<const uint8_t*>(kZeroRow);
-  const uint8_t* p = zero + (b % M16F8_ROW);
-  if (d.kind == 2) {
-    const int row = b / M16F8_ROW, off = b - row * M16F8_ROW;
-    const int t = d.ts + row;
-    if (t < d.kb) {
-      const int vb = block_of(a, t);
-      const int blk = bt_lds[d.e_base + vb];
-      if ((unsigned)blk < (unsigned)a.num_blocks)
-        p = a.kv + ((int64_t)blk * a.bs + (t - vb * a.bs)) * M16F8_ROW + off;
-    }
-  } else if (d.kind == 1) {
-    const int row = b / ROW_BYTES, off = b - row * ROW_BYTES;
-    if (row < d.qrows) p = d.q + (int64_t)row * ROW_BYTES + off;
-  }
-  asm volatile("" : "+v"(p));
-  dma16(p, d.stage_lds + 1024 * g);
-}
-
-// Widen a key tile: bf16 chunk k (8 values) of row r comes from E4M3 bytes
-// 576 r + 8 k of the raw item and goes to chunk k of row r of the swizzled
-// stage layout; consecutive threads take consecutive chunks, so both the
-// 8-byte reads and the 16-byte writes are free of bank conflicts.
-__device__ __forceinline__ void m16f8_widen(const uint8_t* raw, uint8_t* stage, int tid) {
 #pragma unroll
-  for (int i = 0; i < (RING_TILE * D_QK / 8) / M16_THREADS; ++i) {
-    const int c = tid + M16_THREADS * i;
-    const int row = c / (D_QK / 8), k = c - (D_QK / 8) * row;
-    const uint2 v = *reinterpret_cast<const uint2*>(raw + M16F8_ROW * row + 8 * k);
-    const uint4 o = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false)),
-                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true)),
-                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false)),
-                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true))};
-    *reinterpret_cast<uint4*>(stage + ROW_BYTES * row + 16 * ((k & ~7) | ((k ^ ring_swz(row)) & 7))) = o;
+    for (int mt = 0; mt < 8; ++mt) {
+      const bf16x4 a0 = __builtin_bit_cast(bf16x4, v[mt][0]);
+      const bf16x4 a1 = __builtin_bit_cast(bf16x4, v[mt][1]);
+      st.o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                         pf, st.o[mt], 0, 0, 0);
+    }
   }
 }
 
 template <bool F8>
-__global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) {
-  // bf16 cache: NS stages of 36 KiB.  FP8 cache: NS_F8 raw stages of 18 KiB
-  // and one bf16 stage the computation reads.
+__global__ __launch_bounds__(M16_THREADS, F8 ? M16F8_WG_PER_CU : 1) void attn_m16_kernel(DecodeArgs a) {
+  // bf16 cache: 4 stages of 36 KiB, one workgroup per CU.  FP8 cache: 3 of
+  // 18 KiB (about 68 KiB of LDS in all, 236 VGPRs), two workgroups per CU,
+  // each running its tile computation while the other waits on its loads.
   constexpr int NS = F8 ? M16F8_NS : M16_NS;
   constexpr int RAW = F8 ? M16F8_RAW : M16_STAGE;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * RAW + (F8 ? M16_STAGE : 0)];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * RAW];
   __shared__ __attribute__((aligned(16))) uint8_t xchg[4 * 1024];
   __shared__ int bt_lds[M16_BT_WIN];
   __shared__ M16Seg segs[M16_MAXSEG];
@@ -678,16 +717,9 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
   int sel_off[RING_DMA_PER_WAVE];  // per-lane constants of this wave's ring loads
   if constexpr (!F8) ring_dma_offsets(sel_off, wave, lane);
-  uint8_t* const cstage = ring + NS * RAW;  // FP8: the widened tile
-  // FP8: load g of an item is issued by wave g % 4 (waves 0, 1: 5 loads,
-  // waves 2, 3: 4), at its m-th issue slot for g = wave + 4 m
-  auto f8_issue = [&](const F8Item& d, int m) __attribute__((always_inline)) {
-    const int gl = wave + 4 * m;
-    if (gl < M16F8_RAW / 1024) m16f8_issue(a, bt_lds, d, gl, lane);
-  };
-  auto f8_issue_all = [&](const F8Item& d) __attribute__((always_inline)) {
+  auto f8_issue_all = [&](const F8Loads& L) __attribute__((always_inline)) {
 #pragma unroll
-    for (int m = 0; m < 5; ++m) f8_issue(d, m);
+    for (int m = 0; m < 5; ++m) m16f8_issue(L, m, wave);
   };
 
   // state of the group being computed; it survives batch boundaries
@@ -718,7 +750,7 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
 #pragma unroll
     for (int p = 0; p < NS - 1; ++p) {
       if constexpr (F8)
-        f8_issue_all(m16f8_item(a, nseg, ci, ring_lds + p * RAW));
+        f8_issue_all(m16f8_loads(a, bt_lds, nseg, ci, ring_lds + p * RAW, wave, lane));
       else
         ring_issue_all(m16_item_rows(a, bt_lds, nseg, ci, ring_lds + p * RAW, wave, lane), wave, sel_off);
       m16_advance(ci, segs, nseg);
@@ -738,20 +770,18 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
       // ... so its stage can take item it+NS-1
       const uint32_t nxt_lds = ring_lds + ((it + NS - 1) % NS) * RAW;
       RingRows nxt;
-      F8Item nxt8;
+      F8Loads nxt8;
       if constexpr (F8)
-        nxt8 = m16f8_item(a, nseg, ci, nxt_lds);
+        nxt8 = m16f8_loads(a, bt_lds, nseg, ci, nxt_lds, wave, lane);
       else
         nxt = m16_item_rows(a, bt_lds, nseg, ci, nxt_lds, wave, lane);
       m16_advance(ci, segs, nseg);
       const uint8_t* stage = ring + (it % NS) * RAW;
       if (cc.j < 0) {
         // Q item: this wave's k-steps of Q^T (lane (li, g): dims
-        // 32kk + 8g .. +7 of row li, kk = 2k + wave/2; stored like key rows
-        // 0..15, or plainly row after row for an FP8 cache) into registers,
-        // and a fresh state
-        const uint8_t* qp = F8 ? stage + ROW_BYTES * li + 16 * (4 * (wave >> 1) + g)
-                               : stage + ROW_BYTES * li + 16 * ((4 * (wave >> 1) + g) ^ ring_swz(li));
+        // 32kk + 8g .. +7 of row li, kk = 2k + wave/2; stored like bf16 key
+        // rows 0..15) into registers, and a fresh state
+        const uint8_t* qp = stage + ROW_BYTES * li + 16 * ((4 * (wave >> 1) + g) ^ ring_swz(li));
 #pragma unroll
         for (int kk = 0; kk < M16_KSTEPS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 128 * kk);
         if constexpr (F8)
@@ -768,19 +798,14 @@ __global__ __launch_bounds__(M16_THREADS, 1) void attn_m16_kernel(DecodeArgs a) 
         st.l_part = 0.f;
         st.l_out = 0.f;
       } else {
-        if constexpr (F8) {
-          // widen the tile; the barrier at the top of this iteration ended
-          // every read of the previous one
-          m16f8_widen(stage, cstage, tid);
-          __syncthreads();
-          m16_compute(st, qf, cstage, xchg, a.scale_log2, cc.d.ka + M16_TILE * cc.j, cc.d.kb, nrow, lane, wave,
-                      [&](int kk) __attribute__((always_inline)) {
-                        if (kk < 5) f8_issue(nxt8, kk);
-                      });
-        } else {
-          m16_compute(st, qf, stage, xchg, a.scale_log2, cc.d.ka + M16_TILE * cc.j, cc.d.kb, nrow, lane, wave,
-                      [&](int kk) __attribute__((always_inline)) { ring_issue_one(nxt, kk, wave, sel_off); });
-        }
+        if constexpr (F8)
+          m16_compute<true>(st, qf, stage, xchg, a.scale_log2, cc.d.ka + M16_TILE * cc.j, cc.d.kb, nrow, lane, wave,
+                            [&](int kk) __attribute__((always_inline)) {
+                              if (kk < 5) m16f8_issue(nxt8, kk, wave);
+                            });
+        else
+          m16_compute<false>(st, qf, stage, xchg, a.scale_log2, cc.d.ka + M16_TILE * cc.j, cc.d.kb, nrow, lane,
+                             wave, [&](int kk) __attribute__((always_inline)) { ring_issue_one(nxt, kk, wave, sel_off); });
         if (cc.j == cc.nt - 1 && (cc.d.flags & M16_SEG_LAST)) {
           // partial slot: wave w's O^T tiles T = 8w + mt in the accumulator
           // layout [T][lane][4] (one 16-byte store per lane and tile), then
@@ -1340,7 +1365,7 @@ int device_cu_count() {
 
 // The 128-row kernel needs a power-of-two block size (its ring loads use
 // shifts and masks); every other case runs the 16-row kernel.
-Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool allow_r128) {
+Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool allow_r128, bool fp8 = false) {
   Plan p{};
   const int64_t R = (int64_t)q_len * H;
   p.rows_tile = (R <= M16_ROWS || !allow_r128) ? M16_ROWS : R128_ROWS;
@@ -1355,7 +1380,9 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool allow_r12
   // keys through its L2; a few CUs idle when n_rt does not divide the CUs of
   // an XCD.
   const int per_xcd = cus / 8;
-  int64_t nbund = (p.rows_tile == R128_ROWS && p.n_rt <= per_xcd) ? 8 * (per_xcd / p.n_rt) : cus / p.n_rt;
+  int64_t nbund = (p.rows_tile == R128_ROWS && p.n_rt <= per_xcd) ? 8 * (per_xcd / p.n_rt)
+                  : (int64_t)(fp8 ? M16F8_WG_PER_CU : 1) * cus / p.n_rt;
+  if (nbund < 1) nbund = 1;
   const int64_t units = (int64_t)B * ((max_seq_len > 0 ? max_seq_len : 1) + p.ovh);  // of one row tile
   const int64_t by_work = (units + 255) / 256;  // at least 256 keys per workgroup
   if (nbund > by_work) nbund = by_work >= 8 ? by_work / 8 * 8 : by_work;
@@ -1385,9 +1412,13 @@ extern "C" int mla_profile_attention_events(hipEvent_t start, hipEvent_t stop) {
 extern "C" size_t mla_decode_workspace_size(int B, int q_len, int H, int max_seq_len) {
   if (B <= 0 || q_len < 1 || H < 1 || max_seq_len < 0) return 0;
   const int cus = device_cu_count();
-  const size_t a = make_plan(B, q_len, H, max_seq_len, cus, true).bytes;
-  const size_t b = make_plan(B, q_len, H, max_seq_len, cus, false).bytes;
-  return a > b ? a : b;
+  size_t m = 0;
+  for (const bool r128 : {true, false})
+    for (const bool fp8 : {false, true}) {
+      const size_t x = make_plan(B, q_len, H, max_seq_len, cus, r128 && !fp8, fp8).bytes;
+      m = x > m ? x : m;
+    }
+  return m;
 }
 
 namespace {
@@ -1410,7 +1441,7 @@ int decode(const void* q, const int32_t* query_start_loc, const void* kv_cache, 
   if (!q || !kv_cache || !block_table || !seq_lens || !out) return MLA_ERR_INVALID_ARG;
   const bool pow2_bs = (block_size & (block_size - 1)) == 0;
   // an FP8 cache runs on the 16-row kernel only (row tiles of any count)
-  const Plan p = make_plan(B, q_len, H, max_seq_len, device_cu_count(), pow2_bs && !kv_fp8);
+  const Plan p = make_plan(B, q_len, H, max_seq_len, device_cu_count(), pow2_bs && !kv_fp8, kv_fp8 != 0);
   if (workspace_bytes < p.bytes || workspace == nullptr) return MLA_ERR_INVALID_ARG;
 
   DecodeArgs a{};
