@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the paged MLA decode hot path on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N] [--no-cpu-baseline]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N] [--interleave I]
+                [--varlen | --fp8] [--no-cpu-baseline]
 
 A step is one pass of the hot path over one batch of synthetic input:
   * slot mapping of the step's new tokens (cp_local_slot),
@@ -10,6 +11,9 @@ A step is one pass of the hot path over one batch of synthetic input:
   * and, for a sharded workload, the LSE merge of the ranks' partials.
 The default workload is the memory-bound single-token decode (batch 64,
 16 heads, lengths uniform in [1024, 8192]); --config 1..5 picks another.
+--fp8 stores the cache as E4M3 codes with one scale (mla_decode_fp8);
+--varlen draws a query length per request (mla_decode_varlen); --interleave
+deals positions to the ranks in segments of I.
 Inputs are resident in HBM before timing starts.  Prints ONE JSON line.
 """
 from __future__ import annotations
