@@ -10,6 +10,6 @@ a hand-derived slot example); see tests/test_oracle_pins.py.
 """
 from .mla_oracle import (  # noqa: F401
     D_QK, D_V, PAD_SLOT_ID,
-    bf16_bits_to_f64, e4m3_to_f64, owns, held_positions, visible_positions, local_count,
-    attend, mla_decode, mla_decode_varlen, merge_lse, cp_local_slot, kv_write,
+    bf16_bits_to_f64, e4m3_to_f64, e4m3_encode, owns, held_positions, visible_positions, local_count,
+    attend, mla_decode, mla_decode_varlen, merge_lse, cp_local_slot, kv_write, kv_write_fp8,
 )

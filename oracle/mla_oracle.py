@@ -76,6 +76,54 @@ def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
     return np.where((e == 15) & ((c & 7) == 7), np.nan, out)
 
 
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """8-bit E4M3 code of each float32 value: the nearest E4M3 value, ties
+    to the even code (mantissa field even); finite magnitudes at or above
+    448 and infinities saturate to +-448 (0x7E/0xFE); NaN gives 0x7F; the
+    sign of zero and of values that round to zero is kept.
+
+    Written from the format (1 sign, 4 exponent bits with bias 7, 3 mantissa
+    bits, subnormals m/8 * 2^-6): below 2^-6 the code is the number of 2^-9
+    steps, rounded half to even; above, with |x| = (1 + f) 2^e, the exponent
+    field is e + 7 and the mantissa field is 8f rounded half to even, a
+    carry moving to the next exponent.  All steps are exact in float64.
+    """
+    x = np.asarray(x, dtype=np.float32).astype(np.float64).reshape(-1)
+    out = np.empty(x.size, dtype=np.uint8)
+    for i, v in enumerate(x):
+        sign = 0x80 if math.copysign(1.0, v) < 0 else 0
+        if math.isnan(v):
+            out[i] = 0x7F
+            continue
+        a = abs(v)
+        if a >= 448.0:
+            out[i] = sign | 0x7E
+            continue
+        if a < 2.0 ** -6:
+            out[i] = sign | int(np.rint(a * 2.0 ** 9))  # 0..8; 8 is the smallest normal, code 0x08
+            continue
+        fr, k = math.frexp(a)  # a = fr 2^k, fr in [0.5, 1)
+        e = k - 1
+        mant = np.rint((a / 2.0 ** e - 1.0) * 8.0)
+        if mant == 8.0:
+            e, mant = e + 1, 0.0
+        out[i] = sign | ((e + 7) << 3) | int(mant)
+    return out
+
+
+def kv_write_fp8(cache_codes: np.ndarray, rows_bits: np.ndarray, slots: np.ndarray, kv_scale: float) -> np.ndarray:
+    """kv_write into an FP8 cache: each bf16 row is divided by kv_scale in
+    float32 (the correctly rounded quotient) and stored as the E4M3 codes of
+    e4m3_encode, at the same slots and with the same skips as kv_write (the
+    cache then holds value / kv_scale, which mla_decode multiplies back by
+    kv_scale; PR #54012 page, key source snippets: the cache dtype and its
+    scales).  cache_codes [num_blocks, block_size, 576] uint8."""
+    rows = bf16_bits_to_f64(np.asarray(rows_bits)).astype(np.float32)
+    q = (rows / np.float32(kv_scale)).astype(np.float32)
+    codes = e4m3_encode(q).reshape(rows.shape)
+    return kv_write(cache_codes, codes, slots)
+
+
 def held_positions(seq_len: int, W: int, r: int, interleave: int = 1) -> np.ndarray:
     """Global positions of the local rows a rank holds, in order: the first
     seq_len positions it owns (local row t is the t-th of them).  By

@@ -229,6 +229,66 @@ def test_fp8_cache_is_the_bf16_path_on_its_values(kv_scale):
         np.testing.assert_array_equal(l8, lb)
 
 
+def test_e4m3_encode_round_trips_every_finite_code():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    assert np.array_equal(oracle.e4m3_encode(oracle.e4m3_to_f64(codes)), codes)
+
+
+def test_e4m3_encode_matches_torch_below_saturation():
+    # torch rounds to nearest even but turns magnitudes from 464 up into NaN;
+    # below that the two must agree bit for bit
+    rng = np.random.default_rng(5)
+    mag = np.exp2(rng.uniform(-14, np.log2(463.9), 20000)).astype(np.float32)
+    x = np.concatenate([mag * rng.choice([-1, 1], mag.size), np.float32([0.0, -0.0, 2.0 ** -10, -2.0 ** -10,
+                                                                         1.5 * 2.0 ** -10, 448.0, 463.0])])
+    x = x.astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3_encode(x), ref)
+
+
+def test_e4m3_encode_ties_go_to_the_even_code():
+    # the midpoint between two neighbouring codes of one sign (exact in
+    # float32) encodes to whichever of them has an even mantissa field
+    for c in list(range(0, 0x7E)) + list(range(0x80, 0xFE)):
+        lo, hi = oracle.e4m3_to_f64(np.uint8([c, c + 1]))
+        mid = np.float32((lo + hi) / 2)
+        assert float(mid) == (lo + hi) / 2
+        got = int(oracle.e4m3_encode(np.float32([mid]))[0])
+        assert got == (c if c % 2 == 0 else c + 1), hex(c)
+
+
+def test_e4m3_encode_saturates_and_keeps_nan():
+    x = np.float32([448.0, 449.0, 464.0, 500.0, 3e38, np.inf, -448.0, -1e9, -np.inf, np.nan])
+    assert list(oracle.e4m3_encode(x)) == [0x7E] * 6 + [0xFE] * 3 + [0x7F]
+    # smallest subnormal and the half-way points below and above it
+    assert list(oracle.e4m3_encode(np.float32([2.0 ** -9, 2.0 ** -10, 1.5 * 2.0 ** -9, -2.0 ** -11]))) == [1, 0, 2, 0x80]
+
+
+def test_kv_write_fp8_stores_the_nearest_codes_of_value_over_scale():
+    rng = np.random.default_rng(9)
+    n, P, bs, s = 40, 3, 16, 0.0123
+    vals = (rng.standard_normal((n, oracle.D_QK)) * 3).astype(np.float32)
+    rows = (vals.view(np.uint32) >> 16).astype(np.uint16)  # bf16 bits (truncated; any bf16 values do)
+    cache = rng.integers(0, 256, size=(P, bs, oracle.D_QK), dtype=np.uint8)
+    slots = rng.permutation(P * bs)[:n].astype(np.int64)
+    slots[::7] = oracle.PAD_SLOT_ID
+    out = oracle.kv_write_fp8(cache, rows, slots, s)
+    x = oracle.bf16_bits_to_f64(rows)
+    for i, sl in enumerate(slots):
+        if sl < 0:
+            continue
+        got = oracle.e4m3_to_f64(out[sl // bs, sl % bs])
+        q = (x[i].astype(np.float32) / np.float32(s)).astype(np.float64)
+        # nearest: no E4M3 value is closer to the float32 quotient
+        allv = oracle.e4m3_to_f64(np.arange(256, dtype=np.uint8))
+        allv = allv[np.isfinite(allv)]
+        best = np.min(np.abs(q[:, None] - allv[None, :]), axis=1)
+        assert np.all(np.abs(q - got) == best)
+    untouched = np.ones(P * bs, bool)
+    untouched[slots[slots >= 0]] = False
+    assert np.array_equal(out.reshape(P * bs, -1)[untouched], cache.reshape(P * bs, -1)[untouched])
+
+
 # ---------------------------------------------------------------- varlen
 
 def tiny_varlen(q_lens, W=2, causal=True, lengths=(9, 14, 6), seed=17, I=1):
