@@ -151,34 +151,37 @@ def measured_peaks(torch, hip, stream, dev, reps=5):
 
 
 # ------------------------------------------------------------------ KV write
-def kv_write_rates(torch, mla, hip, stream, dev, step_job, reps=20, bulk_rows=1 << 18):
-    """Times mla_kv_write twice: storing the step's new-token rows at their
-    slots (the rows already there, so the cache is unchanged), and a bulk
-    scatter of bulk_rows random rows to a permutation of a scratch cache's
-    rows (bytes = rows x 1152 read + rows x 1152 written + 8 per slot)."""
+def kv_write_rates(torch, mla, hip, stream, dev, step_job, reps=20, bulk_rows=1 << 18, kv_scale=None):
+    """Times mla_kv_write (mla_kv_write_fp8 with kv_scale) twice: storing the
+    step's new-token rows at their slots (the rows already there, so the
+    cache is unchanged; quantised, for FP8), and a bulk scatter of bulk_rows
+    random rows to a permutation of a scratch cache's rows (bytes = rows x
+    1152 read + rows x 1152 written, or x 576 for FP8, + 8 per slot)."""
     rows, slots, cache = step_job
+    kw = {} if kv_scale is None else {"kv_scale": kv_scale}
     a_, b_ = hip.event(), hip.event()
-    mla.kv_write(rows, slots, cache)
+    mla.kv_write(rows, slots, cache, **kw)
     torch.cuda.synchronize()
     step_us = 0.0
     for _ in range(reps):  # one launch between each event pair: the host enqueues slower than it runs
         hip.record(a_, stream)
-        mla.kv_write(rows, slots, cache)
+        mla.kv_write(rows, slots, cache, **kw)
         hip.record(b_, stream)
         step_us += hip.elapsed_ms(a_, b_) * 1e3 / reps
     g = torch.Generator(device=dev).manual_seed(1)
     big_rows = torch.randint(-32768, 32767, (bulk_rows, 576), dtype=torch.int16, device=dev,
                              generator=g).view(torch.bfloat16)
-    big_cache = torch.empty((bulk_rows // 64, 64, 576), dtype=torch.bfloat16, device=dev)
+    big_cache = torch.empty((bulk_rows // 64, 64, 576), dtype=torch.bfloat16 if kv_scale is None else torch.uint8,
+                            device=dev)
     big_slots = torch.randperm(bulk_rows, device=dev, generator=g)
-    mla.kv_write(big_rows, big_slots, big_cache)
+    mla.kv_write(big_rows, big_slots, big_cache, **kw)
     torch.cuda.synchronize()
     hip.record(a_, stream)
     for _ in range(5):
-        mla.kv_write(big_rows, big_slots, big_cache)
+        mla.kv_write(big_rows, big_slots, big_cache, **kw)
     hip.record(b_, stream)
     bulk_us = hip.elapsed_ms(a_, b_) * 1e3 / 5
-    nbytes = bulk_rows * (2 * 1152 + 8)
+    nbytes = bulk_rows * (1152 + (1152 if kv_scale is None else 576) + 8)
     hip.destroy(a_)
     hip.destroy(b_)
     del big_rows, big_cache, big_slots
@@ -414,7 +417,9 @@ def main():
             if p >= 0 and (p // I) % s.W == r0 and t < len(wl.shards[r0][b]):
                 rows_np[b, i] = wl.shards[r0][b][t]
     if s.kv_dtype == "fp8":
-        kvw = None  # mla_kv_write stores bf16 rows; an FP8 cache is written by a quantising store, not built
+        # rows of the step's tokens quantised on the way in; their values do not
+        # change the timing, and the pool is not read after the timed steps
+        kvw = kv_write_rates(torch, mla, hip, stream, dev, (bf16(rows_np), slots0, pools[r0][0]), kv_scale=s.kv_scale)
     else:
         kvw = kv_write_rates(torch, mla, hip, stream, dev, (bf16(rows_np), slots0, pools[r0][0]))
     log("achievable peaks: 1 GiB copy, 8192^3 bf16 GEMM (torch)")

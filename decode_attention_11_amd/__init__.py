@@ -53,6 +53,7 @@ _SIGNATURES = [
                                     ctypes.c_float, _I, _P, _P, _P, ctypes.c_size_t, _P]),
     ("mla_decode_varlen", _I, [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                                ctypes.c_float, _I, _P, _P, _P, ctypes.c_size_t, _P]),
+    ("mla_kv_write_fp8", _I, [_P, _P, ctypes.c_int64, ctypes.c_float, _P, _I, _I, _P]),
     ("mla_decode_fp8", _I, [_P, _P, ctypes.c_float, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                             ctypes.c_float, _I, _P, _P, _P, ctypes.c_size_t, _P]),
 ]
@@ -263,21 +264,34 @@ def cp_local_slot(positions: torch.Tensor, block_table: torch.Tensor, block_size
     return out
 
 
-def kv_write(kv_new: torch.Tensor, slots: torch.Tensor, kv_cache: torch.Tensor) -> torch.Tensor:
+def kv_write(kv_new: torch.Tensor, slots: torch.Tensor, kv_cache: torch.Tensor,
+             kv_scale: Optional[float] = None) -> torch.Tensor:
     """Store new KV rows [..., 576] bf16 at their slots [...] int64 in kv_cache
-    [num_blocks, block_size, 576] bf16 (in place); pad and out-of-range slots
-    write nothing.  Returns kv_cache."""
+    [num_blocks, block_size, 576] (in place); pad and out-of-range slots
+    write nothing.  A bf16 cache takes the rows as they are; an FP8 cache
+    (float8_e4m3fn or uint8 codes, kv_scale given) takes the E4M3 codes of
+    row / kv_scale.  Returns kv_cache."""
     lib = load_library()
     _need(kv_new, "kv_new", torch.bfloat16)
     _need(slots, "slots", torch.int64)
-    _need(kv_cache, "kv_cache", torch.bfloat16, 3)
+    fp8 = kv_scale is not None
+    if fp8:
+        if kv_cache.dtype not in _FP8_KV_DTYPES:
+            raise ValueError("an FP8 cache (kv_scale given) must be float8_e4m3fn or uint8 codes")
+        _need(kv_cache, "kv_cache", kv_cache.dtype, 3)
+    else:
+        _need(kv_cache, "kv_cache", torch.bfloat16, 3)
     if kv_new.shape[-1] != D_QK or kv_cache.shape[2] != D_QK:
         raise ValueError(f"rows must be {D_QK} wide")
     n = kv_new.numel() // D_QK
     if slots.numel() != n or tuple(slots.shape) != tuple(kv_new.shape[:-1]):
         raise ValueError("slots must have one entry per row of kv_new")
-    _check(lib.mla_kv_write(kv_new.data_ptr(), slots.data_ptr(), int(n), kv_cache.data_ptr(),
-                            int(kv_cache.shape[0]), int(kv_cache.shape[1]), _stream(kv_cache.device)))
+    if fp8:
+        _check(lib.mla_kv_write_fp8(kv_new.data_ptr(), slots.data_ptr(), int(n), float(kv_scale), kv_cache.data_ptr(),
+                                    int(kv_cache.shape[0]), int(kv_cache.shape[1]), _stream(kv_cache.device)))
+    else:
+        _check(lib.mla_kv_write(kv_new.data_ptr(), slots.data_ptr(), int(n), kv_cache.data_ptr(),
+                                int(kv_cache.shape[0]), int(kv_cache.shape[1]), _stream(kv_cache.device)))
     return kv_cache
 
 

@@ -168,6 +168,23 @@ int mla_decode_varlen(const void* q, const int32_t* query_start_loc, int max_q_l
                       void* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * mla_kv_write into an FP8 latent cache (the write side of mla_decode_fp8;
+ * PR #54012 page, key source snippets: the cache dtype and its scales).
+ * Each bf16 value v of a new row is stored as the E4M3 code of the
+ * correctly rounded float32 quotient v / kv_scale: the nearest E4M3 value,
+ * ties to the even code, magnitudes from 448 up and infinities saturated to
+ * +-448 (0x7E/0xFE), NaN as 0x7F, the sign of zero kept.
+ * kv_new: [n_rows, 576] bf16 (16-byte aligned); slots: [n_rows] int64 as
+ * for mla_kv_write (pad, negative and past-the-end slots write nothing);
+ * kv_cache: [num_blocks, block_size, 576] bytes (16-byte aligned).  Rows with
+ * the same slot: unspecified which one stays.
+ * Errors: those of mla_kv_write, and MLA_ERR_INVALID_ARG for a kv_scale that
+ * is not finite and positive.
+ */
+int mla_kv_write_fp8(const void* kv_new, const int64_t* slots, int64_t n_rows, float kv_scale, void* kv_cache,
+                     int num_blocks, int block_size, hipStream_t stream);
+
+/*
  * mla_decode_interleaved over an FP8 latent cache (PR #54012 page, key
  * source snippets: the backend's cache dtype and its bmm1/bmm2 scales, and
  * the output scale handed to the decode kernel).  kv_cache holds

@@ -23,7 +23,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["mla_status_string", "mla_decode_workspace_size", "mla_decode",
                                            "mla_merge_lse", "cp_local_slot", "mla_profile_attention_events",
                                            "mla_kv_write", "mla_decode_interleaved", "mla_decode_varlen",
-                                           "mla_decode_fp8"])
+                                           "mla_decode_fp8", "mla_kv_write_fp8"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -185,3 +185,20 @@ def test_fp8_decode_rejects_bad_arguments(kv_scale, kw):
 
 def test_fp8_decode_empty_batch_is_a_noop():
     assert _decode_fp8(0.5, B=0, q=None, kv=None, out=None) == 0
+
+
+def _kv_write_fp8(kv_scale, n=4, rows=16, slots=16, cache=16, nblk=2, bs=64):
+    return mla.load_library().mla_kv_write_fp8(rows, slots, n, ctypes.c_float(kv_scale), cache, nblk, bs, None)
+
+
+@pytest.mark.parametrize("kv_scale,kw", [
+    (0.0, {}), (-2.0, {}), (float("nan"), {}), (float("inf"), {}), (1.0, dict(n=-1)), (1.0, dict(nblk=0)),
+    (1.0, dict(bs=0)), (1.0, dict(rows=None)), (1.0, dict(slots=None)), (1.0, dict(cache=None)),
+    (1.0, dict(rows=8)), (1.0, dict(cache=8)),
+])
+def test_kv_write_fp8_rejects_bad_arguments(kv_scale, kw):
+    assert _kv_write_fp8(kv_scale, **kw) == 1
+
+
+def test_kv_write_fp8_empty_is_a_noop():
+    assert _kv_write_fp8(0.5, n=0, rows=None, slots=None, cache=None) == 0
