@@ -710,10 +710,13 @@ __global__ __launch_bounds__(M16_THREADS, F8 ? M16F8_WG_PER_CU : 1) void attn_m1
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, g = lane >> 4;
-  // ranges in launch order: with one row tile per request each key is read
-  // by one workgroup only, so there is no L2 sharing to gain from grouping
-  // ranges by XCD, and grouping concentrates slow requests on a few XCDs
-  const int bund = blockIdx.x / a.n_rt, tile = blockIdx.x - bund * a.n_rt;
+  // With one row tile per request each key is read by one workgroup only:
+  // ranges go in launch order (grouping them by XCD would concentrate slow
+  // requests on a few XCDs).  With several row tiles, a bundle's workgroups
+  // read the same keys and sit on one XCD, whose L2 then serves all but the
+  // first read.
+  const int wi = a.n_rt > 1 ? xcd_range_index(blockIdx.x, a.G) : (int)blockIdx.x;
+  const int bund = wi / a.n_rt, tile = wi - bund * a.n_rt;
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
   int sel_off[RING_DMA_PER_WAVE];  // per-lane constants of this wave's ring loads
   if constexpr (!F8) ring_dma_offsets(sel_off, wave, lane);
@@ -889,8 +892,11 @@ constexpr int R128_NS = 3;                    // ring stages
 constexpr int R128_O_BYTES = R128_ROWS * D_V * 2;                 // fp16 partial O of a slot
 constexpr int R128_SLOT_BYTES = R128_O_BYTES + 3 * R128_ROWS * 4;  // + m, l, lo per row (fp32)
 constexpr int R128_BT_WIN = 1024;             // block-table entries held in LDS per sub-piece
-constexpr int R128_QREG = 28;                 // Q^T k-steps (of 16 dims) kept in registers; the rest in LDS
-constexpr int R128_QLDS = 36 - R128_QREG;
+// Q^T k-steps (of 16 dims) kept in registers; the rest in LDS.  The FP8
+// instance's ring takes half the LDS, so it moves more of Q^T there and
+// frees registers for its conversions.
+template <bool F8> constexpr int r128_qreg = F8 ? 20 : 28;
+template <bool F8> constexpr int r128_qlds = 36 - r128_qreg<F8>;
 constexpr int R128_PROW = 80;                 // LDS bytes per row of the P tile (64 + 16: conflict-free reads)
 constexpr float R128_RESCALE_LOG2 = 8.f;
 
@@ -910,6 +916,32 @@ __device__ __forceinline__ RingRows r128_tile_rows(const DecodeArgs& a, const in
       rowp = a.kv + ((int64_t)blk * a.bs + (t & (a.bs - 1))) * ROW_BYTES;
   }
   return ring_rows(rowp, stage_lds);
+}
+
+// FP8 cache: source addresses of this wave's loads of tile [ts, ts+32) (the
+// layout and load split of the 16-row kernel's FP8 key items).
+__device__ __forceinline__ F8Loads r128f8_loads(const DecodeArgs& a, const int* bt_lds, int e0, int ts, int k1,
+                                                uint32_t stage_lds, int wave, int lane) {
+  F8Loads L;
+  L.lds = stage_lds;
+  const uint8_t* zero = reinterpret_cast<const uint8_t*>(kZeroRow);
+#pragma unroll
+  for (int m = 0; m < 5; ++m) {
+    const int P = 64 * (wave + 4 * m) + lane;
+    const int r = P / (M16F8_ROW / 16), q = P - (M16F8_ROW / 16) * r;
+    const int ch = f8_chunk_at(r, q);
+    const int t = ts + r;
+    const uint8_t* p = zero + 16 * ch;
+    asm volatile("" : "+v"(p));
+    if (wave + 4 * m < M16F8_LOADS && t < k1) {
+      const int vb = t >> a.bs_shift;
+      const int blk = bt_lds[vb - e0];
+      if ((unsigned)blk < (unsigned)a.num_blocks)
+        p = a.kv + ((int64_t)blk * a.bs + (t & (a.bs - 1))) * M16F8_ROW + 16 * ch;
+    }
+    L.p[m] = p;
+  }
+  return L;
 }
 
 // Per-lane LDS byte offsets inside a stage, fixed for the whole kernel (the
@@ -954,11 +986,16 @@ struct R128State {
 
 // One 32-key tile; the nine ring loads of a later tile (nxt) are issued one
 // every four score MFMAs.
-__device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R128_QREG], const uint8_t* q_tail,
+// FP8 cache (F8): the stage holds E4M3 rows with rotated chunks; score and
+// value fragments are 8-byte reads (value ones transposed) widened to bf16
+// in registers, and the ring loads of a later tile (five or four per wave)
+// are issued one every eight score MFMAs.
+template <bool F8, class Issue>
+__device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[r128_qreg<F8>], const uint8_t* q_tail,
                                              const uint8_t* stage, uint8_t* p_lds, float* alpha_lds,
                                              float scale_log2, int ts, int k1, int nrow, int kfull, int lane,
-                                             int wave, const RingRows& nxt,
-                                             const int (&sel_off)[RING_DMA_PER_WAVE], const R128LaneOff& lo) {
+                                             int wave, Issue&& issue, const R128LaneOff& lo) {
+  constexpr int R128_QREG = r128_qreg<F8>;
   const int r = lane & 31, h = lane >> 5;
   // ---- scores of this wave's rows: S^T[key][row], lane holds keys
   // 8*(i/4) + 4h + i%4 of row r
@@ -966,26 +1003,45 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R
   const uint8_t* kp[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) kp[b] = stage + lo.k[b];
+  // FP8: k-step kk (dims 16kk .. +15) is chunk kk of key row r, half h
+  const uint8_t* kp8 = stage + M16F8_ROW * r + 8 * h;
+  const int krot = f8_rot(r);
+  auto k8_at = [&](int kk) __attribute__((always_inline)) {
+    const int pos = kk < 32 ? (kk + krot) & 31 : 32 + ((kk + krot) & 3);
+    return *reinterpret_cast<const uint2*>(kp8 + 16 * pos);
+  };
   // K fragments (and the last k-steps of Q^T, from this wave's LDS copy laid
   // out [kk][lane]) are read three k-steps ahead of their MFMA
   bf16x8 kf[4], qt[4];
+  uint2 k8[4];
   auto q_at = [&](int kk) __attribute__((always_inline)) {
     return *reinterpret_cast<const bf16x8*>(q_tail + ((kk - R128_QREG) * 64 + lane) * 16);
   };
 #pragma unroll
   for (int kk = 0; kk < 3; ++kk) {
-    kf[kk] = *reinterpret_cast<const bf16x8*>(kp[kk & 3] + 128 * (kk >> 2));
+    if constexpr (F8)
+      k8[kk] = k8_at(kk);
+    else
+      kf[kk] = *reinterpret_cast<const bf16x8*>(kp[kk & 3] + 128 * (kk >> 2));
     if (kk >= R128_QREG) qt[kk % 4] = q_at(kk);
   }
 #pragma unroll
   for (int kk = 0; kk < 36; ++kk) {
     if (kk + 3 < 36) {
-      kf[(kk + 3) % 4] = *reinterpret_cast<const bf16x8*>(kp[(kk + 3) & 3] + 128 * ((kk + 3) >> 2));
+      if constexpr (F8)
+        k8[(kk + 3) % 4] = k8_at(kk + 3);
+      else
+        kf[(kk + 3) % 4] = *reinterpret_cast<const bf16x8*>(kp[(kk + 3) & 3] + 128 * ((kk + 3) >> 2));
       if (kk + 3 >= R128_QREG) qt[(kk + 3) % 4] = q_at(kk + 3);
     }
-    if ((kk & 3) == 0) ring_issue_one(nxt, kk >> 2, wave, sel_off);
+    if constexpr (F8) {
+      if ((kk & 7) == 0) issue(kk >> 3);
+    } else {
+      if ((kk & 3) == 0) issue(kk >> 2);
+    }
     const bf16x8 qv = kk < R128_QREG ? qf[kk < R128_QREG ? kk : 0] : qt[kk % 4];
-    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % 4], qv, sc, 0, 0, 0);
+    const bf16x8 kv = F8 ? f8x8_to_bf16(k8[kk % 4].x, k8[kk % 4].y) : kf[kk % 4];
+    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qv, sc, 0, 0, 0);
     // keep each step's reads three steps ahead of their MFMA (the scheduler
     // would otherwise sink them next to their use)
     __builtin_amdgcn_sched_barrier(0);
@@ -1071,6 +1127,34 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R
 #pragma unroll
     for (int dp = 0; dp < 2; ++dp) vp[rd][dp] = stage + lo.v[rd][dp];
   const uint8_t* pb = p_lds + r * R128_PROW + 16 * h;
+  if constexpr (F8) {
+    // an 8-bit transposed read per (ks, d): in 16-lane group q = lane/16,
+    // lanes 2e and 2e+1 address the halves of key 16ks + 8h + e, value chunk
+    // 2D + q%2 (D = 4w + d), and lane i16 receives value column
+    // 32D + 16(q%2) + i16 of the 8 keys: the A operand of the PV MFMA
+    const int i16 = lane & 15, qg = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 bp[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) bp[rb] = *reinterpret_cast<const bf16x8*>(pb + 32 * rb * R128_PROW + 32 * ks);
+      const int key = 16 * ks + 8 * h + (i16 >> 1);
+      const uint8_t* vrow = stage + M16F8_ROW * key + 8 * (i16 & 1);
+      const int vc = f8_rot(key) + 8 * wave + (qg & 1);
+      i32x2 v[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        v[d] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vrow + 16 * ((vc + 2 * d) & 31)));
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const bf16x8 av = f8x8_to_bf16((uint32_t)v[d].x, (uint32_t)v[d].y);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+          st.o[4 * d + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bp[rb], st.o[4 * d + rb], 0, 0, 0);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     bf16x8 bp[4];
@@ -1094,9 +1178,13 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[R
   }
 }
 
+template <bool F8>
 __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[R128_NS * R128_STAGE];
+  // FP8 cache: stages of 18 KiB (32 rows of 576 E4M3 bytes)
+  constexpr int STAGE = F8 ? M16F8_RAW : R128_STAGE;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[R128_NS * STAGE];
   __shared__ int bt_lds[R128_BT_WIN];
+  constexpr int R128_QREG = r128_qreg<F8>, R128_QLDS = r128_qlds<F8>;
   __shared__ __attribute__((aligned(16))) uint8_t q_tail_lds[4][R128_QLDS * 64 * 16];
   __shared__ __attribute__((aligned(16))) uint8_t p_lds[R128_ROWS * R128_PROW];
   __shared__ float alpha_lds[R128_ROWS];
@@ -1158,24 +1246,50 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
       // prologue: tiles 0 and 1
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        const RingRows rr = r128_tile_rows(a, bt_lds, e0, ka + p * R128_TILE, kb, ring_lds + p * R128_STAGE, wave, lane);
-        ring_issue_all(rr, wave, dma_sel_off);
+        if constexpr (F8) {
+          const F8Loads L = r128f8_loads(a, bt_lds, e0, ka + p * R128_TILE, kb, ring_lds + p * STAGE, wave, lane);
+#pragma unroll
+          for (int m = 0; m < 5; ++m) m16f8_issue(L, m, wave);
+        } else {
+          const RingRows rr = r128_tile_rows(a, bt_lds, e0, ka + p * R128_TILE, kb, ring_lds + p * STAGE, wave, lane);
+          ring_issue_all(rr, wave, dma_sel_off);
+        }
       }
       // stage offsets of tiles it and it+2, rotated instead of computed
       // from it % 3 (which costs every LDS address extra instructions)
-      uint32_t cur = 0, nxt_off = 2 * R128_STAGE;
+      uint32_t cur = 0, nxt_off = 2 * STAGE;
       for (int it = 0; it < nt; ++it) {
+        // FP8: the source addresses of tile it+2's loads need only the block
+        // table window, so they are resolved while the wait below runs
+        F8Loads nxt8;
+        if constexpr (F8)
+          nxt8 = r128f8_loads(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb, ring_lds + nxt_off, wave, lane);
         // tile it landed (only tile it+1 may still be in flight), then
         // every wave is also done with tile it-1 (its stage and the P tile) ...
-        WAIT_VMCNT(R128_DMA_PER_WAVE);  // tile it+1's 9 loads may stay in flight
+        if constexpr (F8) {
+          if (wave < 2)
+            WAIT_VMCNT(5);  // tile it+1's five loads may stay in flight
+          else
+            WAIT_VMCNT(4);
+        } else {
+          WAIT_VMCNT(R128_DMA_PER_WAVE);  // tile it+1's 9 loads may stay in flight
+        }
         __syncthreads();
         // ... so its stage can take tile it+2, loaded while tile it is computed
-        const RingRows nxt = r128_tile_rows(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb, ring_lds + nxt_off, wave,
-                                            lane);
-        r128_compute(st, qf, q_tail, ring + cur, p_lds, alpha_lds, a.scale_log2, ka + it * R128_TILE, kb, nrow,
-                     min(kb, nmin), lane, wave, nxt, dma_sel_off, lane_off);
+        if constexpr (F8) {
+          r128_compute<true>(st, qf, q_tail, ring + cur, p_lds, alpha_lds, a.scale_log2, ka + it * R128_TILE, kb,
+                             nrow, min(kb, nmin), lane, wave,
+                             [&](int m) __attribute__((always_inline)) { m16f8_issue(nxt8, m, wave); }, lane_off);
+        } else {
+          const RingRows nxt = r128_tile_rows(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb, ring_lds + nxt_off, wave,
+                                              lane);
+          r128_compute<false>(st, qf, q_tail, ring + cur, p_lds, alpha_lds, a.scale_log2, ka + it * R128_TILE, kb,
+                              nrow, min(kb, nmin), lane, wave,
+                              [&](int m) __attribute__((always_inline)) { ring_issue_one(nxt, m, wave, dma_sel_off); },
+                              lane_off);
+        }
         nxt_off = cur;
-        cur = __builtin_amdgcn_readfirstlane(cur == (R128_NS - 1) * R128_STAGE ? 0u : cur + R128_STAGE);
+        cur = __builtin_amdgcn_readfirstlane(cur == (R128_NS - 1) * STAGE ? 0u : cur + STAGE);
       }
       WAIT_VMCNT(0);
     }
@@ -1383,9 +1497,9 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool allow_r12
   // (8 * k bundles, each XCD holding k whole bundles) so that they share the
   // keys through its L2; a few CUs idle when n_rt does not divide the CUs of
   // an XCD.
-  const int per_xcd = cus / 8;
-  int64_t nbund = (p.rows_tile == R128_ROWS && p.n_rt <= per_xcd) ? 8 * (per_xcd / p.n_rt)
-                  : (int64_t)(fp8 ? M16F8_WG_PER_CU : 1) * cus / p.n_rt;
+  // The 16-row kernel does the same when a request has several row tiles.
+  const int per_xcd = (p.rows_tile == R128_ROWS ? 1 : fp8 ? M16F8_WG_PER_CU : 1) * cus / 8;  // resident workgroups
+  int64_t nbund = p.n_rt == 1 ? 8 * per_xcd : p.n_rt <= per_xcd ? 8 * (per_xcd / p.n_rt) : 8 * per_xcd / p.n_rt;
   if (nbund < 1) nbund = 1;
   const int64_t units = (int64_t)B * ((max_seq_len > 0 ? max_seq_len : 1) + p.ovh);  // of one row tile
   const int64_t by_work = (units + 255) / 256;  // at least 256 keys per workgroup
@@ -1419,7 +1533,7 @@ extern "C" size_t mla_decode_workspace_size(int B, int q_len, int H, int max_seq
   size_t m = 0;
   for (const bool r128 : {true, false})
     for (const bool fp8 : {false, true}) {
-      const size_t x = make_plan(B, q_len, H, max_seq_len, cus, r128 && !fp8, fp8).bytes;
+      const size_t x = make_plan(B, q_len, H, max_seq_len, cus, r128, fp8).bytes;
       m = x > m ? x : m;
     }
   return m;
@@ -1444,8 +1558,7 @@ int decode(const void* q, const int32_t* query_start_loc, const void* kv_cache, 
   if (B == 0) return MLA_OK;
   if (!q || !kv_cache || !block_table || !seq_lens || !out) return MLA_ERR_INVALID_ARG;
   const bool pow2_bs = (block_size & (block_size - 1)) == 0;
-  // an FP8 cache runs on the 16-row kernel only (row tiles of any count)
-  const Plan p = make_plan(B, q_len, H, max_seq_len, device_cu_count(), pow2_bs && !kv_fp8, kv_fp8 != 0);
+  const Plan p = make_plan(B, q_len, H, max_seq_len, device_cu_count(), pow2_bs, kv_fp8 != 0);
   if (workspace_bytes < p.bytes || workspace == nullptr) return MLA_ERR_INVALID_ARG;
 
   DecodeArgs a{};
@@ -1474,12 +1587,14 @@ int decode(const void* q, const int32_t* query_start_loc, const void* kv_cache, 
   a.lse = lse;
 
   if (tl_prof_start) (void)hipEventRecord(tl_prof_start, stream);
-  if (kv_fp8)
+  if (p.rows_tile == M16_ROWS && kv_fp8)
     hipLaunchKernelGGL(attn_m16_kernel<true>, dim3(p.G), dim3(M16_THREADS), 0, stream, a);
   else if (p.rows_tile == M16_ROWS)
     hipLaunchKernelGGL(attn_m16_kernel<false>, dim3(p.G), dim3(M16_THREADS), 0, stream, a);
+  else if (kv_fp8)
+    hipLaunchKernelGGL(attn_r128_kernel<true>, dim3(p.G), dim3(R128_THREADS), 0, stream, a);
   else
-    hipLaunchKernelGGL(attn_r128_kernel, dim3(p.G), dim3(R128_THREADS), 0, stream, a);
+    hipLaunchKernelGGL(attn_r128_kernel<false>, dim3(p.G), dim3(R128_THREADS), 0, stream, a);
   if (tl_prof_stop) (void)hipEventRecord(tl_prof_stop, stream);
   if (p.rows_tile == M16_ROWS)
     hipLaunchKernelGGL(combine_kernel<M16_ROWS>, dim3(B * p.n_rt * 8), dim3(256), 0, stream, a);

@@ -125,6 +125,16 @@ def test_fp8_equals_bf16_path_to_rounding():
     assert float((l8 - l16).abs().max()) <= 1e-5
 
 
+def test_fp8_equals_bf16_path_bitwise_in_the_128_row_kernel():
+    # more than 16 rows per request: both calls take the 128-row kernel with
+    # the same plan, and its k-steps are summed in the same order whatever
+    # the cache type, so the results are identical
+    o8, l8, o16, l16 = fp8_and_bf16_runs(spec("fp8_vs_bf16_h128", 3, 128, 4, True, [70, 900, 2600],
+                                              global_is_null=True, kv_scale=1.0))
+    assert torch.equal(o8, o16)
+    assert torch.equal(l8, l16)
+
+
 def test_fp8_cache_scale_scales_scores_and_values():
     """Codes c with scale s against codes c with scale 2s: the second equals
     the first with the query doubled (scores) and the output doubled."""
@@ -156,3 +166,19 @@ def test_fp8_full_size_decode_on_sampled_rows():
     ro, rl = oracle.mla_decode(wl.q_bits, wl.global_rows, wl.seq_lens[0], None, 1, 0, True, sp.scale, "e",
                                rows=rows, kv_scale=sp.kv_scale)
     compare(out, lse, ro, rl, f"{sp.name} fp8", rows=[(b, h) for (b, _, h) in rows])
+
+
+def test_fp8_full_size_spec_decode_on_sampled_rows():
+    sp = WL.config(3, kv_dtype="fp8", kv_scale=1.0 / 64)
+    say(f"{sp.name} fp8: generating")
+    wl = WL.build(sp)
+    up = Uploaded(wl)
+    out, lse = up.run(0, max_seq_len=int(wl.seq_lens[0].max()))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out.float()).all()) and bool(torch.isfinite(lse).all())
+    rng = np.random.default_rng(3003)
+    rows = sorted({(int(rng.integers(sp.B)), int(rng.integers(sp.Q)), int(rng.integers(sp.H))) for _ in range(20)}
+                  | {(int(np.argmax(wl.tot)), sp.Q - 1, sp.H - 1), (int(np.argmin(wl.tot)), 0, 0)})
+    ro, rl = oracle.mla_decode(wl.q_bits, wl.global_rows, wl.seq_lens[0], None, 1, 0, True, sp.scale, "e",
+                               rows=rows, kv_scale=sp.kv_scale)
+    compare(out, lse, ro, rl, f"{sp.name} fp8", rows=[(b * sp.Q + j, h) for (b, j, h) in rows])
