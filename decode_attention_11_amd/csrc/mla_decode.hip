@@ -922,6 +922,11 @@ __device__ __forceinline__ RingRows r128_tile_rows(const DecodeArgs& a, const in
 // layout and load split of the 16-row kernel's FP8 key items).
 __device__ __forceinline__ F8Loads r128f8_loads(const DecodeArgs& a, const int* bt_lds, int e0, int ts, int k1,
                                                 uint32_t stage_lds, int wave, int lane) {
+  // the per-lane parts of the addresses (chunk positions, zero-row
+  // defaults) are recomputed for every tile: hoisted out of the tile loop
+  // they are spilled, and each reload's wait would also drain the ring loads
+  // still in flight
+  asm volatile("" : "+v"(lane));
   F8Loads L;
   L.lds = stage_lds;
   const uint8_t* zero = reinterpret_cast<const uint8_t*>(kZeroRow);
