@@ -115,6 +115,44 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
+# ------------------------------------------------------------------ step parts
+def step_parts(torch, hip, stream, n, ranks, slot_jobs, s, mla, bt, outs, lses, merged, T):
+    """The step's parts timed apart with HIP events, n repetitions each: the
+    slot mapping of the step's tokens (every rank), and for a sharded step
+    the LSE merge, whose bytes (the ranks' bf16 partials and fp32 LSEs read,
+    the merged pair written) give its HBM rate."""
+    def timed(fn):
+        # a device-side spin first, so that the n calls are all queued before
+        # the first runs and the events see GPU time, not Python launch time
+        a, b = hip.event(), hip.event()
+        torch.cuda._sleep(4_000_000)
+        hip.record(a, stream)
+        for _ in range(n):
+            fn()
+        hip.record(b, stream)
+        ms = hip.elapsed_ms(a, b) / n
+        hip.destroy(a)
+        hip.destroy(b)
+        return ms
+
+    def slots():
+        for r in ranks:
+            for pos, nv in slot_jobs:
+                mla.cp_local_slot(pos, bt, s.block_size, s.W, r, nv, cp_interleave=s.interleave)
+
+    out = {"slot_calls_per_step": len(ranks) * len(slot_jobs), "slot_us_per_step": round(timed(slots) * 1e3, 2)}
+    if s.W > 1 and len(ranks) == s.W:
+        def merge():
+            mla.mla_merge_lse([outs[r] for r in ranks], [lses[r] for r in ranks], s.lse_base,
+                              out=merged[0], lse=merged[1])
+        ms = timed(merge)
+        nbytes = (len(ranks) + 1) * T * s.H * (512 * 2 + 4)
+        out.update({"merge_us": round(ms * 1e3, 2), "merge_bytes": nbytes,
+                    "merge_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                    "merge_frac_of_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)})
+    return out
+
+
 # ------------------------------------------------------------------ achievable peaks
 def measured_peaks(torch, hip, stream, dev, reps=5):
     """Achievable HBM and bf16 matrix rates on this GPU, measured with torch
@@ -404,6 +442,9 @@ def main():
         if t.get("source_hash") == source_hash():
             traffic = t.get("bytes_per_launch")
     roof["traffic"] = traffic
+    log("step parts, each timed on its own")
+    parts = step_parts(torch, hip, stream, args.steps, ranks, slot_jobs, s, mla, bt, outs, lses, merged, T)
+    parts["attention_ms_per_step"] = round(avg_attn_ms * len(ranks), 5)
     log("kv write: the step's new-token rows, and a bulk scatter")
     r0 = ranks[0]
     pos0, nv0 = slot_jobs[0]
@@ -439,7 +480,7 @@ def main():
         "tflops": round(tflops, 3), "kv_gbps": round(kv_gbps, 1),
         "alg_bytes_per_step": int(step_alg_bytes), "flops_per_step": int(step_flops),
         "attention_kernel_ms": round(avg_attn_ms, 5), "source_hash": source_hash(),
-        "roofline": roof, "measured_peaks": peaks, "kv_write": kvw,
+        "roofline": roof, "measured_peaks": peaks, "kv_write": kvw, "parts": parts,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a bounded sample")
