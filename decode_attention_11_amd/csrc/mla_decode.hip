@@ -1100,6 +1100,33 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[r
   st.l_out = sum_bf16x8(__builtin_shufflevector(p4[2], p4[3], 0, 1, 2, 3, 4, 5, 6, 7), st.l_out);
   if (h == 0) alpha_lds[32 * wave + r] = alpha;
   __syncthreads();
+  // O^T[dv][row] += V^T[dv][key] P^T[key][row] over 2 k-steps of 16 keys:
+  // contraction slot 8h + s is key 16ks + 8h + s on both sides.
+  //   B (P^T): lane reads keys 16ks + 8h .. +7 of row 32rb + r (16 bytes).
+  //   A (V^T): two transposed reads, keys 16ks + 8h + 4rd + (i16/4), value
+  //   columns 32D + 16(q%2) + 4(i16%4) .. +3 for D = 4w + d (q = lane/16,
+  //   i16 = lane%16): logical chunk 4D + 2(q%2) + (i16%4)/2, byte 8(i16%2).
+  const uint8_t* vp[2][2];  // [rd][d%2]
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+    for (int dp = 0; dp < 2; ++dp) vp[rd][dp] = stage + lo.v[rd][dp];
+  const uint8_t* pb = p_lds + r * R128_PROW + 16 * h;
+  bf16x8 bp[2][4];
+  i16x4 v[2][4][2];
+  auto pv_operands = [&](int ks) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) bp[ks][rb] = *reinterpret_cast<const bf16x8*>(pb + 32 * rb * R128_PROW + 32 * ks);
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int rd = 0; rd < 2; ++rd)
+        v[ks][d][rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vp[rd][d & 1] + 16 * ks * R128_ROWB + 128 * (d >> 1)));
+  };
+  // bf16: the first k-step's operands are read before the rescale check,
+  // so their LDS latency overlaps it
+  if constexpr (!F8) pv_operands(0);
   // ---- this wave's value columns for all 128 rows.  The accumulator
   // column of lane l is row 32rb + l%32 in block rb: rescale the blocks whose
   // rows moved their reference (rare)
@@ -1120,18 +1147,6 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[r
                        : "+a"(st.o[4 * d + rb][i]), "=&v"(tmp) : "v"(ab[rb]));
         }
   }
-  // O^T[dv][row] += V^T[dv][key] P^T[key][row] over 2 k-steps of 16 keys:
-  // contraction slot 8h + s is key 16ks + 8h + s on both sides.
-  //   B (P^T): lane reads keys 16ks + 8h .. +7 of row 32rb + r (16 bytes).
-  //   A (V^T): two transposed reads, keys 16ks + 8h + 4rd + (i16/4), value
-  //   columns 32D + 16(q%2) + 4(i16%4) .. +3 for D = 4w + d (q = lane/16,
-  //   i16 = lane%16): logical chunk 4D + 2(q%2) + (i16%4)/2, byte 8(i16%2).
-  const uint8_t* vp[2][2];  // [rd][d%2]
-#pragma unroll
-  for (int rd = 0; rd < 2; ++rd)
-#pragma unroll
-    for (int dp = 0; dp < 2; ++dp) vp[rd][dp] = stage + lo.v[rd][dp];
-  const uint8_t* pb = p_lds + r * R128_PROW + 16 * h;
   if constexpr (F8) {
     // an 8-bit transposed read per (ks, d): in 16-lane group q = lane/16,
     // lanes 2e and 2e+1 address the halves of key 16ks + 8h + e, value chunk
@@ -1162,23 +1177,14 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[r
   }
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    bf16x8 bp[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) bp[rb] = *reinterpret_cast<const bf16x8*>(pb + 32 * rb * R128_PROW + 32 * ks);
-    i16x4 v[4][2];
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int rd = 0; rd < 2; ++rd)
-        v[d][rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vp[rd][d & 1] + 16 * ks * R128_ROWB + 128 * (d >> 1)));
+    if (ks > 0) pv_operands(ks);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const bf16x8 av = __builtin_shufflevector(__builtin_bit_cast(bf16x4, v[d][0]), __builtin_bit_cast(bf16x4, v[d][1]),
-                                                0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 av = __builtin_shufflevector(__builtin_bit_cast(bf16x4, v[ks][d][0]),
+                                                __builtin_bit_cast(bf16x4, v[ks][d][1]), 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
-        st.o[4 * d + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bp[rb], st.o[4 * d + rb], 0, 0, 0);
+        st.o[4 * d + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bp[ks][rb], st.o[4 * d + rb], 0, 0, 0);
     }
   }
 }
