@@ -395,19 +395,25 @@ def main():
     torch.cuda.synchronize()
 
     n_launch = args.steps * len(ranks)
-    pairs = [(hip.event(), hip.event()) for _ in range(n_launch)]
-    todo = list(reversed(pairs))
     t_start, t_stop = hip.event(), hip.event()
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     hip.record(t_start, stream)
     for i in range(args.steps):
-        step(i, todo)
+        step(i)
     hip.record(t_stop, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     total_ms = hip.elapsed_ms(t_start, t_stop)
+    # the attention kernel alone: the same steps again, with events around
+    # each attention launch (kept out of the step timing above)
+    log(f"timing the attention kernel over {args.steps} more steps")
+    pairs = [(hip.event(), hip.event()) for _ in range(n_launch)]
+    todo = list(reversed(pairs))
+    for i in range(args.steps):
+        step(i, todo)
+    torch.cuda.synchronize()
     attn_ms = [hip.elapsed_ms(a, b_) for a, b_ in pairs]
     for a, b_ in pairs:
         hip.destroy(a)
