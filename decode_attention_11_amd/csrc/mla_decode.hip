@@ -31,6 +31,7 @@
 // normalised by the sum of those same rounded values (a row dominated by one
 // key then reproduces that key's value row instead of being off by the
 // rounding of its weight), while the LSE uses the fp32 sum.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <cmath>
 #include <cstdint>
@@ -1597,16 +1598,22 @@ int decode(const void* q, const int32_t* query_start_loc, const void* kv_cache, 
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
 
-  if (tl_prof_start) (void)hipEventRecord(tl_prof_start, stream);
+  // the attention kernel; with profiling events set, the runtime records
+  // them at the kernel's own start and end (no separate marker packets)
+  auto attention = [&](auto kernel, int threads) {
+    if (tl_prof_start)
+      hipExtLaunchKernelGGL(kernel, dim3(p.G), dim3(threads), 0, stream, tl_prof_start, tl_prof_stop, 0, a);
+    else
+      hipLaunchKernelGGL(kernel, dim3(p.G), dim3(threads), 0, stream, a);
+  };
   if (p.rows_tile == M16_ROWS && kv_fp8)
-    hipLaunchKernelGGL(attn_m16_kernel<true>, dim3(p.G), dim3(M16_THREADS), 0, stream, a);
+    attention(attn_m16_kernel<true>, M16_THREADS);
   else if (p.rows_tile == M16_ROWS)
-    hipLaunchKernelGGL(attn_m16_kernel<false>, dim3(p.G), dim3(M16_THREADS), 0, stream, a);
+    attention(attn_m16_kernel<false>, M16_THREADS);
   else if (kv_fp8)
-    hipLaunchKernelGGL(attn_r128_kernel<true>, dim3(p.G), dim3(R128_THREADS), 0, stream, a);
+    attention(attn_r128_kernel<true>, R128_THREADS);
   else
-    hipLaunchKernelGGL(attn_r128_kernel<false>, dim3(p.G), dim3(R128_THREADS), 0, stream, a);
-  if (tl_prof_stop) (void)hipEventRecord(tl_prof_stop, stream);
+    attention(attn_r128_kernel<false>, R128_THREADS);
   if (p.rows_tile == M16_ROWS)
     hipLaunchKernelGGL(combine_kernel<M16_ROWS>, dim3(B * p.n_rt * 8), dim3(256), 0, stream, a);
   else

@@ -207,8 +207,10 @@ int mla_decode_fp8(const void* q, const void* kv_cache, float kv_scale, const in
 
 /*
  * Profiling aid (not part of the computation): for the calling host thread,
- * record `start` just before and `stop` just after the split-KV attention
- * kernel of each following mla_decode call, on that call's stream.  Pass two
+ * record `start` at the start and `stop` at the end of the split-KV
+ * attention kernel of each following mla_decode call (the kernel is then
+ * launched with hipExtLaunchKernel, which records both events as part of its
+ * dispatch on that call's stream).  Pass two
  * NULLs to stop.  The events are created and owned by the caller; each call
  * re-records them, so a caller timing several calls sets a fresh pair before
  * each.  Returns MLA_ERR_INVALID_ARG if exactly one of them is NULL.
