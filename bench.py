@@ -490,7 +490,10 @@ def main():
                    "kv_replicas": replicas, "kv_cache": "fp8_e4m3" if s.kv_dtype == "fp8" else "bf16"},
         "tflops": round(tflops, 3), "kv_gbps": round(kv_gbps, 1),
         "alg_bytes_per_step": int(step_alg_bytes), "flops_per_step": int(step_flops),
-        "attention_kernel_ms": round(avg_attn_ms, 5), "ms_per_step_without_kernel_events": round(plain_ms_per_step, 5),
+        "attention_kernel_ms": round(avg_attn_ms, 5),
+        "attention_kernel_ms_median": round(float(np.median(attn_ms)), 5),
+        "attention_kernel_ms_min": round(float(min(attn_ms)), 5),
+        "ms_per_step_without_kernel_events": round(plain_ms_per_step, 5),
         "source_hash": source_hash(),
         "roofline": roof, "measured_peaks": peaks, "kv_write": kvw, "parts": parts,
     }
