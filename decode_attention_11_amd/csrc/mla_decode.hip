@@ -1497,13 +1497,13 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool allow_r12
   p.rows_tile = (R <= M16_ROWS || !allow_r128) ? M16_ROWS : R128_ROWS;
   p.n_rt = (int)((R + p.rows_tile - 1) / p.rows_tile);
   // per-group overhead in key units, about what a group's start and end
-  // cost in ring time: M16 ~2 tiles (the query item, a partial tile and the
-  // 33 KB partial store), ~4.5 with an FP8 cache (its tiles carry half the
-  // bytes, the query item and the store do not shrink), R128 ~3 tiles
-  // (query load, ring refill and the 130 KB partial store); measured on the
-  // batch-64 single-token workload, where workgroups with two pieces had
-  // ended last
-  p.ovh = p.rows_tile == M16_ROWS ? (fp8 ? 144 : 64) : 96;
+  // cost in ring time: M16 5 tiles (the query item, a partial tile, the
+  // 33 KB partial store and the pipeline refill behind them; 160 units ran
+  // about 1% faster than 64, 128, 192 or 256 on the batch-64 single-token
+  // workload), 4.5 with an FP8 cache (its tiles carry half the bytes, the
+  // query item and the store do not shrink), R128 ~3 tiles (query load,
+  // ring refill and the 130 KB partial store)
+  p.ovh = p.rows_tile == M16_ROWS ? (fp8 ? 144 : 160) : 96;
   // bundles: balanced key ranges, each processed by n_rt workgroups (one per
   // row tile).  The 128-row kernel keeps a bundle's workgroups on one XCD
   // (8 * k bundles, each XCD holding k whole bundles) so that they share the
