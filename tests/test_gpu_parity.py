@@ -295,3 +295,46 @@ def test_slots_large_positions_int64():
     exp = oracle.cp_local_slot(pos, bt, 64, 2, 1)
     np.testing.assert_array_equal(got.cpu().numpy(), exp)
     assert exp[0, 1] == 2_000_000_000 * 64
+
+
+PROFILED = [
+    WL.Spec(name="profiled_m16", B=3, H=16, Q=1, causal=True, seed=71, lengths=[50, 700, 2100]),
+    WL.Spec(name="profiled_r128", B=2, H=128, Q=4, causal=True, seed=72, lengths=[90, 1500]),
+    WL.Spec(name="profiled_m16_fp8", B=2, H=16, Q=1, causal=True, seed=73, lengths=[300, 1000], kv_dtype="fp8",
+            kv_scale=0.5),
+]
+
+
+@pytest.mark.parametrize("sp", PROFILED, ids=[s.name for s in PROFILED])
+def test_profiling_events_leave_results_unchanged(sp):
+    """With profiling events set, the attention kernel is launched through
+    the path that records them at its start and end; the results must be
+    the same bits, and the events must bracket a positive duration."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    say(sp.name)
+    up = Uploaded(WL.build(sp))
+    o1, l1 = up.run(0)
+    ev = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e in ev:
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+    try:
+        mla.profile_attention_events(ev[0].value, ev[1].value)
+        try:
+            o2, l2 = up.run(0)
+        finally:
+            mla.profile_attention_events(None, None)
+        torch.cuda.synchronize()
+        assert hip.hipEventSynchronize(ev[1]) == 0
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
+        assert ms.value > 0.0
+    finally:
+        for e in ev:
+            hip.hipEventDestroy(e)
+    assert torch.equal(o1, o2)
+    assert torch.equal(l1, l2)
