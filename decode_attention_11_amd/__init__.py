@@ -113,6 +113,12 @@ def _need(t: torch.Tensor, name: str, dtype, dim: Optional[int] = None) -> None:
         raise ValueError(f"{name} must have {dim} dims, got shape {tuple(t.shape)}")
 
 
+def _same_device(device, **tensors) -> None:
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device} (every tensor of a call on one GPU)")
+
+
 def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -179,6 +185,8 @@ def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
     if base is None:
         raise ValueError("lse_base must be 'e' or '2'")
     dev = q.device
+    _same_device(dev, kv_cache=kv_cache, block_table=block_table, seq_lens=seq_lens,
+                 causal_seqlens_global=causal_seqlens_global, out=out, lse=lse, workspace=workspace)
     if out is None:
         out = torch.empty((B * Q, H, D_V), dtype=torch.bfloat16, device=dev)
     else:
@@ -230,10 +238,16 @@ def mla_merge_lse(partials: Sequence[torch.Tensor], lses: Sequence[torch.Tensor]
     if base is None:
         raise ValueError("lse_base must be 'e' or '2'")
     dev = partials[0].device
+    _same_device(dev, **{f"partials[{i}]": p for i, p in enumerate(partials)},
+                 **{f"lses[{i}]": l for i, l in enumerate(lses)}, out=out, lse=lse)
     out = torch.empty((rows, H, D_V), dtype=torch.bfloat16, device=dev) if out is None else out
     lse = torch.empty((rows, H), dtype=torch.float32, device=dev) if lse is None else lse
     _need(out, "out", torch.bfloat16, 3)
     _need(lse, "lse", torch.float32, 2)
+    if tuple(out.shape) != (rows, H, D_V):
+        raise ValueError(f"out must be [{rows}, {H}, {D_V}], got {tuple(out.shape)}")
+    if tuple(lse.shape) != (rows, H):
+        raise ValueError(f"lse must be [{rows}, {H}], got {tuple(lse.shape)}")
     parr = (ctypes.c_void_p * n)(*[p.data_ptr() for p in partials])
     larr = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lses])
     _check(lib.mla_merge_lse(ctypes.cast(parr, ctypes.c_void_p), ctypes.cast(larr, ctypes.c_void_p), n,
@@ -255,8 +269,11 @@ def cp_local_slot(positions: torch.Tensor, block_table: torch.Tensor, block_size
         _need(num_valid, "num_valid", torch.int32, 1)
         if num_valid.shape[0] != B:
             raise ValueError("num_valid must have B entries")
+    _same_device(positions.device, block_table=block_table, num_valid=num_valid, out=out)
     out = torch.empty((B, n), dtype=torch.int64, device=positions.device) if out is None else out
     _need(out, "out", torch.int64, 2)
+    if tuple(out.shape) != (B, n):
+        raise ValueError(f"out must be [{B}, {n}], got {tuple(out.shape)}")
     _check(lib.cp_local_slot(positions.data_ptr(), num_valid.data_ptr() if num_valid is not None else None,
                              int(B), int(n), block_table.data_ptr(), int(block_table.shape[1]),
                              int(block_size), int(cp_world), int(cp_rank), int(cp_interleave),
@@ -286,6 +303,7 @@ def kv_write(kv_new: torch.Tensor, slots: torch.Tensor, kv_cache: torch.Tensor,
     n = kv_new.numel() // D_QK
     if slots.numel() != n or tuple(slots.shape) != tuple(kv_new.shape[:-1]):
         raise ValueError("slots must have one entry per row of kv_new")
+    _same_device(kv_cache.device, kv_new=kv_new, slots=slots)
     if fp8:
         _check(lib.mla_kv_write_fp8(kv_new.data_ptr(), slots.data_ptr(), int(n), float(kv_scale), kv_cache.data_ptr(),
                                     int(kv_cache.shape[0]), int(kv_cache.shape[1]), _stream(kv_cache.device)))
@@ -299,14 +317,15 @@ def mla_decode_varlen(q: torch.Tensor, query_start_loc: torch.Tensor, kv_cache: 
                       block_table: torch.Tensor, seq_lens: torch.Tensor,
                       causal_seqlens_global: Optional[torch.Tensor] = None, cp_world: int = 1, cp_rank: int = 0,
                       causal: bool = True, scale: Optional[float] = None, lse_base: str = "e", *,
-                      max_q_len: Optional[int] = None, max_seq_len: Optional[int] = None,
+                      max_q_len: int, max_seq_len: Optional[int] = None,
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None, return_lse: bool = True, cp_interleave: int = 1
                       ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """One rank's decode for requests with different query lengths: q [T, H, 576] bf16 packs the
     requests' tokens, request b owning tokens query_start_loc[b] .. query_start_loc[b+1]-1.
-    Returns out [T, H, 512] bf16 and lse [T, H] float32.  max_q_len (the largest per-request
-    length) is read from query_start_loc with a host sync when not given."""
+    Returns out [T, H, 512] bf16 and lse [T, H] float32.  max_q_len (keyword, required) is a
+    host upper bound on every request's query length: it sizes the work split without reading
+    query_start_loc back from the GPU, so the call never synchronises with the host."""
     lib = load_library()
     _need(q, "q", torch.bfloat16, 3)
     T, H, Dq = q.shape
@@ -325,9 +344,9 @@ def mla_decode_varlen(q: torch.Tensor, query_start_loc: torch.Tensor, kv_cache: 
         _need(causal_seqlens_global, "causal_seqlens_global", torch.int32, 1)
         if causal_seqlens_global.shape[0] != B:
             raise ValueError("causal_seqlens_global must have B entries")
-    if max_q_len is None:
-        max_q_len = int((query_start_loc[1:] - query_start_loc[:-1]).max().item()) if B > 0 else 1
-    max_q_len = max(int(max_q_len), 1)
+    if max_q_len is None or int(max_q_len) < 1:
+        raise ValueError("max_q_len (a host upper bound on the per-request query lengths) must be >= 1")
+    max_q_len = int(max_q_len)
     num_blocks, bs = int(kv_cache.shape[0]), int(kv_cache.shape[1])
     max_blocks = int(block_table.shape[1])
     if max_seq_len is None:
@@ -338,6 +357,9 @@ def mla_decode_varlen(q: torch.Tensor, query_start_loc: torch.Tensor, kv_cache: 
     if base is None:
         raise ValueError("lse_base must be 'e' or '2'")
     dev = q.device
+    _same_device(dev, query_start_loc=query_start_loc, kv_cache=kv_cache, block_table=block_table,
+                 seq_lens=seq_lens, causal_seqlens_global=causal_seqlens_global, out=out, lse=lse,
+                 workspace=workspace)
     if out is None:
         out = torch.empty((T, H, D_V), dtype=torch.bfloat16, device=dev)
     else:

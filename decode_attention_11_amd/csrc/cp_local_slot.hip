@@ -73,7 +73,6 @@ extern "C" int cp_local_slot(const int64_t* positions, const int32_t* num_valid,
              block_size, cp_world, cp_rank, cp_interleave, slots};
   const int64_t blocks = (total + 255) / 256;
   if (blocks > 0x7FFFFFFF) return MLA_ERR_INVALID_ARG;
-  hipLaunchKernelGGL(slot_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+  if (mla::launch(slot_kernel, dim3((unsigned)blocks), dim3(256), stream, a) != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }

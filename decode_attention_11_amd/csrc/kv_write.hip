@@ -17,6 +17,7 @@
 #include <cstdint>
 
 #include "mla_decode.h"
+#include "mla_device.h"
 
 namespace {
 
@@ -107,8 +108,8 @@ extern "C" int mla_kv_write_fp8(const void* kv_new, const int64_t* slots, int64_
   if (blocks > 0x7FFFFFFF) return MLA_ERR_INVALID_ARG;
   KvWriteF8Args a{static_cast<const uint4*>(kv_new), slots, static_cast<uint4*>(kv_cache), n_rows,
                   (int64_t)num_blocks * block_size, kv_scale};
-  hipLaunchKernelGGL(kv_write_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+  if (mla::launch(kv_write_fp8_kernel, dim3((unsigned)blocks), dim3(256), stream, a) != hipSuccess)
+    return MLA_ERR_HIP;
   return MLA_OK;
 }
 
@@ -125,7 +126,6 @@ extern "C" int mla_kv_write(const void* kv_new, const int64_t* slots, int64_t n_
   if (blocks > 0x7FFFFFFF) return MLA_ERR_INVALID_ARG;
   KvWriteArgs a{static_cast<const uint4*>(kv_new), slots, static_cast<uint4*>(kv_cache), n_rows,
                 (int64_t)num_blocks * block_size};
-  hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+  if (mla::launch(kv_write_kernel, dim3((unsigned)blocks), dim3(256), stream, a) != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }

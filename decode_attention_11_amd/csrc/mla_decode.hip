@@ -870,7 +870,7 @@ __global__ __launch_bounds__(M16_THREADS, F8 ? M16F8_WG_PER_CU : 1) void attn_m1
 
 // ---------------------------------------------------------------- R128 partial
 // Compute-bound family: more than 16 rows per request (multi-token or many
-// heads: 4 x 128 or 16 x 128 rows), power-of-two block sizes.  A workgroup
+// heads: 4 x 128 or 16 x 128 rows), any block size.  A workgroup
 // owns 128 rows of one request and a key range; the 32-key tiles of the latent
 // KV are shared by the four waves through a 3-stage LDS ring.
 //
@@ -891,7 +891,8 @@ constexpr int R128_DMA_PER_WAVE = RING_DMA_PER_WAVE;
 constexpr int R128_STAGE = RING_STAGE;        // 36 KiB
 constexpr int R128_NS = 3;                    // ring stages
 constexpr int R128_O_BYTES = R128_ROWS * D_V * 2;                 // fp16 partial O of a slot
-constexpr int R128_SLOT_BYTES = R128_O_BYTES + 3 * R128_ROWS * 4;  // + m, l, lo per row (fp32)
+// + m, l, lo per row and a power-of-two factor per (value-column quarter, row), fp32
+constexpr int R128_SLOT_BYTES = R128_O_BYTES + 7 * R128_ROWS * 4;
 constexpr int R128_BT_WIN = 1024;             // block-table entries held in LDS per sub-piece
 // Q^T k-steps (of 16 dims) kept in registers; the rest in LDS.  The FP8
 // instance's ring takes half the LDS, so it moves more of Q^T there and
@@ -911,10 +912,10 @@ __device__ __forceinline__ RingRows r128_tile_rows(const DecodeArgs& a, const in
   const uint8_t* rowp = reinterpret_cast<const uint8_t*>(kZeroRow);
   asm volatile("" : "+v"(rowp));
   if (t < k1) {
-    const int vb = t >> a.bs_shift;
+    const int vb = block_of(a, t);
     const int blk = bt_lds[vb - e0];
     if ((unsigned)blk < (unsigned)a.num_blocks)
-      rowp = a.kv + ((int64_t)blk * a.bs + (t & (a.bs - 1))) * ROW_BYTES;
+      rowp = a.kv + ((int64_t)blk * a.bs + (t - vb * a.bs)) * ROW_BYTES;
   }
   return ring_rows(rowp, stage_lds);
 }
@@ -940,10 +941,10 @@ __device__ __forceinline__ F8Loads r128f8_loads(const DecodeArgs& a, const int* 
     const uint8_t* p = zero + 16 * ch;
     asm volatile("" : "+v"(p));
     if (wave + 4 * m < M16F8_LOADS && t < k1) {
-      const int vb = t >> a.bs_shift;
+      const int vb = block_of(a, t);
       const int blk = bt_lds[vb - e0];
       if ((unsigned)blk < (unsigned)a.num_blocks)
-        p = a.kv + ((int64_t)blk * a.bs + (t & (a.bs - 1))) * M16F8_ROW + 16 * ch;
+        p = a.kv + ((int64_t)blk * a.bs + (t - vb * a.bs)) * M16F8_ROW + 16 * ch;
     }
     L.p[m] = p;
   }
@@ -1190,6 +1191,74 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[r
   }
 }
 
+// The partial slot of one 128-row piece (every wave calls it with its own
+// O^T quarter and row state; sums_lds is 128 floats of LDS that no wave still
+// reads).
+__device__ __forceinline__ void r128_store_slot(const DecodeArgs& a, const R128State& st, int64_t slot_idx,
+                                                float* sums_lds, int wave, int lane) {
+  // partial slot: O^T / (the row's bf16 sum of P) in fp16, in the
+  // accumulator layout [dv/32][row][h][i] (the 16 values a lane holds per
+  // 32x32 block are contiguous: 2 x 16-byte stores), then per row m, the
+  // fp32 and the bf16 sums of P, then per (value-column quarter, row) the
+  // power of two the quarter's fp16 values are to be multiplied by.  The
+  // quotients are bounded by the largest |V| of the piece, which can be
+  // any bf16 magnitude: each wave scales its 128 columns of a row so that
+  // their largest magnitude lies in [2^14, 2^15), inside fp16's range and
+  // above its subnormals.  The accumulator columns span all 128 rows,
+  // whose sums the owning waves publish through LDS.
+  const float l_row = st.l_part + __shfl_xor(st.l_part, 32, 64);
+  const float lo_row = st.l_out + __shfl_xor(st.l_out, 32, 64);
+  uint8_t* slot = reinterpret_cast<uint8_t*>(a.partials) + slot_idx * R128_SLOT_BYTES;
+  float* pm = reinterpret_cast<float*>(slot + R128_O_BYTES);
+  const int r = lane & 31, h = lane >> 5;
+  if (h == 0) sums_lds[32 * wave + r] = lo_row;
+  __syncthreads();
+  float inv[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const float lo = sums_lds[32 * rb + r];
+    inv[rb] = lo > 0.f ? 1.f / lo : 0.f;
+    // the row's largest quotient over this wave's 128 columns (both lane
+    // halves), and the power of two that brings it into [2^14, 2^15)
+    float mx = 0.f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(st.o[4 * d + rb][i]));
+    mx *= inv[rb];
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    int e = 0;
+    if (mx > 0.f && mx <= 3.0e38f) {
+      frexpf(mx, &e);  // mx < 2^e
+      e = e < -100 ? -100 : e;
+    } else {
+      e = 15;  // zero, or not finite: factor 1
+    }
+    inv[rb] *= __builtin_ldexpf(1.f, 15 - e);
+    if (h == 0) pm[3 * R128_ROWS + wave * R128_ROWS + 32 * rb + r] = __builtin_ldexpf(1.f, e - 15);
+  }
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      _Float16* pl = reinterpret_cast<_Float16*>(slot) + ((4 * wave + d) * R128_ROWS + 32 * rb + r) * 32 + h * 16;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        f16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (_Float16)(st.o[4 * d + rb][8 * c + e] * inv[rb]);
+        *reinterpret_cast<f16x8*>(pl + 8 * c) = v;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  if (h == 0) {
+    const int prow = wave * 32 + r;
+    pm[prow] = st.m_ref;
+    pm[R128_ROWS + prow] = l_row;
+    pm[2 * R128_ROWS + prow] = lo_row;
+  }
+}
+
 template <bool F8>
 __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a) {
   // FP8 cache: stages of 18 KiB (32 rows of 576 E4M3 bytes)
@@ -1305,45 +1374,269 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
       }
       WAIT_VMCNT(0);
     }
-    // partial slot: O^T / (the row's bf16 sum of P) in fp16, in the
-    // accumulator layout [dv/32][row][h][i] (the 16 values a lane holds per
-    // 32x32 block are contiguous: 2 x 16-byte stores), then per row m, the
-    // fp32 and the bf16 sums of P.  The accumulator columns span all 128
-    // rows, whose sums the owning waves publish through LDS.
-    const float l_row = st.l_part + __shfl_xor(st.l_part, 32, 64);
-    const float lo_row = st.l_out + __shfl_xor(st.l_out, 32, 64);
-    uint8_t* slot = reinterpret_cast<uint8_t*>(a.partials) + piece_slot(a, bund, bb, rt) * R128_SLOT_BYTES;
-    float* pm = reinterpret_cast<float*>(slot + R128_O_BYTES);
-    const int r = lane & 31, h = lane >> 5;
     __syncthreads();  // every wave is past its last read of alpha_lds
-    if (h == 0) alpha_lds[32 * wave + r] = lo_row;
-    __syncthreads();
-    float inv[4];
+    r128_store_slot(a, st, piece_slot(a, bund, bb, rt), alpha_lds, wave, lane);
+  });
+}
+
+// ---------------------------------------------------------------- R128, pipelined (bf16 cache)
+// The 128-row kernel's bf16 instance with one barrier per key tile instead
+// of two.  Iteration it computes the scores of tile it+1 (QK^T, the LDS-heavy
+// phase: each wave reads the whole K tile), then the value product of tile
+// it (P.V) with the online softmax of tile it+1 interleaved: its VALU work
+// runs while the value MFMAs execute, instead of between two barriers with
+// the matrix units idle.  P and the rows' rescale factors are double
+// buffered in LDS (the softmax of tile it+1 writes while slower waves still
+// read tile it's).  The ring keeps three stages: during iteration it tiles
+// it (values) and it+1 (keys) are read and tile it+2 is loaded into the
+// stage tile it-1 left, which the barrier at the top of the iteration frees.
+// To fit the second P buffer, more of Q^T lives in registers (32 of its 36
+// k-steps; the 4 rope k-steps in LDS) and the block-table window is 512
+// entries.  The softmax is branch-free: the mask is a compare per score, the
+// row maxima cross the lane halves with v_permlane32_swap, and the
+// reference moves by a select.
+constexpr int R128P_QREG = 32;
+constexpr int R128P_QLDS = 36 - R128P_QREG;
+constexpr int R128P_BT_WIN = 512;
+
+// x[l] and x[l ^ 32] for every lane l, lower half first (v_permlane32_swap:
+// no LDS round trip); both halves then combine them in the same order.
+__device__ __forceinline__ f32x2 xor32_pair(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return f32x2{__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1])};
+}
+
+// S^T of this wave's 32 rows against one 32-key tile: 36 chained MFMAs, K
+// fragments (and the rope k-steps of Q^T) read three steps ahead; issue(m)
+// places ring load m of a later tile after every fourth MFMA.
+template <class Issue>
+__device__ __forceinline__ f32x16 r128p_scores(const bf16x8 (&qf)[R128P_QREG], const uint8_t* q_tail,
+                                               const uint8_t* stage, int lane, const R128LaneOff& lo,
+                                               Issue&& issue) {
+  f32x16 sc = {};
+  const uint8_t* kp[4];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const float lo = alpha_lds[32 * rb + r];
-      inv[rb] = lo > 0.f ? 1.f / lo : 0.f;
+  for (int b = 0; b < 4; ++b) kp[b] = stage + lo.k[b];
+  bf16x8 kf[4], qt[4];
+  auto q_at = [&](int kk) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(q_tail + ((kk - R128P_QREG) * 64 + lane) * 16);
+  };
+#pragma unroll
+  for (int kk = 0; kk < 3; ++kk) {
+    kf[kk] = *reinterpret_cast<const bf16x8*>(kp[kk & 3] + 128 * (kk >> 2));
+    if (kk >= R128P_QREG) qt[kk % 4] = q_at(kk);
+  }
+#pragma unroll
+  for (int kk = 0; kk < 36; ++kk) {
+    if (kk + 3 < 36) {
+      kf[(kk + 3) % 4] = *reinterpret_cast<const bf16x8*>(kp[(kk + 3) & 3] + 128 * ((kk + 3) >> 2));
+      if (kk + 3 >= R128P_QREG) qt[(kk + 3) % 4] = q_at(kk + 3);
     }
+    if ((kk & 3) == 0) issue(kk >> 2);
+    const bf16x8 qv = kk < R128P_QREG ? qf[kk < R128P_QREG ? kk : 0] : qt[kk % 4];
+    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % 4], qv, sc, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return sc;
+}
+
+// Online softmax of one S^T tile of this wave's rows (keys ts.. of the tile
+// at and past lim = min(piece end, row bound) masked), branch-free: writes
+// the wave's 32 rows of the bf16 P tile and their rescale factors.
+__device__ __forceinline__ void r128p_softmax(R128State& st, const f32x16& sc, uint8_t* p_buf, float* alpha_buf,
+                                              float scale_log2, int ts, int lim, int lane, int wave) {
+  const int r = lane & 31, h = lane >> 5;
+  float s[16];
+  float mx = NEG_INF;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = ts + 8 * (i >> 2) + 4 * h + (i & 3);
+    s[i] = t < lim ? sc[i] * scale_log2 : NEG_INF;
+    mx = fmaxf(mx, s[i]);
+  }
+  const f32x2 mp = xor32_pair(mx);
+  mx = fmaxf(mp[0], mp[1]);
+  // move the reference only when the row's max grew by more than 2^8 over
+  // it (the first visible keys of a row set it with factor 1: O and the
+  // sums are still zero)
+  const bool move = mx > st.m_ref + R128_RESCALE_LOG2;
+  const float alpha = (move && st.m_ref != NEG_INF) ? fast_exp2(st.m_ref - mx) : 1.f;
+  st.m_ref = move ? mx : st.m_ref;
+  st.l_part *= alpha;
+  st.l_out *= alpha;
+  // masked scores are -inf and exp2(-inf) = 0; a row with no visible key
+  // yet has only -inf scores and a -inf reference, so it subtracts 0
+  const float m_sub = st.m_ref == NEG_INF ? 0.f : st.m_ref;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    s[i] = fast_exp2(s[i] - m_sub);
+    st.l_part += s[i];
+  }
+  uint8_t* prow = p_buf + (32 * wave + r) * R128_PROW + 8 * h;
+  bf16x4 p4[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    p4[q] = to_bf16x4(s[4 * q + 0], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
+    *reinterpret_cast<bf16x4*>(prow + 16 * q) = p4[q];
+  }
+  st.l_out = sum_bf16x8(__builtin_shufflevector(p4[0], p4[1], 0, 1, 2, 3, 4, 5, 6, 7), st.l_out);
+  st.l_out = sum_bf16x8(__builtin_shufflevector(p4[2], p4[3], 0, 1, 2, 3, 4, 5, 6, 7), st.l_out);
+  // both lane halves hold the row's factor and store it (a guarded store
+  // would end the basic block and with it the interleave with the MFMAs)
+  alpha_buf[32 * wave + r] = alpha;
+}
+
+// O^T[this wave's 128 columns][all 128 rows] += V^T P^T over one 32-key
+// tile (two k-steps of 16 keys), after rescaling the rows whose reference
+// moved; between() runs after the first k-step's operands are requested
+// (the next tile's softmax, overlapping the value MFMAs).
+template <class Between>
+__device__ __forceinline__ void r128p_values(R128State& st, const uint8_t* stage, const uint8_t* p_buf,
+                                             const float* alpha_buf, int lane, const R128LaneOff& lo,
+                                             Between&& between) {
+  const int r = lane & 31, h = lane >> 5;
+  float ab[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) ab[rb] = alpha_buf[32 * rb + r];
+  if (__ballot(ab[0] != 1.f || ab[1] != 1.f || ab[2] != 1.f || ab[3] != 1.f) != 0) {
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        _Float16* pl = reinterpret_cast<_Float16*>(slot) + ((4 * wave + d) * R128_ROWS + 32 * rb + r) * 32 + h * 16;
+      for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          f16x8 v;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (_Float16)(st.o[4 * d + rb][8 * c + e] * inv[rb]);
-          *reinterpret_cast<f16x8*>(pl + 8 * c) = v;
+        for (int i = 0; i < 16; ++i) {
+          float tmp;
+          asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                       : "+a"(st.o[4 * d + rb][i]), "=&v"(tmp) : "v"(ab[rb]));
         }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    if (h == 0) {
-      const int prow = wave * 32 + r;
-      pm[prow] = st.m_ref;
-      pm[R128_ROWS + prow] = l_row;
-      pm[2 * R128_ROWS + prow] = lo_row;
+  }
+  const uint8_t* vp[2][2];
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+    for (int dp = 0; dp < 2; ++dp) vp[rd][dp] = stage + lo.v[rd][dp];
+  const uint8_t* pb = p_buf + r * R128_PROW + 16 * h;
+  bf16x8 bp[2][4];
+  i16x4 v[2][4][2];
+  auto operands = [&](int ks) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) bp[ks][rb] = *reinterpret_cast<const bf16x8*>(pb + 32 * rb * R128_PROW + 32 * ks);
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int rd = 0; rd < 2; ++rd)
+        v[ks][d][rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vp[rd][d & 1] + 16 * ks * R128_ROWB + 128 * (d >> 1)));
+  };
+  operands(0);
+  between();
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      if (ks == 1 && d == 0) operands(1);
+      const bf16x8 av = __builtin_shufflevector(__builtin_bit_cast(bf16x4, v[ks][d][0]),
+                                                __builtin_bit_cast(bf16x4, v[ks][d][1]), 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        st.o[4 * d + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bp[ks][rb], st.o[4 * d + rb], 0, 0, 0);
     }
+}
+
+__global__ __launch_bounds__(R128_THREADS, 1) void attn_r128p_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[R128_NS * R128_STAGE];
+  __shared__ int bt_lds[R128P_BT_WIN];
+  __shared__ __attribute__((aligned(16))) uint8_t q_tail_lds[4][R128P_QLDS * 64 * 16];
+  __shared__ __attribute__((aligned(16))) uint8_t p_lds[2][R128_ROWS * R128_PROW];
+  __shared__ float alpha_lds[2][R128_ROWS];
+  __shared__ PlanLds<R128_THREADS> plan;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = xcd_range_index(blockIdx.x, a.G);
+  const int bund = w / a.n_rt, tile = w - bund * a.n_rt;
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
+  int dma_sel_off[RING_DMA_PER_WAVE];
+  ring_dma_offsets(dma_sel_off, wave, lane);
+  const R128LaneOff lane_off = r128_lane_offsets(lane, wave);
+
+  for_each_piece<R128_THREADS>(a, bund, tile, plan, [&](int bb, int rt, int k0, int k1, int seq, int tot) {
+    int q_len, q_base;
+    request_tokens(a, bb, q_len, q_base);
+    q_len = __builtin_amdgcn_readfirstlane(q_len);
+    q_base = __builtin_amdgcn_readfirstlane(q_base);
+    if (rt * R128_ROWS >= q_len * a.H) return;
+    const int32_t* btr = a.bt + (int64_t)bb * a.max_blocks;
+    const int my_row = rt * R128_ROWS + wave * 32 + (lane & 31);
+    const bool row_ok = my_row < q_len * a.H;
+    const int nrow = row_ok ? row_bound(seq, tot, q_len, my_row / a.H, a.W, a.rank, a.I, a.causal) : 0;
+    bf16x8 qf[R128P_QREG];
+    uint8_t* q_tail = q_tail_lds[wave];
+    {
+      const uint8_t* qrow = a.q + ((int64_t)q_base * a.H + (row_ok ? my_row : 0)) * ROW_BYTES + 16 * (lane >> 5);
+#pragma unroll
+      for (int kk = 0; kk < R128P_QREG; ++kk) qf[kk] = row_ok ? gload_bf16x8(qrow + 32 * kk) : zero_bf16x8();
+#pragma unroll
+      for (int kk = 0; kk < R128P_QLDS; ++kk)
+        *reinterpret_cast<bf16x8*>(q_tail + (kk * 64 + lane) * 16) =
+            row_ok ? gload_bf16x8(qrow + 32 * (R128P_QREG + kk)) : zero_bf16x8();
+    }
+    R128State st;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) st.o[m] = f32x16{};
+    st.m_ref = NEG_INF;
+    st.l_part = 0.f;
+    st.l_out = 0.f;
+
+    const int span_keys = (R128P_BT_WIN - 1) * a.bs;
+    for (int ka = k0; ka < k1; ka += span_keys) {
+      const int kb = (k1 - ka) < span_keys ? k1 : ka + span_keys;
+      const int lim = min(kb, nrow);
+      const int e0 = block_of(a, ka), e1 = block_of(a, kb - 1);
+      __syncthreads();  // the previous sub-piece is done with the window, the ring and P
+      for (int e = e0 + tid; e <= e1; e += R128_THREADS) bt_lds[e - e0] = e < a.max_blocks ? gload_i32(btr + e) : -1;
+      __syncthreads();
+      const int nt = (kb - ka + R128_TILE - 1) / R128_TILE;
+      // prologue: tiles 0 and 1 requested, the scores and softmax of tile 0
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        ring_issue_all(r128_tile_rows(a, bt_lds, e0, ka + p * R128_TILE, kb, ring_lds + p * R128_STAGE, wave, lane),
+                       wave, dma_sel_off);
+      WAIT_VMCNT(R128_DMA_PER_WAVE);
+      __syncthreads();
+      {
+        const f32x16 sc = r128p_scores(qf, q_tail, ring, lane, lane_off, [](int) {});
+        r128p_softmax(st, sc, p_lds[0], alpha_lds[0], a.scale_log2, ka, lim, lane, wave);
+      }
+      // ring stages of tiles it, it+1 and it+2, rotated
+      uint32_t cur = 0, nxt = R128_STAGE, far = 2 * R128_STAGE;
+      int pb = 0;
+      for (int it = 0; it + 1 < nt; ++it) {
+        // tile it+1 landed (its loads are all that is outstanding), P and
+        // the factors of tile it are visible, and every wave is done with
+        // tile it-1 and P buffer pb^1
+        WAIT_VMCNT(0);
+        __syncthreads();
+        const RingRows rr = r128_tile_rows(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb, ring_lds + far, wave, lane);
+        const f32x16 sc = r128p_scores(qf, q_tail, ring + nxt, lane, lane_off, [&](int m) __attribute__((always_inline)) {
+          ring_issue_one(rr, m, wave, dma_sel_off);
+        });
+        r128p_values(st, ring + cur, p_lds[pb], alpha_lds[pb], lane, lane_off, [&]() __attribute__((always_inline)) {
+          r128p_softmax(st, sc, p_lds[pb ^ 1], alpha_lds[pb ^ 1], a.scale_log2, ka + (it + 1) * R128_TILE, lim, lane,
+                        wave);
+        });
+        const uint32_t t = cur;
+        cur = nxt;
+        nxt = far;
+        far = t;
+        pb ^= 1;
+      }
+      WAIT_VMCNT(0);
+      __syncthreads();
+      r128p_values(st, ring + cur, p_lds[pb], alpha_lds[pb], lane, lane_off, []() {});
+    }
+    __syncthreads();  // every wave is past its last read of alpha_lds
+    r128_store_slot(a, st, piece_slot(a, bund, bb, rt), alpha_lds[0], wave, lane);
   });
 }
 
@@ -1356,7 +1649,8 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
 // layouts.  M16: [dv/16][g][row][i] with dv % 16 = 4g + i; R128:
 // [dv/32][row][h][i] with dv % 32 = 8*(i/4) + 4h + i%4.  After the ROWS*512
 // values: m[ROWS] (log2 units), the fp32 sums of P[ROWS] (for the LSE) and
-// the sums of P as rounded to bf16[ROWS] (for the output).
+// the sums of P as rounded to bf16[ROWS] (for the output); R128 slots then
+// hold the fp16 values' factors [4 column quarters][ROWS].
 template <int ROWS>
 __device__ __forceinline__ int slot_index(int row, int dv) {
   if (ROWS == M16_ROWS) return (dv >> 4) * 256 + ((dv & 15) >> 2) * 64 + row * 4 + (dv & 3);
@@ -1365,7 +1659,8 @@ __device__ __forceinline__ int slot_index(int row, int dv) {
 }
 
 // M16 slots hold fp32 O (unnormalised); R128 slots hold fp16 O divided by
-// the row's bf16 sum of P, so its weight in the merge carries that sum.
+// the row's bf16 sum of P and scaled per (column quarter, row) by a power of
+// two, so its weight in the merge carries that sum and the factor.
 template <int ROWS>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   constexpr int SLICE = 64;                       // output columns per workgroup
@@ -1400,17 +1695,20 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   // the overall maximum); later batches rescale the running sums.
   constexpr int NMAX = ROWS == M16_ROWS ? 8 : 4;
   const bool some_empty = T < a.nbund;  // with T >= nbund units every range holds one
+  // R128: this thread's columns lie in one 128-column quarter of the slot
+  const int quarter = col0 / 128;
   float M = NEG_INF, L = 0.f, Lo = 0.f;
   float acc[PER];
 #pragma unroll
   for (int c = 0; c < PER; ++c) acc[c] = 0.f;
   for (int jb = j0; jb <= j1; jb += NMAX) {
-    float mw[NMAX], lw[NMAX], low[NMAX], v[NMAX][PER];
+    float mw[NMAX], lw[NMAX], low[NMAX], fac[NMAX], v[NMAX][PER];
 #pragma unroll
     for (int t = 0; t < NMAX; ++t) {
       const int j = jb + t;
       mw[t] = NEG_INF;
       lw[t] = low[t] = 0.f;
+      fac[t] = 1.f;
 #pragma unroll
       for (int c = 0; c < PER; ++c) v[t][c] = 0.f;
       if (j <= j1 && (!some_empty || range_nonempty(j, T, a.nbund))) {
@@ -1419,6 +1717,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
         mw[t] = pm[row];
         lw[t] = pm[ROWS + row];
         low[t] = pm[2 * ROWS + row];
+        if (F16) fac[t] = pm[3 * ROWS + quarter * ROWS + row];
 #pragma unroll
         for (int c = 0; c < PER; ++c)
           v[t][c] = F16 ? (float)reinterpret_cast<const _Float16*>(slot)[slot_index<ROWS>(row, col0 + c)]
@@ -1439,7 +1738,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
       const float f = (mw[t] == NEG_INF) ? 0.f : fast_exp2(mw[t] - Mb);
       L += f * lw[t];
       Lo += f * low[t];
-      const float fv = F16 ? f * low[t] : f;
+      const float fv = F16 ? f * low[t] * fac[t] : f;
 #pragma unroll
       for (int c = 0; c < PER; ++c) acc[c] += fv * v[t][c];
     }
@@ -1489,12 +1788,12 @@ int device_cu_count() {
   return cache[dev];
 }
 
-// The 128-row kernel needs a power-of-two block size (its ring loads use
-// shifts and masks); every other case runs the 16-row kernel.
-Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool allow_r128, bool fp8 = false) {
+// Requests of up to 16 rows run the 16-row kernel, larger ones the 128-row
+// kernel (any block size: a power of two takes shifts, others a division).
+Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool fp8 = false) {
   Plan p{};
   const int64_t R = (int64_t)q_len * H;
-  p.rows_tile = (R <= M16_ROWS || !allow_r128) ? M16_ROWS : R128_ROWS;
+  p.rows_tile = R <= M16_ROWS ? M16_ROWS : R128_ROWS;
   p.n_rt = (int)((R + p.rows_tile - 1) / p.rows_tile);
   // per-group overhead in key units, about what a group's start and end
   // cost in ring time: M16 5 tiles (the query item, a partial tile, the
@@ -1543,11 +1842,10 @@ extern "C" size_t mla_decode_workspace_size(int B, int q_len, int H, int max_seq
   if (B <= 0 || q_len < 1 || H < 1 || max_seq_len < 0) return 0;
   const int cus = device_cu_count();
   size_t m = 0;
-  for (const bool r128 : {true, false})
-    for (const bool fp8 : {false, true}) {
-      const size_t x = make_plan(B, q_len, H, max_seq_len, cus, r128, fp8).bytes;
-      m = x > m ? x : m;
-    }
+  for (const bool fp8 : {false, true}) {
+    const size_t x = make_plan(B, q_len, H, max_seq_len, cus, fp8).bytes;
+    m = x > m ? x : m;
+  }
   return m;
 }
 
@@ -1569,8 +1867,7 @@ int decode(const void* q, const int32_t* query_start_loc, const void* kv_cache, 
   if (causal && cp_world > 1 && causal_seqlens_global == nullptr) return MLA_ERR_INVALID_ARG;
   if (B == 0) return MLA_OK;
   if (!q || !kv_cache || !block_table || !seq_lens || !out) return MLA_ERR_INVALID_ARG;
-  const bool pow2_bs = (block_size & (block_size - 1)) == 0;
-  const Plan p = make_plan(B, q_len, H, max_seq_len, device_cu_count(), pow2_bs, kv_fp8 != 0);
+  const Plan p = make_plan(B, q_len, H, max_seq_len, device_cu_count(), kv_fp8 != 0);
   if (workspace_bytes < p.bytes || workspace == nullptr) return MLA_ERR_INVALID_ARG;
 
   DecodeArgs a{};
@@ -1600,25 +1897,13 @@ int decode(const void* q, const int32_t* query_start_loc, const void* kv_cache, 
 
   // the attention kernel; with profiling events set, the runtime records
   // them at the kernel's own start and end (no separate marker packets)
-  auto attention = [&](auto kernel, int threads) {
-    if (tl_prof_start)
-      hipExtLaunchKernelGGL(kernel, dim3(p.G), dim3(threads), 0, stream, tl_prof_start, tl_prof_stop, 0, a);
-    else
-      hipLaunchKernelGGL(kernel, dim3(p.G), dim3(threads), 0, stream, a);
-  };
-  if (p.rows_tile == M16_ROWS && kv_fp8)
-    attention(attn_m16_kernel<true>, M16_THREADS);
-  else if (p.rows_tile == M16_ROWS)
-    attention(attn_m16_kernel<false>, M16_THREADS);
-  else if (kv_fp8)
-    attention(attn_r128_kernel<true>, R128_THREADS);
-  else
-    attention(attn_r128_kernel<false>, R128_THREADS);
-  if (p.rows_tile == M16_ROWS)
-    hipLaunchKernelGGL(combine_kernel<M16_ROWS>, dim3(B * p.n_rt * 8), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(combine_kernel<R128_ROWS>, dim3(B * p.n_rt * 8), dim3(256), 0, stream, a);
-  if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+  void (*attn)(DecodeArgs) = p.rows_tile == M16_ROWS ? (kv_fp8 ? attn_m16_kernel<true> : attn_m16_kernel<false>)
+                                                     : (kv_fp8 ? attn_r128_kernel<true> : attn_r128_kernel<false>);
+  const int threads = p.rows_tile == M16_ROWS ? M16_THREADS : R128_THREADS;
+  if (launch(attn, dim3(p.G), dim3(threads), stream, a, tl_prof_start, tl_prof_stop) != hipSuccess)
+    return MLA_ERR_HIP;
+  void (*comb)(DecodeArgs) = p.rows_tile == M16_ROWS ? combine_kernel<M16_ROWS> : combine_kernel<R128_ROWS>;
+  if (launch(comb, dim3(B * p.n_rt * 8), dim3(256), stream, a) != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }
 

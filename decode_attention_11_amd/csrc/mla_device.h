@@ -1,5 +1,6 @@
 // Device-side helpers shared by the gfx950 kernels of libmla_decode.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
@@ -113,6 +114,19 @@ __device__ __forceinline__ int range_owner(int64_t u, int64_t T, int G) {
 // (and can lie between the owners of two units).
 __device__ __forceinline__ bool range_nonempty(int w, int64_t T, int G) {
   return floordiv((int64_t)w * T, G) < floordiv((int64_t)(w + 1) * T, G);
+}
+
+// Launch a kernel that takes one argument struct and return the runtime's
+// status for this launch itself (hipGetLastError would also report a
+// sticky error left behind by earlier, unrelated work).  With events given,
+// the runtime records them at the kernel's own start and end.
+template <class A>
+inline hipError_t launch(void (*kernel)(A), dim3 grid, dim3 block, hipStream_t stream, A& args,
+                         hipEvent_t start = nullptr, hipEvent_t stop = nullptr) {
+  void* argv[] = {&args};
+  if (start != nullptr)
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, stream, start, stop, 0);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, stream);
 }
 
 }  // namespace mla

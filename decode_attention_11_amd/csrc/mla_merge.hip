@@ -89,7 +89,6 @@ extern "C" int mla_merge_lse(const void* const* partials, const float* const* ls
   a.lse = lse;
   const int64_t blocks = (a.items + 3) / 4;
   if (blocks > 0x7FFFFFFF) return MLA_ERR_INVALID_ARG;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+  if (launch(merge_kernel, dim3((unsigned)blocks), dim3(256), stream, a) != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }

@@ -48,8 +48,8 @@ extern "C" {
 /* Status codes. */
 #define MLA_OK 0
 #define MLA_ERR_INVALID_ARG 1  /* a null pointer, a size or index out of range, a workspace too small */
-#define MLA_ERR_UNSUPPORTED 2  /* a valid request this library does not implement (interleave != 1 in attention) */
-#define MLA_ERR_HIP 3          /* the HIP runtime refused a launch */
+#define MLA_ERR_UNSUPPORTED 2  /* reserved: a valid request this library does not implement (no call returns it today) */
+#define MLA_ERR_HIP 3          /* the HIP runtime refused one of this call's launches (that launch's own status) */
 
 /* Short static description of a status code; never NULL. */
 const char* mla_status_string(int status);

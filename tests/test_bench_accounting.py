@@ -53,3 +53,18 @@ def test_flop_count_of_one_row_and_key():
     w = bench.rank_work(WL.build(spec), 0)
     assert w["flops"] == 2176 and w["kv_bytes"] == 1152
     assert np.isclose(w["q_bytes"], 1152) and w["out_bytes"] == 1024 and w["lse_bytes"] == 4
+
+
+@pytest.mark.parametrize("spec", SPECS, ids=[s.name for s in SPECS])
+def test_cpu_baseline_runs_every_item_of_a_tiny_workload(spec):
+    """The benchmark's CPU-baseline leg (the oracle in a pool of worker
+    processes) on each kind of workload, varlen and FP8 included: every
+    (request, rank) item finishes inside the budget, the reported work equals
+    the accounting above, and the record names its worker count."""
+    wl = WL.build(spec)
+    ranks = sorted(wl.pools)
+    unit = "TFLOP/s" if spec.H * spec.Q > 16 else "GB/s"
+    res = bench.cpu_baseline(wl, ranks, unit, budget_s=120.0, workers=2)
+    assert res["kind"] == "oracle" and res["cores"] == 2 and res["unit"] == unit
+    assert res["value"] > 0
+    assert res["sample"].startswith(f"{spec.B * len(ranks)} of {spec.B * len(ranks)} (request, rank) items")

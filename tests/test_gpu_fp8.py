@@ -39,6 +39,10 @@ CASES = [
     spec("fp8_peaky", 3, 16, 1, True, [100, 1500, 4000], q_mult=8.0, global_is_null=True),
     spec("fp8_h16_q4_dcp2_interleave4", 3, 16, 4, True, [5, 333, 2049], W=2, interleave=4),
     spec("fp8_many_tiny_requests", 300, 16, 1, True, [(7 * i) % 5 for i in range(300)], global_is_null=True),
+    spec("fp8_bs48_h128_q4", 2, 128, 4, True, [47, 2401], global_is_null=True, bs=48),
+    spec("fp8_bs80_h128_q4_dcp2", 2, 128, 4, True, [161, 3000], W=2, bs=80),
+    spec("fp8_bs48_h16_q1", 3, 16, 1, True, [48, 49, 3000], global_is_null=True, bs=48),
+    spec("fp8_bs80_h16_q1", 3, 16, 1, True, [79, 800, 2500], global_is_null=True, bs=80),
 ]
 
 

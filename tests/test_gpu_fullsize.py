@@ -1,8 +1,10 @@
 """GPU parity at the benchmark's full sizes, in the launch configuration
 bench.py times (max_seq_len = the rank's longest local length, the same
-workspace sizing), on sampled rows the oracle computes one by one; every row
-is also checked for the properties that hold at any size (finite outputs,
-the empty-row contract), and slot mappings are compared bit-exactly in full.
+workspace sizing), over every output element: the float64 oracle computes
+the whole workload in a GPU-free child process with a worker pool
+(tests/oracle_full.py) while the GPU runs, and every (row, head, column) of
+every rank is compared, together with the DCP-8 merge against the unsharded
+attention.  Slot mappings are compared bit-exactly in full.
 """
 import numpy as np
 import pytest
@@ -11,23 +13,12 @@ import torch
 import decode_attention_11_amd as mla
 import oracle
 import workloads as WL
+from tests import oracle_full
 from tests.gpu_util import Uploaded, compare, say, i32_dev, i64_dev
 
 pytestmark = pytest.mark.gpu
 
-
-def sample_rows(wl, n, seed):
-    """(b, j, h) triples: the longest and shortest requests at their first and
-    last query rows and heads, then seeded random ones."""
-    s = wl.spec
-    rng = np.random.default_rng(seed)
-    rows = set()
-    for b in (int(np.argmax(wl.tot)), int(np.argmin(wl.tot))):
-        rows.add((b, s.Q - 1, s.H - 1))
-        rows.add((b, 0, 0))
-    while len(rows) < n:
-        rows.add((int(rng.integers(s.B)), int(rng.integers(s.Q)), int(rng.integers(s.H))))
-    return sorted(rows)
+ORACLE_TIMEOUT_S = 900
 
 
 def run_rank(up, wl, r):
@@ -45,55 +36,74 @@ def every_row_properties(out, lse, label):
         assert bool((o[empty] == 0).all()), f"{label}: empty rows must be zero"
 
 
-def oracle_rows(wl, r, rows):
-    s = wl.spec
-    tot = None if (s.global_is_null and s.W == 1) else wl.tot
-    return oracle.mla_decode(wl.q_bits, wl.global_rows, wl.seq_lens[r], tot, s.W, r, s.causal, s.scale,
-                             s.lse_base, rows=rows)
+def wait_oracle(proc, label):
+    rc = proc.wait(timeout=ORACLE_TIMEOUT_S)
+    assert rc == 0, f"{label}: the oracle process failed ({rc})"
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 5])
-def test_full_size_rank_matches_oracle_on_sampled_rows(cfg):
+def test_full_size_rank_matches_oracle_on_every_element(cfg, tmp_path):
     spec = WL.config(cfg)
-    say(f"{spec.name}: generating")
-    wl = WL.build(spec)
-    up = Uploaded(wl)
-    rows = sample_rows(wl, 24, 7000 + cfg)
-    for r in sorted(wl.pools):
-        say(f"{spec.name} rank {r}: {len(rows)} sampled rows")
-        out, lse = run_rank(up, wl, r)
-        torch.cuda.synchronize()
-        every_row_properties(out, lse, f"{spec.name} r{r}")
-        ro, rl = oracle_rows(wl, r, rows)
-        compare(out, lse, ro, rl, f"{spec.name} r{r}", rows=[(b * spec.Q + j, h) for (b, j, h) in rows])
+    say(f"{spec.name}: oracle started in a worker pool; generating")
+    proc = oracle_full.start(cfg, tmp_path)
+    try:
+        wl = WL.build(spec)
+        up = Uploaded(wl)
+        got = {}
+        for r in sorted(wl.pools):
+            say(f"{spec.name} rank {r}: GPU")
+            out, lse = run_rank(up, wl, r)
+            torch.cuda.synchronize()
+            every_row_properties(out, lse, f"{spec.name} r{r}")
+            got[r] = (out.cpu(), lse.cpu())
+        del up
+        say(f"{spec.name}: waiting for the oracle")
+        wait_oracle(proc, spec.name)
+    finally:
+        if proc.poll() is None:
+            proc.kill()
+            proc.wait()
+    for r, (out, lse) in got.items():
+        ro, rl = oracle_full.load(tmp_path, r)
+        assert not np.isnan(ro).any() and not np.isnan(rl).any(), "the oracle left rows uncomputed"
+        compare(out, lse, ro, rl, f"{spec.name} r{r}, all {ro.size} outputs")
 
 
-def test_full_size_dcp8_shards_merge_to_the_unsharded_attention():
+def test_full_size_dcp8_every_rank_and_the_merge_match_on_every_element(tmp_path):
     spec = WL.config(4)
-    say(f"{spec.name}: generating")
-    wl = WL.build(spec)
-    up = Uploaded(wl)
-    rows = sample_rows(wl, 16, 7004)
-    flat = [(b * spec.Q + j, h) for (b, j, h) in rows]
-    outs, lses = [], []
-    for r in range(spec.W):
-        say(f"{spec.name} rank {r}")
-        out, lse = run_rank(up, wl, r)
+    say(f"{spec.name}: oracle (8 shards and the unsharded attention) started; generating")
+    proc = oracle_full.start(4, tmp_path, unsharded=True)
+    try:
+        wl = WL.build(spec)
+        up = Uploaded(wl)
+        outs, lses = [], []
+        for r in range(spec.W):
+            say(f"{spec.name} rank {r}: GPU")
+            out, lse = run_rank(up, wl, r)
+            torch.cuda.synchronize()
+            every_row_properties(out, lse, f"{spec.name} r{r}")
+            outs.append(out)
+            lses.append(lse)
+        mo, ml = mla.mla_merge_lse(outs, lses, spec.lse_base)
         torch.cuda.synchronize()
-        every_row_properties(out, lse, f"{spec.name} r{r}")
-        if r in (0, spec.W - 1):
-            ro, rl = oracle_rows(wl, r, rows)
-            compare(out, lse, ro, rl, f"{spec.name} r{r}", rows=flat)
-        outs.append(out)
-        lses.append(lse)
-    mo, ml = mla.mla_merge_lse(outs, lses, spec.lse_base)
-    torch.cuda.synchronize()
-    every_row_properties(mo, ml, f"{spec.name} merged")
-    # the unsharded attention over the contiguous global KV (W = 1, every row
-    # sees its global causal prefix)
-    ro, rl = oracle.mla_decode(wl.q_bits, wl.global_rows, wl.tot.astype(np.int32), wl.tot, 1, 0, True, spec.scale,
-                               spec.lse_base, rows=rows)
-    compare(mo, ml, ro, rl, f"{spec.name} merged vs unsharded", rows=flat)
+        every_row_properties(mo, ml, f"{spec.name} merged")
+        got = [(o.cpu(), l.cpu()) for o, l in zip(outs, lses)]
+        merged = (mo.cpu(), ml.cpu())
+        del up, outs, lses
+        say(f"{spec.name}: waiting for the oracle")
+        wait_oracle(proc, spec.name)
+    finally:
+        if proc.poll() is None:
+            proc.kill()
+            proc.wait()
+    for r, (out, lse) in enumerate(got):
+        ro, rl = oracle_full.load(tmp_path, r)
+        assert not np.isnan(ro).any(), "the oracle left rows uncomputed"
+        compare(out, lse, ro, rl, f"{spec.name} r{r}, all {ro.size} outputs")
+    # the merged shards against the attention over each row's whole global
+    # causal prefix (W = 1 over the contiguous global KV)
+    ro, rl = oracle_full.load(tmp_path, "u")
+    compare(merged[0], merged[1], ro, rl, f"{spec.name} merged vs unsharded, all {ro.size} outputs")
 
 
 def test_full_size_draft_block_slots_bit_exact():

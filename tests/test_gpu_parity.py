@@ -70,6 +70,12 @@ CASES = [
     spec("h128_q4_dcp4_interleave16", 2, 128, 4, True, [70, 1500], W=4, interleave=16, bs=64),
     spec("h16_q16_noncausal_dcp3_interleave2", 2, 16, 16, False, [100, 900], W=3, interleave=2),
     spec("h24_q3_dcp8_interleave8_bs128", 2, 24, 3, True, [200, 1111], W=8, interleave=8, bs=128),
+    # block sizes that are not powers of two: both kernel families divide
+    # instead of shifting
+    spec("bs48_h128_q4", 3, 128, 4, True, [47, 1000, 2401], global_is_null=True, bs=48),
+    spec("bs80_h128_q4_dcp2", 2, 128, 4, True, [161, 3000], W=2, bs=80),
+    spec("bs48_h16_q1", 4, 16, 1, True, [1, 48, 49, 3000], global_is_null=True, bs=48),
+    spec("bs80_h16_q1_dcp3", 3, 16, 1, True, [79, 800, 2500], W=3, bs=80),
 ]
 
 
