@@ -24,7 +24,7 @@ __all__ = [
     "D_QK", "D_V", "PAD_SLOT_ID", "LSE_BASE_E", "LSE_BASE_2", "MLAError",
     "library_path", "load_library", "exported_symbols",
     "mla_decode", "mla_decode_varlen", "mla_decode_workspace_size", "mla_merge_lse", "cp_local_slot", "kv_write",
-    "profile_attention_events",
+    "profile_attention_events", "mla_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 D_QK = 576
@@ -32,6 +32,7 @@ D_V = 512
 PAD_SLOT_ID = -1
 LSE_BASE_E = 0
 LSE_BASE_2 = 1
+NOALLOC_SCRATCH_BYTES = 96 * 1024 * 1024  # MLA_NOALLOC_SCRATCH_BYTES
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libmla_decode.so"
@@ -56,6 +57,8 @@ _SIGNATURES = [
     ("mla_kv_write_fp8", _I, [_P, _P, ctypes.c_int64, ctypes.c_float, _P, _I, _I, _P]),
     ("mla_decode_fp8", _I, [_P, _P, ctypes.c_float, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                             ctypes.c_float, _I, _P, _P, _P, ctypes.c_size_t, _P]),
+    ("mla_decode_noalloc", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                                ctypes.c_float, _I, _P, _P, _P]),
 ]
 
 # dtypes accepted for an FP8 (E4M3) cache: torch's OCP E4M3 type or raw codes
@@ -216,6 +219,59 @@ def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
     else:
         _check(lib.mla_decode_interleaved(*head, int(cp_interleave), *tail))
     return out, (lse if return_lse else None)
+
+
+def mla_decode_noalloc(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                       causal_seqlens_global: Optional[torch.Tensor] = None, cp_world: int = 1, cp_rank: int = 0,
+                       causal: bool = True, scale: Optional[float] = None, lse_base: str = "e", *,
+                       out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                       max_seq_len: Optional[int] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """mla_decode that allocates nothing, for callers that cannot allocate: the split-KV
+    partials live in the library's fixed per-GPU device array, and the caller passes out
+    [B*q_len, H, 512] bf16 (and lse [B*q_len, H] float32, or None).  Calls on one GPU share
+    that array and must not overlap.  q: [B, q_len, H, 576] bf16; other arguments as for
+    mla_decode (bf16 cache, interleave 1)."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16, 4)
+    B, Q, H, Dq = q.shape
+    if Dq != D_QK:
+        raise ValueError(f"q last dim must be {D_QK}")
+    _need(kv_cache, "kv_cache", torch.bfloat16, 3)
+    if kv_cache.shape[2] != D_QK:
+        raise ValueError(f"kv_cache last dim must be {D_QK}")
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    if block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_table and seq_lens must have B rows")
+    if causal_seqlens_global is not None:
+        _need(causal_seqlens_global, "causal_seqlens_global", torch.int32, 1)
+        if causal_seqlens_global.shape[0] != B:
+            raise ValueError("causal_seqlens_global must have B entries")
+    _need(out, "out", torch.bfloat16, 3)
+    if tuple(out.shape) != (B * Q, H, D_V):
+        raise ValueError("out must be [B*q_len, H, 512]")
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2)
+        if tuple(lse.shape) != (B * Q, H):
+            raise ValueError("lse must be [B*q_len, H]")
+    dev = q.device
+    _same_device(dev, kv_cache=kv_cache, block_table=block_table, seq_lens=seq_lens,
+                 causal_seqlens_global=causal_seqlens_global, out=out, lse=lse)
+    num_blocks, bs = int(kv_cache.shape[0]), int(kv_cache.shape[1])
+    max_blocks = int(block_table.shape[1])
+    if max_seq_len is None:
+        max_seq_len = max_blocks * bs
+    if scale is None:
+        scale = 1.0 / math.sqrt(192.0)
+    base = {"e": LSE_BASE_E, "2": LSE_BASE_2}.get(str(lse_base))
+    if base is None:
+        raise ValueError("lse_base must be 'e' or '2'")
+    _check(lib.mla_decode_noalloc(
+        q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(),
+        causal_seqlens_global.data_ptr() if causal_seqlens_global is not None else None,
+        B, Q, H, num_blocks, bs, max_blocks, int(max_seq_len), int(cp_world), int(cp_rank), 1 if causal else 0,
+        float(scale), base, out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream(dev)))
+    return out, lse
 
 
 def mla_merge_lse(partials: Sequence[torch.Tensor], lses: Sequence[torch.Tensor], lse_base: str = "e",

@@ -1952,3 +1952,54 @@ extern "C" int mla_decode_fp8(const void* q, const void* kv_cache, float kv_scal
                 block_size, max_blocks, max_seq_len, cp_world, cp_rank, cp_interleave, causal, scale, lse_base, 1,
                 kv_scale, out, lse, workspace, workspace_bytes, stream);
 }
+
+// ---------------------------------------------------------------- no-allocation variant
+// mla_decode_noalloc takes its workspace from this array instead of the
+// caller.  In host code `scratch` is only a stand-in for the device symbol:
+// its device address (one per GPU) comes from hipGetSymbolAddress, looked up
+// on the first call on each device with that device current, and only that
+// address is passed to kernels.  Nothing in the workspace needs clearing
+// between calls: the request offsets are written by the attention kernel
+// before the combine reads them, and every partial slot the combine reads
+// was written by the same call.
+static __device__ __align__(256) uint8_t scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, or null.
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_addr[dev] = ptr;
+  }
+  return g_scratch_addr[dev];
+}
+
+}  // namespace
+
+extern "C" int mla_decode_noalloc(const void* q, const void* kv_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, const int32_t* causal_seqlens_global, int B, int q_len,
+                                  int H, int num_blocks, int block_size, int max_blocks, int max_seq_len,
+                                  int cp_world, int cp_rank, int causal, float scale, int lse_base, void* out,
+                                  float* lse, hipStream_t stream) {
+  if (B < 0 || q_len < 1 || H < 1 || max_seq_len < 0 || (int64_t)q_len * H > (1 << 24)) return MLA_ERR_INVALID_ARG;
+  void* ws = nullptr;
+  if (B > 0) {
+    // sizes beyond the array are refused before anything touches the GPU
+    if (make_plan(B, q_len, H, max_seq_len, device_cu_count()).bytes > MLA_NOALLOC_SCRATCH_BYTES)
+      return MLA_ERR_INVALID_ARG;
+    ws = device_scratch();
+    if (ws == nullptr) return MLA_ERR_HIP;
+  }
+  return decode(q, nullptr, kv_cache, block_table, seq_lens, causal_seqlens_global, B, q_len, H, num_blocks,
+                block_size, max_blocks, max_seq_len, cp_world, cp_rank, 1, causal, scale, lse_base, 0, 1.f, out, lse,
+                ws, ws ? MLA_NOALLOC_SCRATCH_BYTES : 0, stream);
+}

@@ -206,6 +206,36 @@ int mla_decode_fp8(const void* q, const void* kv_cache, float kv_scale, const in
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Size of the device array mla_decode_noalloc uses as its workspace: 96 MiB
+ * on each GPU the library runs on, held until the process ends.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)96 * 1024 * 1024)
+
+/*
+ * mla_decode for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, serving loops that forbid
+ * allocation, harnesses without an allocator.  Same arguments, layouts,
+ * results and errors as mla_decode, without workspace and workspace_bytes:
+ * the split-KV partials live in a fixed device array of
+ * MLA_NOALLOC_SCRATCH_BYTES per GPU instead.  The call allocates nothing and
+ * calls no allocating routine; its first call on a device looks up that
+ * device's array once.  The caller still owns and passes every input and
+ * output.
+ * Every call on one GPU shares that GPU's array, which keeps the last
+ * call's contents (nothing in it needs to start at zero): calls that overlap
+ * on one GPU, on any streams, race and must be serialised by the caller.
+ * Errors: those of mla_decode, and MLA_ERR_INVALID_ARG when the sizes need
+ * more than MLA_NOALLOC_SCRATCH_BYTES (mla_decode_workspace_size(B, q_len,
+ * H, max_seq_len) bytes; e.g. B = 16, q_len = 16, H = 128 and a 131072-key
+ * bound need 69 MB); MLA_ERR_HIP if the array's address cannot be obtained.
+ */
+int mla_decode_noalloc(const void* q, const void* kv_cache, const int32_t* block_table,
+                       const int32_t* seq_lens, const int32_t* causal_seqlens_global,
+                       int B, int q_len, int H, int num_blocks, int block_size, int max_blocks,
+                       int max_seq_len, int cp_world, int cp_rank, int causal, float scale,
+                       int lse_base, void* out, float* lse, hipStream_t stream);
+
+/*
  * Profiling aid (not part of the computation): for the calling host thread,
  * record `start` at the start and `stop` at the end of the split-KV
  * attention kernel of each following mla_decode call (the kernel is then

@@ -23,7 +23,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["mla_status_string", "mla_decode_workspace_size", "mla_decode",
                                            "mla_merge_lse", "cp_local_slot", "mla_profile_attention_events",
                                            "mla_kv_write", "mla_decode_interleaved", "mla_decode_varlen",
-                                           "mla_decode_fp8", "mla_kv_write_fp8"])
+                                           "mla_decode_fp8", "mla_kv_write_fp8", "mla_decode_noalloc"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -202,3 +202,28 @@ def test_kv_write_fp8_rejects_bad_arguments(kv_scale, kw):
 
 def test_kv_write_fp8_empty_is_a_noop():
     assert _kv_write_fp8(0.5, n=0, rows=None, slots=None, cache=None) == 0
+
+
+def _noalloc(**kw):
+    lib = mla.load_library()
+    a = dict(q=1, kv=1, bt=1, sl=1, gl=None, B=2, Q=1, H=16, nblk=4, bs=64, maxb=2, maxlen=128, W=1, r=0,
+             causal=1, scale=0.1, base=0, out=1, lse=1, stream=None)
+    a.update(kw)
+    return lib.mla_decode_noalloc(a["q"], a["kv"], a["bt"], a["sl"], a["gl"], a["B"], a["Q"], a["H"], a["nblk"],
+                                  a["bs"], a["maxb"], a["maxlen"], a["W"], a["r"], a["causal"],
+                                  ctypes.c_float(a["scale"]), a["base"], a["out"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("bad", [dict(Q=0), dict(H=0), dict(B=-1), dict(maxlen=-1),
+                                 # more partial slots than the fixed array holds
+                                 dict(B=4096, Q=16, H=128, maxlen=1 << 20), dict(B=64, Q=16, H=128, maxlen=1 << 18)])
+def test_noalloc_rejects_bad_arguments_and_sizes_beyond_its_array(bad):
+    assert _noalloc(**bad) == 1
+
+
+def test_noalloc_array_size_is_the_documented_one():
+    src = open(HEADER).read()
+    assert "#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)96 * 1024 * 1024)" in src
+    assert mla.NOALLOC_SCRATCH_BYTES == 96 * 1024 * 1024
+    # the largest benchmark workload (B 16, q_len 16, H 128, 131072-key bound) fits
+    assert mla.mla_decode_workspace_size(16, 16, 128, 131072) <= mla.NOALLOC_SCRATCH_BYTES
