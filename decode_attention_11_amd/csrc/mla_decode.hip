@@ -1379,267 +1379,6 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
   });
 }
 
-// ---------------------------------------------------------------- R128, pipelined (bf16 cache)
-// The 128-row kernel's bf16 instance with one barrier per key tile instead
-// of two.  Iteration it computes the scores of tile it+1 (QK^T, the LDS-heavy
-// phase: each wave reads the whole K tile), then the value product of tile
-// it (P.V) with the online softmax of tile it+1 interleaved: its VALU work
-// runs while the value MFMAs execute, instead of between two barriers with
-// the matrix units idle.  P and the rows' rescale factors are double
-// buffered in LDS (the softmax of tile it+1 writes while slower waves still
-// read tile it's).  The ring keeps three stages: during iteration it tiles
-// it (values) and it+1 (keys) are read and tile it+2 is loaded into the
-// stage tile it-1 left, which the barrier at the top of the iteration frees.
-// To fit the second P buffer, more of Q^T lives in registers (32 of its 36
-// k-steps; the 4 rope k-steps in LDS) and the block-table window is 512
-// entries.  The softmax is branch-free: the mask is a compare per score, the
-// row maxima cross the lane halves with v_permlane32_swap, and the
-// reference moves by a select.
-constexpr int R128P_QREG = 32;
-constexpr int R128P_QLDS = 36 - R128P_QREG;
-constexpr int R128P_BT_WIN = 512;
-
-// x[l] and x[l ^ 32] for every lane l, lower half first (v_permlane32_swap:
-// no LDS round trip); both halves then combine them in the same order.
-__device__ __forceinline__ f32x2 xor32_pair(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
-                                                  false, false);
-  return f32x2{__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1])};
-}
-
-// S^T of this wave's 32 rows against one 32-key tile: 36 chained MFMAs, K
-// fragments (and the rope k-steps of Q^T) read three steps ahead; issue(m)
-// places ring load m of a later tile after every fourth MFMA.
-template <class Issue>
-__device__ __forceinline__ f32x16 r128p_scores(const bf16x8 (&qf)[R128P_QREG], const uint8_t* q_tail,
-                                               const uint8_t* stage, int lane, const R128LaneOff& lo,
-                                               Issue&& issue) {
-  f32x16 sc = {};
-  const uint8_t* kp[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) kp[b] = stage + lo.k[b];
-  bf16x8 kf[4], qt[4];
-  auto q_at = [&](int kk) __attribute__((always_inline)) {
-    return *reinterpret_cast<const bf16x8*>(q_tail + ((kk - R128P_QREG) * 64 + lane) * 16);
-  };
-#pragma unroll
-  for (int kk = 0; kk < 3; ++kk) {
-    kf[kk] = *reinterpret_cast<const bf16x8*>(kp[kk & 3] + 128 * (kk >> 2));
-    if (kk >= R128P_QREG) qt[kk % 4] = q_at(kk);
-  }
-#pragma unroll
-  for (int kk = 0; kk < 36; ++kk) {
-    if (kk + 3 < 36) {
-      kf[(kk + 3) % 4] = *reinterpret_cast<const bf16x8*>(kp[(kk + 3) & 3] + 128 * ((kk + 3) >> 2));
-      if (kk + 3 >= R128P_QREG) qt[(kk + 3) % 4] = q_at(kk + 3);
-    }
-    if ((kk & 3) == 0) issue(kk >> 2);
-    const bf16x8 qv = kk < R128P_QREG ? qf[kk < R128P_QREG ? kk : 0] : qt[kk % 4];
-    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % 4], qv, sc, 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  return sc;
-}
-
-// Online softmax of one S^T tile of this wave's rows (keys ts.. of the tile
-// at and past lim = min(piece end, row bound) masked), branch-free: writes
-// the wave's 32 rows of the bf16 P tile and their rescale factors.
-__device__ __forceinline__ void r128p_softmax(R128State& st, const f32x16& sc, uint8_t* p_buf, float* alpha_buf,
-                                              float scale_log2, int ts, int lim, int lane, int wave) {
-  const int r = lane & 31, h = lane >> 5;
-  float s[16];
-  float mx = NEG_INF;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int t = ts + 8 * (i >> 2) + 4 * h + (i & 3);
-    s[i] = t < lim ? sc[i] * scale_log2 : NEG_INF;
-    mx = fmaxf(mx, s[i]);
-  }
-  const f32x2 mp = xor32_pair(mx);
-  mx = fmaxf(mp[0], mp[1]);
-  // move the reference only when the row's max grew by more than 2^8 over
-  // it (the first visible keys of a row set it with factor 1: O and the
-  // sums are still zero)
-  const bool move = mx > st.m_ref + R128_RESCALE_LOG2;
-  const float alpha = (move && st.m_ref != NEG_INF) ? fast_exp2(st.m_ref - mx) : 1.f;
-  st.m_ref = move ? mx : st.m_ref;
-  st.l_part *= alpha;
-  st.l_out *= alpha;
-  // masked scores are -inf and exp2(-inf) = 0; a row with no visible key
-  // yet has only -inf scores and a -inf reference, so it subtracts 0
-  const float m_sub = st.m_ref == NEG_INF ? 0.f : st.m_ref;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    s[i] = fast_exp2(s[i] - m_sub);
-    st.l_part += s[i];
-  }
-  uint8_t* prow = p_buf + (32 * wave + r) * R128_PROW + 8 * h;
-  bf16x4 p4[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    p4[q] = to_bf16x4(s[4 * q + 0], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
-    *reinterpret_cast<bf16x4*>(prow + 16 * q) = p4[q];
-  }
-  st.l_out = sum_bf16x8(__builtin_shufflevector(p4[0], p4[1], 0, 1, 2, 3, 4, 5, 6, 7), st.l_out);
-  st.l_out = sum_bf16x8(__builtin_shufflevector(p4[2], p4[3], 0, 1, 2, 3, 4, 5, 6, 7), st.l_out);
-  // both lane halves hold the row's factor and store it (a guarded store
-  // would end the basic block and with it the interleave with the MFMAs)
-  alpha_buf[32 * wave + r] = alpha;
-}
-
-// O^T[this wave's 128 columns][all 128 rows] += V^T P^T over one 32-key
-// tile (two k-steps of 16 keys), after rescaling the rows whose reference
-// moved; between() runs after the first k-step's operands are requested
-// (the next tile's softmax, overlapping the value MFMAs).
-template <class Between>
-__device__ __forceinline__ void r128p_values(R128State& st, const uint8_t* stage, const uint8_t* p_buf,
-                                             const float* alpha_buf, int lane, const R128LaneOff& lo,
-                                             Between&& between) {
-  const int r = lane & 31, h = lane >> 5;
-  float ab[4];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) ab[rb] = alpha_buf[32 * rb + r];
-  if (__ballot(ab[0] != 1.f || ab[1] != 1.f || ab[2] != 1.f || ab[3] != 1.f) != 0) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float tmp;
-          asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                       : "+a"(st.o[4 * d + rb][i]), "=&v"(tmp) : "v"(ab[rb]));
-        }
-  }
-  const uint8_t* vp[2][2];
-#pragma unroll
-  for (int rd = 0; rd < 2; ++rd)
-#pragma unroll
-    for (int dp = 0; dp < 2; ++dp) vp[rd][dp] = stage + lo.v[rd][dp];
-  const uint8_t* pb = p_buf + r * R128_PROW + 16 * h;
-  bf16x8 bp[2][4];
-  i16x4 v[2][4][2];
-  auto operands = [&](int ks) __attribute__((always_inline)) {
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) bp[ks][rb] = *reinterpret_cast<const bf16x8*>(pb + 32 * rb * R128_PROW + 32 * ks);
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int rd = 0; rd < 2; ++rd)
-        v[ks][d][rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vp[rd][d & 1] + 16 * ks * R128_ROWB + 128 * (d >> 1)));
-  };
-  operands(0);
-  between();
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      if (ks == 1 && d == 0) operands(1);
-      const bf16x8 av = __builtin_shufflevector(__builtin_bit_cast(bf16x4, v[ks][d][0]),
-                                                __builtin_bit_cast(bf16x4, v[ks][d][1]), 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        st.o[4 * d + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bp[ks][rb], st.o[4 * d + rb], 0, 0, 0);
-    }
-}
-
-__global__ __launch_bounds__(R128_THREADS, 1) void attn_r128p_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[R128_NS * R128_STAGE];
-  __shared__ int bt_lds[R128P_BT_WIN];
-  __shared__ __attribute__((aligned(16))) uint8_t q_tail_lds[4][R128P_QLDS * 64 * 16];
-  __shared__ __attribute__((aligned(16))) uint8_t p_lds[2][R128_ROWS * R128_PROW];
-  __shared__ float alpha_lds[2][R128_ROWS];
-  __shared__ PlanLds<R128_THREADS> plan;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int w = xcd_range_index(blockIdx.x, a.G);
-  const int bund = w / a.n_rt, tile = w - bund * a.n_rt;
-  const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
-  int dma_sel_off[RING_DMA_PER_WAVE];
-  ring_dma_offsets(dma_sel_off, wave, lane);
-  const R128LaneOff lane_off = r128_lane_offsets(lane, wave);
-
-  for_each_piece<R128_THREADS>(a, bund, tile, plan, [&](int bb, int rt, int k0, int k1, int seq, int tot) {
-    int q_len, q_base;
-    request_tokens(a, bb, q_len, q_base);
-    q_len = __builtin_amdgcn_readfirstlane(q_len);
-    q_base = __builtin_amdgcn_readfirstlane(q_base);
-    if (rt * R128_ROWS >= q_len * a.H) return;
-    const int32_t* btr = a.bt + (int64_t)bb * a.max_blocks;
-    const int my_row = rt * R128_ROWS + wave * 32 + (lane & 31);
-    const bool row_ok = my_row < q_len * a.H;
-    const int nrow = row_ok ? row_bound(seq, tot, q_len, my_row / a.H, a.W, a.rank, a.I, a.causal) : 0;
-    bf16x8 qf[R128P_QREG];
-    uint8_t* q_tail = q_tail_lds[wave];
-    {
-      const uint8_t* qrow = a.q + ((int64_t)q_base * a.H + (row_ok ? my_row : 0)) * ROW_BYTES + 16 * (lane >> 5);
-#pragma unroll
-      for (int kk = 0; kk < R128P_QREG; ++kk) qf[kk] = row_ok ? gload_bf16x8(qrow + 32 * kk) : zero_bf16x8();
-#pragma unroll
-      for (int kk = 0; kk < R128P_QLDS; ++kk)
-        *reinterpret_cast<bf16x8*>(q_tail + (kk * 64 + lane) * 16) =
-            row_ok ? gload_bf16x8(qrow + 32 * (R128P_QREG + kk)) : zero_bf16x8();
-    }
-    R128State st;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) st.o[m] = f32x16{};
-    st.m_ref = NEG_INF;
-    st.l_part = 0.f;
-    st.l_out = 0.f;
-
-    const int span_keys = (R128P_BT_WIN - 1) * a.bs;
-    for (int ka = k0; ka < k1; ka += span_keys) {
-      const int kb = (k1 - ka) < span_keys ? k1 : ka + span_keys;
-      const int lim = min(kb, nrow);
-      const int e0 = block_of(a, ka), e1 = block_of(a, kb - 1);
-      __syncthreads();  // the previous sub-piece is done with the window, the ring and P
-      for (int e = e0 + tid; e <= e1; e += R128_THREADS) bt_lds[e - e0] = e < a.max_blocks ? gload_i32(btr + e) : -1;
-      __syncthreads();
-      const int nt = (kb - ka + R128_TILE - 1) / R128_TILE;
-      // prologue: tiles 0 and 1 requested, the scores and softmax of tile 0
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-        ring_issue_all(r128_tile_rows(a, bt_lds, e0, ka + p * R128_TILE, kb, ring_lds + p * R128_STAGE, wave, lane),
-                       wave, dma_sel_off);
-      WAIT_VMCNT(R128_DMA_PER_WAVE);
-      __syncthreads();
-      {
-        const f32x16 sc = r128p_scores(qf, q_tail, ring, lane, lane_off, [](int) {});
-        r128p_softmax(st, sc, p_lds[0], alpha_lds[0], a.scale_log2, ka, lim, lane, wave);
-      }
-      // ring stages of tiles it, it+1 and it+2, rotated
-      uint32_t cur = 0, nxt = R128_STAGE, far = 2 * R128_STAGE;
-      int pb = 0;
-      for (int it = 0; it + 1 < nt; ++it) {
-        // tile it+1 landed (its loads are all that is outstanding), P and
-        // the factors of tile it are visible, and every wave is done with
-        // tile it-1 and P buffer pb^1
-        WAIT_VMCNT(0);
-        __syncthreads();
-        const RingRows rr = r128_tile_rows(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb, ring_lds + far, wave, lane);
-        const f32x16 sc = r128p_scores(qf, q_tail, ring + nxt, lane, lane_off, [&](int m) __attribute__((always_inline)) {
-          ring_issue_one(rr, m, wave, dma_sel_off);
-        });
-        r128p_values(st, ring + cur, p_lds[pb], alpha_lds[pb], lane, lane_off, [&]() __attribute__((always_inline)) {
-          r128p_softmax(st, sc, p_lds[pb ^ 1], alpha_lds[pb ^ 1], a.scale_log2, ka + (it + 1) * R128_TILE, lim, lane,
-                        wave);
-        });
-        const uint32_t t = cur;
-        cur = nxt;
-        nxt = far;
-        far = t;
-        pb ^= 1;
-      }
-      WAIT_VMCNT(0);
-      __syncthreads();
-      r128p_values(st, ring + cur, p_lds[pb], alpha_lds[pb], lane, lane_off, []() {});
-    }
-    __syncthreads();  // every wave is past its last read of alpha_lds
-    r128_store_slot(a, st, piece_slot(a, bund, bb, rt), alpha_lds[0], wave, lane);
-  });
-}
-
 // ---------------------------------------------------------------- combine
 // Grid: (request, row tile) groups x 8 slices of 64 output columns.  Merges
 // the partial slots of the workgroups that covered the group and writes bf16
