@@ -14,8 +14,9 @@ Without --config every workload runs, one after another in one process:
   3 causal spec decode (B=32, H=128, q_len 4), 4 DCP-8 shards + merge
   (B=16, H=128, q_len 4), 5 the non-causal draft block under DCP 2
   (B=16, H=128, q_len 16, rank 1), the largest, which is the headline
-  (the line's top-level value, roofline and cpu_baseline); every workload's
-  own figures are under "configs".  --config N runs workload N alone as the
+  (the line's top-level value, roofline and cpu_baseline); and 6, spec
+  decode with 16 heads (B=64, H=16, q_len 4: the 64-row tile).  Every
+  workload's own figures are under "configs".  --config N runs workload N alone as the
   headline.  --fp8 stores the cache as E4M3 codes with one scale
   (mla_decode_fp8); --varlen draws a query length per request
   (mla_decode_varlen); --interleave deals positions to the ranks in
@@ -44,7 +45,7 @@ FLOP_PER_KEY_ROW = 2 * 576 + 2 * 512   # QK^T (576-wide) + PV (512-wide) per (ro
 KV_ROW_BYTES = 576 * 2
 FP8_KV_SCALE = 1.0 / 64           # --fp8: codes of N(0,1) values / this scale (|value| < 7 stays below 448)
 HEADLINE = 5                      # the largest workload
-MEM_BOUND = (1, 2)                # single-token 16-head workloads: HBM is the binding roof
+MEM_BOUND = (1, 2, 6)             # 16-head workloads (64 rows and fewer): HBM is the binding roof
 MAX_CPU_WORKERS = 16              # host share of one GPU on the measurement boxes
 
 
@@ -561,8 +562,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--config", type=int, default=0, choices=[0, 1, 2, 3, 4, 5],
-                    help="run only this workload (0: all five, the largest as the headline)")
+    ap.add_argument("--config", type=int, default=0, choices=[0, 1, 2, 3, 4, 5, 6],
+                    help="run only this workload (0: all six, the largest as the headline)")
     ap.add_argument("--replicas", type=int, default=0, help="KV replicas rotated per step (0: auto)")
     ap.add_argument("--varlen", action="store_true",
                     help="per-request query lengths uniform in [1, q_len] (seeded), through mla_decode_varlen")
@@ -596,7 +597,7 @@ def main():
         unit = "GB/s" if n in MEM_BOUND else "TFLOP/s"
         print(json.dumps(cpu_baseline(wl, sorted(wl.pools), unit, args.cpu_budget)), flush=True)
         return
-    order = [args.config] if args.config else [1, 2, 3, 4, 5]
+    order = [args.config] if args.config else [1, 2, 6, 3, 4, 5]
     headline = args.config or HEADLINE
 
     # the CPU baselines first, each in a child process of its own, so that

@@ -890,9 +890,16 @@ constexpr int R128_ROWB = ROW_BYTES;          // LDS bytes per key row (unpadded
 constexpr int R128_DMA_PER_WAVE = RING_DMA_PER_WAVE;
 constexpr int R128_STAGE = RING_STAGE;        // 36 KiB
 constexpr int R128_NS = 3;                    // ring stages
-constexpr int R128_O_BYTES = R128_ROWS * D_V * 2;                 // fp16 partial O of a slot
-// + m, l, lo per row and a power-of-two factor per (value-column quarter, row), fp32
-constexpr int R128_SLOT_BYTES = R128_O_BYTES + 7 * R128_ROWS * 4;
+// The same kernel also runs tiles of 32 or 64 rows (requests of 17 to 64
+// rows: fewer heads, a few query tokens), with NRB = rows / 32 row blocks:
+// only waves 0 .. NRB-1 compute scores and softmax, every wave accumulates
+// its 128 value columns for the NRB row blocks.
+// Partial slot of a tile of `rows` rows: fp16 O, then m, l, lo per row and
+// a power-of-two factor per (value-column quarter, row), fp32.
+constexpr int r128_o_bytes(int rows) { return rows * D_V * 2; }
+constexpr int r128_slot_bytes(int rows) { return r128_o_bytes(rows) + 7 * rows * 4; }
+constexpr int R128_O_BYTES = r128_o_bytes(R128_ROWS);
+constexpr int R128_SLOT_BYTES = r128_slot_bytes(R128_ROWS);
 constexpr int R128_BT_WIN = 1024;             // block-table entries held in LDS per sub-piece
 // Q^T k-steps (of 16 dims) kept in registers; the rest in LDS.  The FP8
 // instance's ring takes half the LDS, so it moves more of Q^T there and
@@ -983,11 +990,12 @@ __device__ __forceinline__ R128LaneOff r128_lane_offsets(int lane, int wave) {
   return lo;
 }
 
-// o[4d + rb]: value columns 128w + 32d .. +31, rows 32rb .. +31 of O^T.
+// o[NRB d + rb]: value columns 128w + 32d .. +31, rows 32rb .. +31 of O^T.
 // m_ref, l_part, l_out: the softmax state of this wave's own row
-// 32w + lane%32 (both lane halves hold the same values).
+// 32w + lane%32 (both lane halves hold the same values; waves w < NRB).
+template <int NRB>
 struct R128State {
-  f32x16 o[16];
+  f32x16 o[4 * NRB];
   float m_ref, l_part, l_out;
 };
 
@@ -997,13 +1005,14 @@ struct R128State {
 // value fragments are 8-byte reads (value ones transposed) widened to bf16
 // in registers, and the ring loads of a later tile (five or four per wave)
 // are issued one every eight score MFMAs.
-template <bool F8, class Issue>
-__device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[r128_qreg<F8>], const uint8_t* q_tail,
-                                             const uint8_t* stage, uint8_t* p_lds, float* alpha_lds,
-                                             float scale_log2, int ts, int k1, int nrow, int kfull, int lane,
-                                             int wave, Issue&& issue, const R128LaneOff& lo) {
+template <bool F8, int NRB, class Issue>
+__device__ __forceinline__ void r128_compute(R128State<NRB>& st, const bf16x8 (&qf)[r128_qreg<F8>],
+                                             const uint8_t* q_tail, const uint8_t* stage, uint8_t* p_lds,
+                                             float* alpha_lds, float scale_log2, int ts, int k1, int nrow, int kfull,
+                                             int lane, int wave, Issue&& issue, const R128LaneOff& lo) {
   constexpr int R128_QREG = r128_qreg<F8>;
   const int r = lane & 31, h = lane >> 5;
+  if (wave < NRB) {
   // ---- scores of this wave's rows: S^T[key][row], lane holds keys
   // 8*(i/4) + 4h + i%4 of row r
   f32x16 sc = {};
@@ -1101,6 +1110,12 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[r
   st.l_out = sum_bf16x8(__builtin_shufflevector(p4[0], p4[1], 0, 1, 2, 3, 4, 5, 6, 7), st.l_out);
   st.l_out = sum_bf16x8(__builtin_shufflevector(p4[2], p4[3], 0, 1, 2, 3, 4, 5, 6, 7), st.l_out);
   if (h == 0) alpha_lds[32 * wave + r] = alpha;
+  } else {
+    // a wave without score rows (tiles of fewer than 128 rows) only issues
+    // its ring loads of the later tile
+#pragma unroll
+    for (int m = 0; m < (F8 ? 5 : RING_DMA_PER_WAVE); ++m) issue(m);
+  }
   __syncthreads();
   // O^T[dv][row] += V^T[dv][key] P^T[key][row] over 2 k-steps of 16 keys:
   // contraction slot 8h + s is key 16ks + 8h + s on both sides.
@@ -1114,11 +1129,11 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[r
 #pragma unroll
     for (int dp = 0; dp < 2; ++dp) vp[rd][dp] = stage + lo.v[rd][dp];
   const uint8_t* pb = p_lds + r * R128_PROW + 16 * h;
-  bf16x8 bp[2][4];
+  bf16x8 bp[2][NRB];
   i16x4 v[2][4][2];
   auto pv_operands = [&](int ks) __attribute__((always_inline)) {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) bp[ks][rb] = *reinterpret_cast<const bf16x8*>(pb + 32 * rb * R128_PROW + 32 * ks);
+    for (int rb = 0; rb < NRB; ++rb) bp[ks][rb] = *reinterpret_cast<const bf16x8*>(pb + 32 * rb * R128_PROW + 32 * ks);
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -1132,21 +1147,25 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[r
   // ---- this wave's value columns for all 128 rows.  The accumulator
   // column of lane l is row 32rb + l%32 in block rb: rescale the blocks whose
   // rows moved their reference (rare)
-  float ab[4];
+  float ab[NRB];
+  bool moved = false;
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) ab[rb] = alpha_lds[32 * rb + r];
-  if (__ballot(ab[0] != 1.f || ab[1] != 1.f || ab[2] != 1.f || ab[3] != 1.f) != 0) {
+  for (int rb = 0; rb < NRB; ++rb) {
+    ab[rb] = alpha_lds[32 * rb + r];
+    moved = moved || ab[rb] != 1.f;
+  }
+  if (__ballot(moved) != 0) {
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+      for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           // in place on the accumulator register (a plain multiply makes the
           // register allocator keep two copies of all 256 accumulators)
           float tmp;
           asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                       : "+a"(st.o[4 * d + rb][i]), "=&v"(tmp) : "v"(ab[rb]));
+                       : "+a"(st.o[NRB * d + rb][i]), "=&v"(tmp) : "v"(ab[rb]));
         }
   }
   if constexpr (F8) {
@@ -1157,9 +1176,9 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[r
     const int i16 = lane & 15, qg = lane >> 4;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 bp[4];
+      bf16x8 bp[NRB];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) bp[rb] = *reinterpret_cast<const bf16x8*>(pb + 32 * rb * R128_PROW + 32 * ks);
+      for (int rb = 0; rb < NRB; ++rb) bp[rb] = *reinterpret_cast<const bf16x8*>(pb + 32 * rb * R128_PROW + 32 * ks);
       const int key = 16 * ks + 8 * h + (i16 >> 1);
       const uint8_t* vrow = stage + M16F8_ROW * key + 8 * (i16 & 1);
       const int vc = f8_rot(key) + 8 * wave + (qg & 1);
@@ -1171,8 +1190,8 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[r
       for (int d = 0; d < 4; ++d) {
         const bf16x8 av = f8x8_to_bf16((uint32_t)v[d].x, (uint32_t)v[d].y);
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-          st.o[4 * d + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bp[rb], st.o[4 * d + rb], 0, 0, 0);
+        for (int rb = 0; rb < NRB; ++rb)
+          st.o[NRB * d + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bp[rb], st.o[NRB * d + rb], 0, 0, 0);
       }
     }
     return;
@@ -1185,8 +1204,8 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[r
       const bf16x8 av = __builtin_shufflevector(__builtin_bit_cast(bf16x4, v[ks][d][0]),
                                                 __builtin_bit_cast(bf16x4, v[ks][d][1]), 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        st.o[4 * d + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bp[ks][rb], st.o[4 * d + rb], 0, 0, 0);
+      for (int rb = 0; rb < NRB; ++rb)
+        st.o[NRB * d + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bp[ks][rb], st.o[NRB * d + rb], 0, 0, 0);
     }
   }
 }
@@ -1194,8 +1213,10 @@ __device__ __forceinline__ void r128_compute(R128State& st, const bf16x8 (&qf)[r
 // The partial slot of one 128-row piece (every wave calls it with its own
 // O^T quarter and row state; sums_lds is 128 floats of LDS that no wave still
 // reads).
-__device__ __forceinline__ void r128_store_slot(const DecodeArgs& a, const R128State& st, int64_t slot_idx,
+template <int NRB>
+__device__ __forceinline__ void r128_store_slot(const DecodeArgs& a, const R128State<NRB>& st, int64_t slot_idx,
                                                 float* sums_lds, int wave, int lane) {
+  constexpr int ROWS = 32 * NRB;
   // partial slot: O^T / (the row's bf16 sum of P) in fp16, in the
   // accumulator layout [dv/32][row][h][i] (the 16 values a lane holds per
   // 32x32 block are contiguous: 2 x 16-byte stores), then per row m, the
@@ -1208,14 +1229,14 @@ __device__ __forceinline__ void r128_store_slot(const DecodeArgs& a, const R128S
   // whose sums the owning waves publish through LDS.
   const float l_row = st.l_part + __shfl_xor(st.l_part, 32, 64);
   const float lo_row = st.l_out + __shfl_xor(st.l_out, 32, 64);
-  uint8_t* slot = reinterpret_cast<uint8_t*>(a.partials) + slot_idx * R128_SLOT_BYTES;
-  float* pm = reinterpret_cast<float*>(slot + R128_O_BYTES);
+  uint8_t* slot = reinterpret_cast<uint8_t*>(a.partials) + slot_idx * r128_slot_bytes(ROWS);
+  float* pm = reinterpret_cast<float*>(slot + r128_o_bytes(ROWS));
   const int r = lane & 31, h = lane >> 5;
-  if (h == 0) sums_lds[32 * wave + r] = lo_row;
+  if (h == 0 && wave < NRB) sums_lds[32 * wave + r] = lo_row;
   __syncthreads();
-  float inv[4];
+  float inv[NRB];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
+  for (int rb = 0; rb < NRB; ++rb) {
     const float lo = sums_lds[32 * rb + r];
     inv[rb] = lo > 0.f ? 1.f / lo : 0.f;
     // the row's largest quotient over this wave's 128 columns (both lane
@@ -1224,7 +1245,7 @@ __device__ __forceinline__ void r128_store_slot(const DecodeArgs& a, const R128S
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(st.o[4 * d + rb][i]));
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(st.o[NRB * d + rb][i]));
     mx *= inv[rb];
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     int e = 0;
@@ -1235,44 +1256,47 @@ __device__ __forceinline__ void r128_store_slot(const DecodeArgs& a, const R128S
       e = 15;  // zero, or not finite: factor 1
     }
     inv[rb] *= __builtin_ldexpf(1.f, 15 - e);
-    if (h == 0) pm[3 * R128_ROWS + wave * R128_ROWS + 32 * rb + r] = __builtin_ldexpf(1.f, e - 15);
+    if (h == 0) pm[3 * ROWS + wave * ROWS + 32 * rb + r] = __builtin_ldexpf(1.f, e - 15);
   }
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      _Float16* pl = reinterpret_cast<_Float16*>(slot) + ((4 * wave + d) * R128_ROWS + 32 * rb + r) * 32 + h * 16;
+    for (int rb = 0; rb < NRB; ++rb) {
+      _Float16* pl = reinterpret_cast<_Float16*>(slot) + ((4 * wave + d) * ROWS + 32 * rb + r) * 32 + h * 16;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         f16x8 v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (_Float16)(st.o[4 * d + rb][8 * c + e] * inv[rb]);
+        for (int e = 0; e < 8; ++e) v[e] = (_Float16)(st.o[NRB * d + rb][8 * c + e] * inv[rb]);
         *reinterpret_cast<f16x8*>(pl + 8 * c) = v;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-  if (h == 0) {
+  if (h == 0 && wave < NRB) {
     const int prow = wave * 32 + r;
     pm[prow] = st.m_ref;
-    pm[R128_ROWS + prow] = l_row;
-    pm[2 * R128_ROWS + prow] = lo_row;
+    pm[ROWS + prow] = l_row;
+    pm[2 * ROWS + prow] = lo_row;
   }
 }
 
-template <bool F8>
+template <bool F8, int NRB>
 __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a) {
+  constexpr int ROWS = 32 * NRB;
   // FP8 cache: stages of 18 KiB (32 rows of 576 E4M3 bytes)
   constexpr int STAGE = F8 ? M16F8_RAW : R128_STAGE;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[R128_NS * STAGE];
   __shared__ int bt_lds[R128_BT_WIN];
   constexpr int R128_QREG = r128_qreg<F8>, R128_QLDS = r128_qlds<F8>;
-  __shared__ __attribute__((aligned(16))) uint8_t q_tail_lds[4][R128_QLDS * 64 * 16];
-  __shared__ __attribute__((aligned(16))) uint8_t p_lds[R128_ROWS * R128_PROW];
-  __shared__ float alpha_lds[R128_ROWS];
+  __shared__ __attribute__((aligned(16))) uint8_t q_tail_lds[NRB][R128_QLDS * 64 * 16];
+  __shared__ __attribute__((aligned(16))) uint8_t p_lds[ROWS * R128_PROW];
+  __shared__ float alpha_lds[ROWS];
   __shared__ PlanLds<R128_THREADS> plan;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int w = xcd_range_index(blockIdx.x, a.G);
+  // 128-row tiles keep a bundle's workgroups on one XCD; smaller tiles
+  // (one per request) take ranges in launch order, as the 16-row kernel does
+  const int w = (NRB == 4 || a.n_rt > 1) ? xcd_range_index(blockIdx.x, a.G) : (int)blockIdx.x;
   const int bund = w / a.n_rt, tile = w - bund * a.n_rt;
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
   int dma_sel_off[RING_DMA_PER_WAVE];  // per-lane constants of this wave's ring loads
@@ -1287,10 +1311,10 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
     request_tokens(a, bb, q_len, q_base);
     q_len = __builtin_amdgcn_readfirstlane(q_len);
     q_base = __builtin_amdgcn_readfirstlane(q_base);
-    if (rt * R128_ROWS >= q_len * a.H) return;
+    if (rt * ROWS >= q_len * a.H) return;
     const int32_t* btr = a.bt + (int64_t)bb * a.max_blocks;
-    const int my_row = rt * R128_ROWS + wave * 32 + (lane & 31);
-    const bool row_ok = my_row < q_len * a.H;
+    const int my_row = rt * ROWS + wave * 32 + (lane & 31);
+    const bool row_ok = wave < NRB && my_row < q_len * a.H;
     const int nrow = row_ok ? row_bound(seq, tot, q_len, my_row / a.H, a.W, a.rank, a.I, a.causal) : 0;
     // the smallest bound over the wave's rows: tiles below it are unmasked
     int nmin = nrow;
@@ -1298,8 +1322,8 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
     for (int off = 32; off > 0; off >>= 1) nmin = min(nmin, __shfl_xor(nmin, off, 64));
     nmin = __builtin_amdgcn_readfirstlane(nmin);
     bf16x8 qf[R128_QREG];
-    uint8_t* q_tail = q_tail_lds[wave];
-    {
+    uint8_t* q_tail = q_tail_lds[wave < NRB ? wave : 0];  // read by the score waves only
+    if (wave < NRB) {
       const uint8_t* qrow = a.q + ((int64_t)q_base * a.H + (row_ok ? my_row : 0)) * ROW_BYTES + 16 * (lane >> 5);
 #pragma unroll
       for (int kk = 0; kk < R128_QREG; ++kk) qf[kk] = row_ok ? gload_bf16x8(qrow + 32 * kk) : zero_bf16x8();
@@ -1308,9 +1332,9 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
         *reinterpret_cast<bf16x8*>(q_tail + (kk * 64 + lane) * 16) =
             row_ok ? gload_bf16x8(qrow + 32 * (R128_QREG + kk)) : zero_bf16x8();
     }
-    R128State st;
+    R128State<NRB> st;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) st.o[m] = f32x16{};
+    for (int m = 0; m < 4 * NRB; ++m) st.o[m] = f32x16{};
     st.m_ref = NEG_INF;
     st.l_part = 0.f;
     st.l_out = 0.f;
@@ -1358,13 +1382,13 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
         __syncthreads();
         // ... so its stage can take tile it+2, loaded while tile it is computed
         if constexpr (F8) {
-          r128_compute<true>(st, qf, q_tail, ring + cur, p_lds, alpha_lds, a.scale_log2, ka + it * R128_TILE, kb,
+          r128_compute<true, NRB>(st, qf, q_tail, ring + cur, p_lds, alpha_lds, a.scale_log2, ka + it * R128_TILE, kb,
                              nrow, min(kb, nmin), lane, wave,
                              [&](int m) __attribute__((always_inline)) { m16f8_issue(nxt8, m, wave); }, lane_off);
         } else {
           const RingRows nxt = r128_tile_rows(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb, ring_lds + nxt_off, wave,
                                               lane);
-          r128_compute<false>(st, qf, q_tail, ring + cur, p_lds, alpha_lds, a.scale_log2, ka + it * R128_TILE, kb,
+          r128_compute<false, NRB>(st, qf, q_tail, ring + cur, p_lds, alpha_lds, a.scale_log2, ka + it * R128_TILE, kb,
                               nrow, min(kb, nmin), lane, wave,
                               [&](int m) __attribute__((always_inline)) { ring_issue_one(nxt, m, wave, dma_sel_off); },
                               lane_off);
@@ -1404,9 +1428,9 @@ template <int ROWS>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   constexpr int SLICE = 64;                       // output columns per workgroup
   constexpr int PER = ROWS * SLICE / 256;         // outputs per thread
-  constexpr bool F16 = ROWS == R128_ROWS;
-  constexpr int64_t SLOT_BYTES = F16 ? R128_SLOT_BYTES : (ROWS * D_V + 3 * ROWS) * 4;
-  constexpr int O_BYTES = F16 ? R128_O_BYTES : ROWS * D_V * 4;
+  constexpr bool F16 = ROWS != M16_ROWS;  // slots of the 32-, 64- and 128-row tiles
+  constexpr int64_t SLOT_BYTES = F16 ? r128_slot_bytes(ROWS) : (ROWS * D_V + 3 * ROWS) * 4;
+  constexpr int O_BYTES = F16 ? r128_o_bytes(ROWS) : ROWS * D_V * 4;
   const int grp = blockIdx.x >> 3, slice = blockIdx.x & 7;
   const int b = grp / a.n_rt, rt = grp - b * a.n_rt;
   const int row = threadIdx.x % ROWS;
@@ -1532,7 +1556,7 @@ int device_cu_count() {
 Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool fp8 = false) {
   Plan p{};
   const int64_t R = (int64_t)q_len * H;
-  p.rows_tile = R <= M16_ROWS ? M16_ROWS : R128_ROWS;
+  p.rows_tile = R <= M16_ROWS ? M16_ROWS : R <= 32 ? 32 : R <= 64 ? 64 : R128_ROWS;
   p.n_rt = (int)((R + p.rows_tile - 1) / p.rows_tile);
   // per-group overhead in key units, about what a group's start and end
   // cost in ring time: M16 5 tiles (the query item, a partial tile, the
@@ -1548,7 +1572,7 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool fp8 = fal
   // keys through its L2; a few CUs idle when n_rt does not divide the CUs of
   // an XCD.
   // The 16-row kernel does the same when a request has several row tiles.
-  const int per_xcd = (p.rows_tile == R128_ROWS ? 1 : fp8 ? M16F8_WG_PER_CU : 1) * cus / 8;  // resident workgroups
+  const int per_xcd = (p.rows_tile != M16_ROWS ? 1 : fp8 ? M16F8_WG_PER_CU : 1) * cus / 8;  // resident workgroups
   int64_t nbund = p.n_rt == 1 ? 8 * per_xcd : p.n_rt <= per_xcd ? 8 * (per_xcd / p.n_rt) : 8 * per_xcd / p.n_rt;
   if (nbund < 1) nbund = 1;
   const int64_t units = (int64_t)B * ((max_seq_len > 0 ? max_seq_len : 1) + p.ovh);  // of one row tile
@@ -1557,7 +1581,7 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool fp8 = fal
   if (nbund < 1) nbund = 1;
   p.nbund = (int)nbund;
   p.G = p.nbund * p.n_rt;
-  const size_t slot = p.rows_tile == R128_ROWS ? (size_t)R128_SLOT_BYTES
+  const size_t slot = p.rows_tile != M16_ROWS ? (size_t)r128_slot_bytes(p.rows_tile)
                                                : (size_t)(p.rows_tile * D_V + 3 * p.rows_tile) * sizeof(float);
   p.prefix_off = 0;
   p.partial_off = align_up((size_t)(B + 1) * sizeof(int64_t));
@@ -1636,12 +1660,29 @@ int decode(const void* q, const int32_t* query_start_loc, const void* kv_cache, 
 
   // the attention kernel; with profiling events set, the runtime records
   // them at the kernel's own start and end (no separate marker packets)
-  void (*attn)(DecodeArgs) = p.rows_tile == M16_ROWS ? (kv_fp8 ? attn_m16_kernel<true> : attn_m16_kernel<false>)
-                                                     : (kv_fp8 ? attn_r128_kernel<true> : attn_r128_kernel<false>);
+  void (*attn)(DecodeArgs) = nullptr;
+  void (*comb)(DecodeArgs) = nullptr;
+  switch (p.rows_tile) {
+    case M16_ROWS:
+      attn = kv_fp8 ? attn_m16_kernel<true> : attn_m16_kernel<false>;
+      comb = combine_kernel<M16_ROWS>;
+      break;
+    case 32:
+      attn = kv_fp8 ? attn_r128_kernel<true, 1> : attn_r128_kernel<false, 1>;
+      comb = combine_kernel<32>;
+      break;
+    case 64:
+      attn = kv_fp8 ? attn_r128_kernel<true, 2> : attn_r128_kernel<false, 2>;
+      comb = combine_kernel<64>;
+      break;
+    default:
+      attn = kv_fp8 ? attn_r128_kernel<true, 4> : attn_r128_kernel<false, 4>;
+      comb = combine_kernel<R128_ROWS>;
+      break;
+  }
   const int threads = p.rows_tile == M16_ROWS ? M16_THREADS : R128_THREADS;
   if (launch(attn, dim3(p.G), dim3(threads), stream, a, tl_prof_start, tl_prof_stop) != hipSuccess)
     return MLA_ERR_HIP;
-  void (*comb)(DecodeArgs) = p.rows_tile == M16_ROWS ? combine_kernel<M16_ROWS> : combine_kernel<R128_ROWS>;
   if (launch(comb, dim3(B * p.n_rt * 8), dim3(256), stream, a) != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }

@@ -43,6 +43,8 @@ CASES = [
     spec("fp8_bs80_h128_q4_dcp2", 2, 128, 4, True, [161, 3000], W=2, bs=80),
     spec("fp8_bs48_h16_q1", 3, 16, 1, True, [48, 49, 3000], global_is_null=True, bs=48),
     spec("fp8_bs80_h16_q1", 3, 16, 1, True, [79, 800, 2500], global_is_null=True, bs=80),
+    spec("fp8_rows24_h24_q1", 2, 24, 1, True, [40, 3000], global_is_null=True),
+    spec("fp8_rows48_h16_q3_dcp2", 2, 16, 3, True, [500, 3000], W=2),
 ]
 
 

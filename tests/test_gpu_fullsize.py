@@ -41,7 +41,7 @@ def wait_oracle(proc, label):
     assert rc == 0, f"{label}: the oracle process failed ({rc})"
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 5])
+@pytest.mark.parametrize("cfg", [2, 3, 5, 6])
 def test_full_size_rank_matches_oracle_on_every_element(cfg, tmp_path):
     spec = WL.config(cfg)
     say(f"{spec.name}: oracle started in a worker pool; generating")

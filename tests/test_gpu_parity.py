@@ -76,6 +76,14 @@ CASES = [
     spec("bs80_h128_q4_dcp2", 2, 128, 4, True, [161, 3000], W=2, bs=80),
     spec("bs48_h16_q1", 4, 16, 1, True, [1, 48, 49, 3000], global_is_null=True, bs=48),
     spec("bs80_h16_q1_dcp3", 3, 16, 1, True, [79, 800, 2500], W=3, bs=80),
+    # 17-32 and 33-64 rows per request: the 32- and 64-row tiles (one or two
+    # score waves), full and partly filled
+    spec("rows24_h24_q1", 3, 24, 1, True, [40, 1000, 3000], global_is_null=True),
+    spec("rows32_h16_q2_dcp2", 3, 16, 2, True, [5, 700, 2600], W=2),
+    spec("rows48_h48_q1", 2, 48, 1, True, [900, 4100], global_is_null=True),
+    spec("rows64_h16_q4_spec", 4, 16, 4, True, [3, 64, 1500, 5000], global_is_null=True),
+    spec("rows48_h16_q3_dcp2_bs48", 2, 16, 3, True, [500, 3000], W=2, bs=48),
+    spec("rows64_h16_q4_noncausal_dcp4_interleave2", 2, 16, 4, False, [100, 2100], W=4, interleave=2),
 ]
 
 

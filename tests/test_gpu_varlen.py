@@ -20,6 +20,7 @@ CASES = [
     ("h128_skipped_row_tiles", 128, [4, 1, 2], [70, 900, 1600], 2, True, 1),
     ("h16_noncausal_dcp2", 16, [16, 3, 0, 9], [100, 2500, 40, 800], 2, False, 1),
     ("h24_interleave2_dcp3", 24, [3, 1, 2, 3], [31, 400, 1111, 90], 3, True, 2),
+    ("h16_rows64_tile", 16, [4, 1, 3, 0], [700, 30, 2500, 90], 1, True, 1),
 ]
 
 

@@ -317,7 +317,7 @@ def draft_slot_inputs(wl: Workload, n_draft: int = 16) -> dict:
 # --- the five workloads the measurements use -------------------------------
 
 def config(n: int, **overrides) -> Spec:
-    """Workload n in 1..5 (sizes of the single- and multi-token MLA decode cases)."""
+    """Workload n in 1..6 (sizes of the single- and multi-token MLA decode cases)."""
     base = {
         1: dict(name="tiny_b2_h16_q1", B=2, H=16, Q=1, causal=True, seed=1001, lengths=[37, 100],
                 pool_blocks=4, global_is_null=True),
@@ -329,6 +329,10 @@ def config(n: int, **overrides) -> Spec:
                 lengths=("uniform", 32768, 131072), W=8, ranks=tuple(range(8))),
         5: dict(name="dcp2r1_b16_h128_q16_noncausal_len64k-256k", B=16, H=128, Q=16, causal=False, seed=1005,
                 lengths=("uniform", 65536, 262144), W=2, ranks=(1,)),
+        # beyond the five: speculative decode with 16 heads (a tensor-parallel
+        # shard of the heads) and q_len 4, 64 rows per request
+        6: dict(name="spec_b64_h16_q4_causal_len1k-8k", B=64, H=16, Q=4, causal=True, seed=1006,
+                lengths=("uniform", 1024, 8192), global_is_null=True),
     }[n]
     base.update(overrides)
     return Spec(**base)
