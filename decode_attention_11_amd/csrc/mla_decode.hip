@@ -962,18 +962,24 @@ __device__ __forceinline__ F8Loads r128f8_loads(const DecodeArgs& a, const int* 
 // stage base is one wave-uniform value per tile, so every address costs a
 // single add).
 struct R128LaneOff {
-  uint32_t k[4];      // K fragment of k-step 4a + b: k[b] + 128a
+  uint32_t k[4];      // K fragment of the wave's k-step kb0 + 4a + b: k[b] + 128a
   uint32_t v[2][2];   // V^T transposed reads [rd][d%2]: + 16*1152*ks + 128*(d/2)
 };
 
-__device__ __forceinline__ R128LaneOff r128_lane_offsets(int lane, int wave) {
+// kb0: the wave's first k-step (0, or the first of its slice of the 576
+// dims when the scores of a row block are split across waves)
+__device__ __forceinline__ R128LaneOff r128_lane_offsets(int lane, int wave, int kb0 = 0) {
   R128LaneOff lo;
   const int r = lane & 31, h = lane >> 5;
-  // k-step kk = 4a + b reads logical chunk 2kk + h of row r: physical byte
-  // 128a + 16*((2b + h) ^ f(r)) of the row
+  // k-step kk reads logical chunk c = 2kk + h of row r, at physical chunk
+  // (c & ~7) | ((c ^ f(r)) & 7); four k-steps further is 8 chunks (128 bytes)
+  // further in both
   const int fk = ring_swz(r);
 #pragma unroll
-  for (int b = 0; b < 4; ++b) lo.k[b] = r * R128_ROWB + 16 * ((2 * b + h) ^ fk);
+  for (int b = 0; b < 4; ++b) {
+    const int c = 2 * (kb0 + b) + h;
+    lo.k[b] = r * R128_ROWB + 16 * ((c & ~7) | ((c ^ fk) & 7));
+  }
   // V^T: lane (q, i16) of a transposed read covers key row 8h + 4rd + i16/4
   // (+16ks), logical chunk 4D + 2(q%2) + (i16%4)/2 for D = 4w + d, byte
   // 8(i16%2)
@@ -1009,10 +1015,87 @@ template <bool F8, int NRB, class Issue>
 __device__ __forceinline__ void r128_compute(R128State<NRB>& st, const bf16x8 (&qf)[r128_qreg<F8>],
                                              const uint8_t* q_tail, const uint8_t* stage, uint8_t* p_lds,
                                              float* alpha_lds, float scale_log2, int ts, int k1, int nrow, int kfull,
-                                             int lane, int wave, Issue&& issue, const R128LaneOff& lo) {
+                                             int lane, int wave, Issue&& issue, const R128LaneOff& lo,
+                                             uint8_t* xchg) {
   constexpr int R128_QREG = r128_qreg<F8>;
   const int r = lane & 31, h = lane >> 5;
-  if (wave < NRB) {
+  if constexpr (NRB < 4) {
+    // 32- and 64-row tiles: the score MFMAs of row block rb are split across
+    // the DS = 4/NRB waves rb + NRB*s by dims (wave slice s: k-steps
+    // s*KS .. s*KS + KS-1), the slices s > 0 hand their partial S^T to the
+    // slice-0 wave through LDS, which adds them in slice order and runs the
+    // softmax of the block's rows
+    constexpr int DS = 4 / NRB, KS = 36 / DS;
+    const int slice = wave / NRB;
+    f32x16 sc = {};
+    const uint8_t* kp8 = stage + M16F8_ROW * r + 8 * h;
+    const int krot = f8_rot(r);
+    const int kb0 = slice * KS;
+    bf16x8 kf[4];
+    auto k_at = [&](int j) __attribute__((always_inline)) {
+      if constexpr (F8) {
+        const int kk = kb0 + j;
+        const int pos = kk < 32 ? (kk + krot) & 31 : 32 + ((kk + krot) & 3);
+        const uint2 x = *reinterpret_cast<const uint2*>(kp8 + 16 * pos);
+        return f8x8_to_bf16(x.x, x.y);
+      } else {
+        return *reinterpret_cast<const bf16x8*>(stage + lo.k[j & 3] + 128 * (j >> 2));
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < 3; ++j) kf[j] = k_at(j);
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      if (j + 3 < KS) kf[(j + 3) % 4] = k_at(j + 3);
+      // the wave's ring loads of a later tile, spread over its MFMAs
+      constexpr int NL = F8 ? 5 : RING_DMA_PER_WAVE;
+#pragma unroll
+      for (int m = 0; m < NL; ++m)
+        if ((m * KS) / NL == j) issue(m);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % 4], qf[j], sc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    f32x16* xw = reinterpret_cast<f32x16*>(xchg) + (size_t)(wave - NRB) * 64 + lane;
+    if (slice > 0) *xw = sc;
+    __syncthreads();
+    if (slice == 0) {
+#pragma unroll
+      for (int s = 1; s < DS; ++s) sc += reinterpret_cast<const f32x16*>(xchg)[(size_t)(s * NRB + wave - NRB) * 64 + lane];
+      float mx = NEG_INF;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int t = ts + 8 * (i >> 2) + 4 * h + (i & 3);
+        sc[i] = (t < k1 && t < nrow) ? sc[i] * scale_log2 : NEG_INF;
+        mx = fmaxf(mx, sc[i]);
+      }
+      float alpha = 1.f;
+      if (__ballot(mx > st.m_ref + R128_RESCALE_LOG2) != 0) {
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        if (mx > st.m_ref + R128_RESCALE_LOG2) {
+          alpha = fast_exp2(st.m_ref - mx);
+          st.l_part *= alpha;
+          st.l_out *= alpha;
+          st.m_ref = mx;
+        }
+      }
+      const float m_sub = st.m_ref == NEG_INF ? 0.f : st.m_ref;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sc[i] = fast_exp2(sc[i] - m_sub);
+        st.l_part += sc[i];
+      }
+      uint8_t* prow = p_lds + (32 * wave + r) * R128_PROW + 8 * h;
+      bf16x4 p4[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        p4[q] = to_bf16x4(sc[4 * q + 0], sc[4 * q + 1], sc[4 * q + 2], sc[4 * q + 3]);
+        *reinterpret_cast<bf16x4*>(prow + 16 * q) = p4[q];
+      }
+      st.l_out = sum_bf16x8(__builtin_shufflevector(p4[0], p4[1], 0, 1, 2, 3, 4, 5, 6, 7), st.l_out);
+      st.l_out = sum_bf16x8(__builtin_shufflevector(p4[2], p4[3], 0, 1, 2, 3, 4, 5, 6, 7), st.l_out);
+      if (h == 0) alpha_lds[32 * wave + r] = alpha;
+    }
+  } else {
   // ---- scores of this wave's rows: S^T[key][row], lane holds keys
   // 8*(i/4) + 4h + i%4 of row r
   f32x16 sc = {};
@@ -1110,11 +1193,6 @@ __device__ __forceinline__ void r128_compute(R128State<NRB>& st, const bf16x8 (&
   st.l_out = sum_bf16x8(__builtin_shufflevector(p4[0], p4[1], 0, 1, 2, 3, 4, 5, 6, 7), st.l_out);
   st.l_out = sum_bf16x8(__builtin_shufflevector(p4[2], p4[3], 0, 1, 2, 3, 4, 5, 6, 7), st.l_out);
   if (h == 0) alpha_lds[32 * wave + r] = alpha;
-  } else {
-    // a wave without score rows (tiles of fewer than 128 rows) only issues
-    // its ring loads of the later tile
-#pragma unroll
-    for (int m = 0; m < (F8 ? 5 : RING_DMA_PER_WAVE); ++m) issue(m);
   }
   __syncthreads();
   // O^T[dv][row] += V^T[dv][key] P^T[key][row] over 2 k-steps of 16 keys:
@@ -1288,7 +1366,10 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
   __shared__ __attribute__((aligned(1024))) uint8_t ring[R128_NS * STAGE];
   __shared__ int bt_lds[R128_BT_WIN];
   constexpr int R128_QREG = r128_qreg<F8>, R128_QLDS = r128_qlds<F8>;
-  __shared__ __attribute__((aligned(16))) uint8_t q_tail_lds[NRB][R128_QLDS * 64 * 16];
+  // the 128-row tile keeps Q^T's last k-steps here; smaller tiles exchange
+  // partial scores between the waves of a row block here instead
+  __shared__ __attribute__((aligned(16)))
+  uint8_t q_tail_lds[NRB == 4 ? 4 * R128_QLDS * 64 * 16 : (4 - NRB) * 64 * 64];
   __shared__ __attribute__((aligned(16))) uint8_t p_lds[ROWS * R128_PROW];
   __shared__ float alpha_lds[ROWS];
   __shared__ PlanLds<R128_THREADS> plan;
@@ -1301,7 +1382,10 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
   int dma_sel_off[RING_DMA_PER_WAVE];  // per-lane constants of this wave's ring loads
   ring_dma_offsets(dma_sel_off, wave, lane);
-  const R128LaneOff lane_off = r128_lane_offsets(lane, wave);
+  // the wave's row block and, for tiles under 128 rows, its slice of the dims
+  const int wrb = NRB == 4 ? wave : wave % NRB;
+  const int wkb0 = NRB == 4 ? 0 : (wave / NRB) * (36 / (4 / NRB));
+  const R128LaneOff lane_off = r128_lane_offsets(lane, wave, wkb0);
 
   for_each_piece<R128_THREADS>(a, bund, tile, plan, [&](int bb, int rt, int k0, int k1, int seq, int tot) {
     // ---- one piece: rows [128 rt, 128 rt + 128) of request bb, keys [k0, k1);
@@ -1322,8 +1406,8 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
     for (int off = 32; off > 0; off >>= 1) nmin = min(nmin, __shfl_xor(nmin, off, 64));
     nmin = __builtin_amdgcn_readfirstlane(nmin);
     bf16x8 qf[R128_QREG];
-    uint8_t* q_tail = q_tail_lds[wave < NRB ? wave : 0];  // read by the score waves only
-    if (wave < NRB) {
+    uint8_t* q_tail = q_tail_lds + (NRB == 4 ? wave * R128_QLDS * 64 * 16 : 0);
+    if constexpr (NRB == 4) {
       const uint8_t* qrow = a.q + ((int64_t)q_base * a.H + (row_ok ? my_row : 0)) * ROW_BYTES + 16 * (lane >> 5);
 #pragma unroll
       for (int kk = 0; kk < R128_QREG; ++kk) qf[kk] = row_ok ? gload_bf16x8(qrow + 32 * kk) : zero_bf16x8();
@@ -1331,6 +1415,14 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
       for (int kk = 0; kk < R128_QLDS; ++kk)
         *reinterpret_cast<bf16x8*>(q_tail + (kk * 64 + lane) * 16) =
             row_ok ? gload_bf16x8(qrow + 32 * (R128_QREG + kk)) : zero_bf16x8();
+    } else {
+      // this wave's slice of the dims of its row block's query rows
+      constexpr int KS = 36 / (4 / NRB);
+      const int qr = rt * ROWS + wrb * 32 + (lane & 31);
+      const bool q_ok = qr < q_len * a.H;
+      const uint8_t* qrow = a.q + ((int64_t)q_base * a.H + (q_ok ? qr : 0)) * ROW_BYTES + 16 * (lane >> 5) + 32 * wkb0;
+#pragma unroll
+      for (int j = 0; j < KS; ++j) qf[j] = q_ok ? gload_bf16x8(qrow + 32 * j) : zero_bf16x8();
     }
     R128State<NRB> st;
 #pragma unroll
@@ -1384,14 +1476,15 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
         if constexpr (F8) {
           r128_compute<true, NRB>(st, qf, q_tail, ring + cur, p_lds, alpha_lds, a.scale_log2, ka + it * R128_TILE, kb,
                              nrow, min(kb, nmin), lane, wave,
-                             [&](int m) __attribute__((always_inline)) { m16f8_issue(nxt8, m, wave); }, lane_off);
+                             [&](int m) __attribute__((always_inline)) { m16f8_issue(nxt8, m, wave); }, lane_off,
+                                  q_tail_lds);
         } else {
           const RingRows nxt = r128_tile_rows(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb, ring_lds + nxt_off, wave,
                                               lane);
           r128_compute<false, NRB>(st, qf, q_tail, ring + cur, p_lds, alpha_lds, a.scale_log2, ka + it * R128_TILE, kb,
                               nrow, min(kb, nmin), lane, wave,
                               [&](int m) __attribute__((always_inline)) { ring_issue_one(nxt, m, wave, dma_sel_off); },
-                              lane_off);
+                              lane_off, q_tail_lds);
         }
         nxt_off = cur;
         cur = __builtin_amdgcn_readfirstlane(cur == (R128_NS - 1) * STAGE ? 0u : cur + STAGE);
