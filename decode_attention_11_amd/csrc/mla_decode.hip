@@ -124,8 +124,8 @@ __device__ __forceinline__ int xcd_range_index(int block, int G) {
 // also stores them for the combine kernel.
 template <int NT>
 __device__ __forceinline__ int64_t block_sum_i64(int64_t v, int64_t* s_red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int lane = lane_id_fresh(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int off = 32; off > 0; off >>= 1) v += shfl_i64(v, lane ^ off);
   __syncthreads();
   if (lane == 0) s_red[wave] = v;
   __syncthreads();
@@ -136,9 +136,9 @@ __device__ __forceinline__ int64_t block_sum_i64(int64_t v, int64_t* s_red) {
 
 template <int NT>
 __device__ __forceinline__ int64_t block_incl_scan_i64(int64_t v, int64_t* s_red, int64_t& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = lane_id_fresh(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   for (int off = 1; off < 64; off <<= 1) {
-    const int64_t y = __shfl_up(v, off, 64);
+    const int64_t y = shfl_i64(v, lane >= off ? lane - off : lane);
     if (lane >= off) v += y;
   }
   __syncthreads();
@@ -184,40 +184,63 @@ __device__ __forceinline__ void request_piece(const DecodeArgs& a, int bb, int64
 // kernel.  All arguments of piece() are wave-uniform.  The workgroup scans
 // the requests in chunks of NT, reading each length once per chunk (with up
 // to NT requests one scan gives both the total and the offsets).
+// A 64-bit value that is the same in every lane, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// What the plan keeps across the pieces is wave-uniform (scalar registers)
+// or in LDS: a per-lane value live across the piece loop would be spilled,
+// and each reload waits for every vector-memory operation in flight.
 template <int NT, class F>
 __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int j, int rt, PlanLds<NT>& pl, F&& piece) {
   const int tid = threadIdx.x;
-  int nb, seq, tot;
-  request_info(a, tid, nb, seq, tot);
-  int64_t total0;
-  const int64_t incl0 = block_incl_scan_i64<NT>(request_units(a, nb), pl.red, total0);
-  int64_t T = total0;
-  for (int base = NT; base < a.B; base += NT) {
-    int nb2, seq2, tot2;
-    request_info(a, base + tid, nb2, seq2, tot2);
-    T += block_sum_i64<NT>(request_units(a, nb2), pl.red);
+  int64_t T, total0;
+  {
+    // chunk 0's offsets and lengths go to LDS for the first pass below
+    int nb, seq, tot;
+    request_info(a, tid, nb, seq, tot);
+    int64_t t0;
+    const int64_t incl0 = block_incl_scan_i64<NT>(request_units(a, nb), pl.red, t0);
+    pl.excl[tid] = incl0 - request_units(a, nb);
+    pl.nb[tid] = nb;
+    pl.seq[tid] = seq;
+    pl.tot[tid] = tot;
+    total0 = uniform_i64(t0);
+    T = total0;
+    for (int base = NT; base < a.B; base += NT) {
+      int nb2, seq2, tot2;
+      request_info(a, base + tid, nb2, seq2, tot2);
+      T += uniform_i64(block_sum_i64<NT>(request_units(a, nb2), pl.red));
+    }
   }
-  const int64_t u0 = floordiv((int64_t)j * T, a.nbund), u1 = floordiv((int64_t)(j + 1) * T, a.nbund);
+  const int64_t u0 = uniform_i64(floordiv((int64_t)j * T, a.nbund));
+  const int64_t u1 = uniform_i64(floordiv((int64_t)(j + 1) * T, a.nbund));
 
   int64_t carry = 0;
   for (int base = 0; base < a.B; base += NT) {
-    int64_t incl = incl0, chunk_total = total0;
+    int64_t chunk_total = total0;
     if (base > 0) {
+      int nb, seq, tot;
       request_info(a, base + tid, nb, seq, tot);
-      incl = block_incl_scan_i64<NT>(request_units(a, nb), pl.red, chunk_total);
+      int64_t t;
+      const int64_t incl = block_incl_scan_i64<NT>(request_units(a, nb), pl.red, t);
+      chunk_total = uniform_i64(t);
+      pl.excl[tid] = incl - request_units(a, nb) + carry;
+      pl.nb[tid] = nb;
+      pl.seq[tid] = seq;
+      pl.tot[tid] = tot;
     }
     const int b = base + tid;
-    const int64_t x = request_units(a, nb);
-    incl += carry;
-    const int64_t excl = incl - x;
+    const int64_t excl = pl.excl[tid];
+    const int64_t x = request_units(a, pl.nb[tid]);
+    const int64_t incl = excl + x;
     if (j == 0 && rt == 0 && b < a.B) {
       a.prefix[b + 1] = incl;
       if (b == 0) a.prefix[0] = 0;
     }
-    pl.excl[tid] = excl;
-    pl.nb[tid] = nb;
-    pl.seq[tid] = seq;
-    pl.tot[tid] = tot;
     // the requests overlapping the range are contiguous: each wave finds its
     // first and last one by ballot, one barrier publishes them
     const uint64_t hit = __ballot(x > 0 && excl < u1 && incl > u0);
@@ -233,12 +256,14 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int j, int r
       first = min(first, pl.first_last[0][v]);
       last = max(last, pl.first_last[1][v]);
     }
+    first = __builtin_amdgcn_readfirstlane(first);
+    last = __builtin_amdgcn_readfirstlane(last);
     carry += chunk_total;
 
     for (int i = first; i <= last; ++i)
-      request_piece(a, __builtin_amdgcn_readfirstlane(base + i), pl.excl[i], __builtin_amdgcn_readfirstlane(pl.nb[i]),
-                    __builtin_amdgcn_readfirstlane(pl.seq[i]), __builtin_amdgcn_readfirstlane(pl.tot[i]), u0, u1, rt,
-                    piece);
+      request_piece(a, __builtin_amdgcn_readfirstlane(base + i), uniform_i64(pl.excl[i]),
+                    __builtin_amdgcn_readfirstlane(pl.nb[i]), __builtin_amdgcn_readfirstlane(pl.seq[i]),
+                    __builtin_amdgcn_readfirstlane(pl.tot[i]), u0, u1, rt, piece);
     __syncthreads();
   }
 }
@@ -1070,7 +1095,7 @@ __device__ __forceinline__ void r128_compute(R128State<NRB>& st, const bf16x8 (&
       }
       float alpha = 1.f;
       if (__ballot(mx > st.m_ref + R128_RESCALE_LOG2) != 0) {
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = fmaxf(mx, shfl_xor_fresh(mx, 32));
         if (mx > st.m_ref + R128_RESCALE_LOG2) {
           alpha = fast_exp2(st.m_ref - mx);
           st.l_part *= alpha;
@@ -1165,7 +1190,7 @@ __device__ __forceinline__ void r128_compute(R128State<NRB>& st, const bf16x8 (&
   }
   float alpha = 1.f;
   if (__ballot(mx > st.m_ref + R128_RESCALE_LOG2) != 0) {
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = fmaxf(mx, shfl_xor_fresh(mx, 32));
     if (mx > st.m_ref + R128_RESCALE_LOG2) {
       alpha = fast_exp2(st.m_ref - mx);
       st.l_part *= alpha;
@@ -1305,8 +1330,8 @@ __device__ __forceinline__ void r128_store_slot(const DecodeArgs& a, const R128S
   // their largest magnitude lies in [2^14, 2^15), inside fp16's range and
   // above its subnormals.  The accumulator columns span all 128 rows,
   // whose sums the owning waves publish through LDS.
-  const float l_row = st.l_part + __shfl_xor(st.l_part, 32, 64);
-  const float lo_row = st.l_out + __shfl_xor(st.l_out, 32, 64);
+  const float l_row = st.l_part + shfl_xor_fresh(st.l_part, 32);
+  const float lo_row = st.l_out + shfl_xor_fresh(st.l_out, 32);
   uint8_t* slot = reinterpret_cast<uint8_t*>(a.partials) + slot_idx * r128_slot_bytes(ROWS);
   float* pm = reinterpret_cast<float*>(slot + r128_o_bytes(ROWS));
   const int r = lane & 31, h = lane >> 5;
@@ -1325,7 +1350,7 @@ __device__ __forceinline__ void r128_store_slot(const DecodeArgs& a, const R128S
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(st.o[NRB * d + rb][i]));
     mx *= inv[rb];
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = fmaxf(mx, shfl_xor_fresh(mx, 32));
     int e = 0;
     if (mx > 0.f && mx <= 3.0e38f) {
       frexpf(mx, &e);  // mx < 2^e
@@ -1397,17 +1422,67 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
     q_base = __builtin_amdgcn_readfirstlane(q_base);
     if (rt * ROWS >= q_len * a.H) return;
     const int32_t* btr = a.bt + (int64_t)bb * a.max_blocks;
-    const int my_row = rt * ROWS + wave * 32 + (lane & 31);
+    const int lf = lane_id_fresh();
+    const int row0 = rt * ROWS + wave * 32;  // the wave's first row
+    const int my_row = row0 + (lf & 31);
     const bool row_ok = wave < NRB && my_row < q_len * a.H;
     const int nrow = row_ok ? row_bound(seq, tot, q_len, my_row / a.H, a.W, a.rank, a.I, a.causal) : 0;
-    // the smallest bound over the wave's rows: tiles below it are unmasked
-    int nmin = nrow;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) nmin = min(nmin, __shfl_xor(nmin, off, 64));
+    // the smallest bound over the wave's rows (tiles below it are unmasked):
+    // a row's bound grows with its query token, so it is the first row's
+    // bound, or 0 when a row of the wave lies past the request's rows
+    int nmin = 0;
+    if (wave < NRB && row0 + 31 < q_len * a.H) nmin = row_bound(seq, tot, q_len, row0 / a.H, a.W, a.rank, a.I, a.causal);
     nmin = __builtin_amdgcn_readfirstlane(nmin);
     bf16x8 qf[R128_QREG];
     uint8_t* q_tail = q_tail_lds + (NRB == 4 ? wave * R128_QLDS * 64 * 16 : 0);
-    if constexpr (NRB == 4) {
+    if constexpr (!F8) {
+      // the tile's query rows come through the ring like key tiles (32 rows
+      // per stage, 1 KiB contiguous loads, rows past the request's rows
+      // read the zero row): row blocks 0 .. 2 into stages 0 .. 2, then row
+      // block 3 into stage 0.  Each wave reads its fragments from its row
+      // block's stage in the key fragments' layout (k-step kb0 + j at
+      // lane_off.k[j % 4] + 128 (j / 4)).  The previous piece's waves are
+      // all past their last ring read (the barrier before its slot store).
+      const R128LaneOff qlo = r128_lane_offsets(lf, wave, wkb0);
+      auto q_rows = [&](int rb, uint32_t stage_lds) __attribute__((always_inline)) {
+        const int row = rt * ROWS + 32 * rb + 8 * wave + (lf & 7);
+        const uint8_t* rowp = reinterpret_cast<const uint8_t*>(kZeroRow);
+        asm volatile("" : "+v"(rowp));
+        if (row < q_len * a.H) rowp = a.q + ((int64_t)q_base * a.H + row) * ROW_BYTES;
+        return ring_rows(rowp, stage_lds);
+      };
+      auto q_frags = [&](const uint8_t* stage) __attribute__((always_inline)) {
+        if constexpr (NRB == 4) {
+#pragma unroll
+          for (int kk = 0; kk < R128_QREG; ++kk)
+            qf[kk] = *reinterpret_cast<const bf16x8*>(stage + qlo.k[kk & 3] + 128 * (kk >> 2));
+#pragma unroll
+          for (int kk = R128_QREG; kk < 36; ++kk)
+            *reinterpret_cast<bf16x8*>(q_tail + ((kk - R128_QREG) * 64 + lf) * 16) =
+                *reinterpret_cast<const bf16x8*>(stage + qlo.k[kk & 3] + 128 * (kk >> 2));
+        } else {
+          constexpr int KS = 36 / (4 / NRB);
+#pragma unroll
+          for (int j = 0; j < KS; ++j)
+            qf[j] = *reinterpret_cast<const bf16x8*>(stage + qlo.k[j & 3] + 128 * (j >> 2));
+        }
+      };
+      constexpr int R1 = NRB < 3 ? NRB : 3;
+#pragma unroll
+      for (int rb = 0; rb < R1; ++rb) ring_issue_all(q_rows(rb, ring_lds + rb * STAGE), wave, dma_sel_off);
+      WAIT_VMCNT(0);
+      __syncthreads();
+      if (wrb < R1) q_frags(ring + wrb * STAGE);
+      if constexpr (NRB == 4) {
+        __syncthreads();
+        ring_issue_all(q_rows(3, ring_lds), wave, dma_sel_off);
+        WAIT_VMCNT(0);
+        __syncthreads();
+        if (wave == 3) q_frags(ring);
+      }
+      // the sub-piece loop's first barrier orders these reads before the
+      // prologue's loads into stage 0
+    } else if constexpr (NRB == 4) {
       const uint8_t* qrow = a.q + ((int64_t)q_base * a.H + (row_ok ? my_row : 0)) * ROW_BYTES + 16 * (lane >> 5);
 #pragma unroll
       for (int kk = 0; kk < R128_QREG; ++kk) qf[kk] = row_ok ? gload_bf16x8(qrow + 32 * kk) : zero_bf16x8();

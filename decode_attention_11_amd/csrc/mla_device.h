@@ -104,6 +104,30 @@ __device__ __forceinline__ int row_bound(int seq, int tot, int q_len, int j, int
   return n < seq ? (int)n : seq;
 }
 
+// The lane's index in its wave, computed afresh from the execution mask
+// (two instructions).  Code that runs once per piece, between long loops
+// that need every register, takes it from here: a lane index or anything
+// derived from it that is kept across such a loop is spilled, and each
+// reload waits for all vector-memory operations in flight.  The opaque zero
+// keeps the compiler from hoisting the computation out of the loop.
+__device__ __forceinline__ int lane_id_fresh() {
+  uint32_t z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, z));
+}
+
+// Lane shuffles whose source lane is derived from lane_id_fresh() at the
+// point of use (ds_bpermute reads lane addr/4 of its source).
+__device__ __forceinline__ float shfl_xor_fresh(float x, int off) {
+  const int src = lane_id_fresh() ^ off;
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
+}
+__device__ __forceinline__ int64_t shfl_i64(int64_t v, int src) {
+  const int lo = __builtin_amdgcn_ds_bpermute(src << 2, (int)(uint32_t)v);
+  const int hi = __builtin_amdgcn_ds_bpermute(src << 2, (int)(uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
 // Index of the balanced work range that holds unit u when T units are cut
 // into G ranges [floor(w*T/G), floor((w+1)*T/G)).
 __device__ __forceinline__ int range_owner(int64_t u, int64_t T, int G) {
