@@ -1731,9 +1731,13 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool fp8 = fal
   // 33 KB partial store and the pipeline refill behind them; 160 units ran
   // about 1% faster than 64, 128, 192 or 256 on the batch-64 single-token
   // workload), 4.5 with an FP8 cache (its tiles carry half the bytes, the
-  // query item and the store do not shrink), R128 ~3 tiles (query load,
-  // ring refill and the 130 KB partial store)
-  p.ovh = p.rows_tile == M16_ROWS ? (fp8 ? 144 : 160) : 96;
+  // query item and the store do not shrink); the larger tiles ~7 tiles
+  // (row bounds, query rows, block-table window, ring refill and the
+  // partial store: per-workgroup timestamps put a 128-row piece at about
+  // 11 us, against 2.1-2.3 us per 32-key tile; 224 ran 2% faster than 96
+  // on the DCP-8 shard and 5% on the 16-head spec-decode workload, and as
+  // fast as 160 or 288 or faster)
+  p.ovh = p.rows_tile == M16_ROWS ? (fp8 ? 144 : 160) : 224;
   // bundles: balanced key ranges, each processed by n_rt workgroups (one per
   // row tile).  The 128-row kernel keeps a bundle's workgroups on one XCD
   // (8 * k bundles, each XCD holding k whole bundles) so that they share the
