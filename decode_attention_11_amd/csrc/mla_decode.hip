@@ -926,11 +926,9 @@ constexpr int r128_slot_bytes(int rows) { return r128_o_bytes(rows) + 7 * rows *
 constexpr int R128_O_BYTES = r128_o_bytes(R128_ROWS);
 constexpr int R128_SLOT_BYTES = r128_slot_bytes(R128_ROWS);
 constexpr int R128_BT_WIN = 1024;             // block-table entries held in LDS per sub-piece
-// Q^T k-steps (of 16 dims) kept in registers; the rest in LDS.  The FP8
-// instance's ring takes half the LDS, so it moves more of Q^T there and
-// frees registers for its conversions.
-template <bool F8> constexpr int r128_qreg = F8 ? 20 : 28;
-template <bool F8> constexpr int r128_qlds = 36 - r128_qreg<F8>;
+// Q^T k-steps (of 16 dims) kept in registers; the rest in LDS.
+constexpr int R128_QREG = 28;
+constexpr int R128_QLDS = 36 - R128_QREG;
 constexpr int R128_PROW = 80;                 // LDS bytes per row of the P tile (64 + 16: conflict-free reads)
 constexpr float R128_RESCALE_LOG2 = 8.f;
 
@@ -952,35 +950,103 @@ __device__ __forceinline__ RingRows r128_tile_rows(const DecodeArgs& a, const in
   return ring_rows(rowp, stage_lds);
 }
 
-// FP8 cache: source addresses of this wave's loads of tile [ts, ts+32) (the
-// layout and load split of the 16-row kernel's FP8 key items).
-__device__ __forceinline__ F8Loads r128f8_loads(const DecodeArgs& a, const int* bt_lds, int e0, int ts, int k1,
-                                                uint32_t stage_lds, int wave, int lane) {
-  // the per-lane parts of the addresses (chunk positions, zero-row
-  // defaults) are recomputed for every tile: hoisted out of the tile loop
-  // they are spilled, and each reload's wait would also drain the ring loads
-  // still in flight
-  asm volatile("" : "+v"(lane));
-  F8Loads L;
-  L.lds = stage_lds;
-  const uint8_t* zero = reinterpret_cast<const uint8_t*>(kZeroRow);
-#pragma unroll
-  for (int m = 0; m < 5; ++m) {
-    const int P = 64 * (wave + 4 * m) + lane;
-    const int r = P / (M16F8_ROW / 16), q = P - (M16F8_ROW / 16) * r;
-    const int ch = f8_chunk_at(r, q);
-    const int t = ts + r;
-    const uint8_t* p = zero + 16 * ch;
-    asm volatile("" : "+v"(p));
-    if (wave + 4 * m < M16F8_LOADS && t < k1) {
-      const int vb = block_of(a, t);
-      const int blk = bt_lds[vb - e0];
-      if ((unsigned)blk < (unsigned)a.num_blocks)
-        p = a.kv + ((int64_t)blk * a.bs + (t - vb * a.bs)) * M16F8_ROW + 16 * ch;
+// An E4M3 tile of zeros: the source of every key past the piece or in an
+// invalid block.
+__device__ __attribute__((aligned(64))) const uint4 kZeroTileF8[M16F8_RAW / 16] = {};
+
+// FP8 cache: what the loads of tile [ts, ts+32) need, all wave-uniform.
+// The stage holds the tile's 32 E4M3 rows row-major (576 bytes each; the
+// tile is widened before any fragment is read), filled by 18 one-KiB loads:
+// load g (g = wave + 4m, m < 5, g < 18) copies stage bytes 1024 g .. +1023.
+// With blocks of 32 keys or more the tile lies in at most two blocks, each
+// holding its rows contiguously, so stage byte 16 P comes from base + 16 P
+// with base = a (rows before `split`), b (rows from `split` on) or the zero
+// tile (rows at or past `rows`): two compares per load instead of a
+// block-table lookup per lane.  Smaller blocks look each row up at issue.
+struct F8Tile {
+  const uint8_t* a;
+  const uint8_t* b;
+  int split16, rows16;  // 576 * split and 576 * rows: byte bounds within the tile
+  int ts, k1;
+  uint32_t lds;
+  bool rowwise;         // blocks under 32 keys
+};
+
+__device__ __forceinline__ F8Tile r128f8_tile(const DecodeArgs& a, const int* bt_lds, int e0, int ts, int k1,
+                                              uint32_t stage_lds) {
+  F8Tile T;
+  const uint8_t* zero = reinterpret_cast<const uint8_t*>(kZeroTileF8);
+  T.lds = stage_lds;
+  T.ts = ts;
+  T.k1 = k1;
+  T.rowwise = a.bs < R128_TILE;
+  const int rows = k1 - ts < 0 ? 0 : (k1 - ts > R128_TILE ? R128_TILE : k1 - ts);
+  T.rows16 = M16F8_ROW * rows;
+  T.a = T.b = zero;
+  T.split16 = T.rows16;
+  if (!T.rowwise && rows > 0) {
+    const int vb = block_of(a, ts);
+    const int off = ts - vb * a.bs;
+    const int split = a.bs - off;  // rows of the tile in block vb
+    T.split16 = M16F8_ROW * (split < rows ? split : rows);
+    const int blk = __builtin_amdgcn_readfirstlane(bt_lds[vb - e0]);
+    if ((unsigned)blk < (unsigned)a.num_blocks) T.a = a.kv + ((int64_t)blk * a.bs + off) * M16F8_ROW;
+    if (split < rows) {
+      const int blk2 = __builtin_amdgcn_readfirstlane(bt_lds[vb + 1 - e0]);
+      // row r >= split of the tile is row r - split of block vb + 1
+      if ((unsigned)blk2 < (unsigned)a.num_blocks) T.b = a.kv + ((int64_t)blk2 * a.bs - split) * M16F8_ROW;
     }
-    L.p[m] = p;
   }
-  return L;
+  return T;
+}
+
+// Load m of this wave for tile T (nothing for g = wave + 4m >= 18): the
+// two-block path, and the row-by-row one for blocks under 32 keys.
+__device__ __forceinline__ void r128f8_issue(const F8Tile& T, int m, int wave, int lane) {
+  const int g = wave + 4 * m;
+  if (g >= M16F8_LOADS) return;
+  const int b16 = 16 * (64 * g + lane);
+  const uint8_t* src = (b16 < T.split16 ? T.a : T.b) + b16;
+  if (b16 >= T.rows16) src = reinterpret_cast<const uint8_t*>(kZeroTileF8) + b16;
+  dma16(src, T.lds + 1024 * g);
+}
+
+__device__ __forceinline__ void r128f8_issue_rowwise(const DecodeArgs& a, const int* bt_lds, int e0, const F8Tile& T,
+                                                     int m, int wave) {
+  const int g = wave + 4 * m;
+  if (g >= M16F8_LOADS) return;
+  // the lane index afresh: the per-lane row and chunk split would otherwise
+  // be hoisted out of the tile loop and spilled
+  const int P = 64 * g + lane_id_fresh();
+  const int r = P / (M16F8_ROW / 16), ch = P - (M16F8_ROW / 16) * r;
+  const int t = T.ts + r;
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(kZeroTileF8) + 16 * P;
+  if (t < T.k1) {
+    const int vb = block_of(a, t);
+    const int blk = bt_lds[vb - e0];
+    if ((unsigned)blk < (unsigned)a.num_blocks)
+      src = a.kv + ((int64_t)blk * a.bs + (t - vb * a.bs)) * M16F8_ROW + 16 * ch;
+  }
+  dma16(src, T.lds + 1024 * g);
+}
+
+// The landed E4M3 tile (32 rows of 576 bytes, row-major) widened into a
+// bf16 tile in the ring's swizzled layout, once per workgroup: lane l of wave
+// w converts row 8w + l/8, bytes 72 (l%8) .. +71, nine 8-byte groups that
+// each become one 16-byte bf16 chunk (logical chunk c at physical chunk
+// (c & ~7) | ((c ^ f(r)) & 7)).  E4M3 values are exact in bf16, and the
+// zero row stays zero.
+__device__ __forceinline__ void r128f8_widen(const uint8_t* src, uint8_t* dst, int wave, int lane) {
+  const int r = 8 * wave + (lane >> 3), c0 = 9 * (lane & 7);
+  const int fr = ring_swz(r);
+  const uint8_t* sp = src + r * M16F8_ROW + 8 * c0;
+  uint8_t* dp = dst + r * R128_ROWB;
+#pragma unroll
+  for (int m = 0; m < 9; ++m) {
+    const uint2 x = *reinterpret_cast<const uint2*>(sp + 8 * m);
+    const int c = c0 + m;
+    *reinterpret_cast<bf16x8*>(dp + 16 * ((c & ~7) | ((c ^ fr) & 7))) = f8x8_to_bf16(x.x, x.y);
+  }
 }
 
 // Per-lane LDS byte offsets inside a stage, fixed for the whole kernel (the
@@ -1030,19 +1096,15 @@ struct R128State {
   float m_ref, l_part, l_out;
 };
 
-// One 32-key tile; the nine ring loads of a later tile (nxt) are issued one
-// every four score MFMAs.
-// FP8 cache (F8): the stage holds E4M3 rows with rotated chunks; score and
-// value fragments are 8-byte reads (value ones transposed) widened to bf16
-// in registers, and the ring loads of a later tile (five or four per wave)
-// are issued one every eight score MFMAs.
-template <bool F8, int NRB, class Issue>
-__device__ __forceinline__ void r128_compute(R128State<NRB>& st, const bf16x8 (&qf)[r128_qreg<F8>],
+// One 32-key tile of bf16 rows in the ring's swizzled layout; the ring
+// loads of a later tile are issued one every four score MFMAs (issue(m),
+// m = 0..8).
+template <int NRB, class Issue>
+__device__ __forceinline__ void r128_compute(R128State<NRB>& st, const bf16x8 (&qf)[R128_QREG],
                                              const uint8_t* q_tail, const uint8_t* stage, uint8_t* p_lds,
                                              float* alpha_lds, float scale_log2, int ts, int k1, int nrow, int kfull,
                                              int lane, int wave, Issue&& issue, const R128LaneOff& lo,
                                              uint8_t* xchg) {
-  constexpr int R128_QREG = r128_qreg<F8>;
   const int r = lane & 31, h = lane >> 5;
   if constexpr (NRB < 4) {
     // 32- and 64-row tiles: the score MFMAs of row block rb are split across
@@ -1053,19 +1115,9 @@ __device__ __forceinline__ void r128_compute(R128State<NRB>& st, const bf16x8 (&
     constexpr int DS = 4 / NRB, KS = 36 / DS;
     const int slice = wave / NRB;
     f32x16 sc = {};
-    const uint8_t* kp8 = stage + M16F8_ROW * r + 8 * h;
-    const int krot = f8_rot(r);
-    const int kb0 = slice * KS;
     bf16x8 kf[4];
     auto k_at = [&](int j) __attribute__((always_inline)) {
-      if constexpr (F8) {
-        const int kk = kb0 + j;
-        const int pos = kk < 32 ? (kk + krot) & 31 : 32 + ((kk + krot) & 3);
-        const uint2 x = *reinterpret_cast<const uint2*>(kp8 + 16 * pos);
-        return f8x8_to_bf16(x.x, x.y);
-      } else {
-        return *reinterpret_cast<const bf16x8*>(stage + lo.k[j & 3] + 128 * (j >> 2));
-      }
+      return *reinterpret_cast<const bf16x8*>(stage + lo.k[j & 3] + 128 * (j >> 2));
     };
 #pragma unroll
     for (int j = 0; j < 3; ++j) kf[j] = k_at(j);
@@ -1073,7 +1125,7 @@ __device__ __forceinline__ void r128_compute(R128State<NRB>& st, const bf16x8 (&
     for (int j = 0; j < KS; ++j) {
       if (j + 3 < KS) kf[(j + 3) % 4] = k_at(j + 3);
       // the wave's ring loads of a later tile, spread over its MFMAs
-      constexpr int NL = F8 ? 5 : RING_DMA_PER_WAVE;
+      constexpr int NL = RING_DMA_PER_WAVE;
 #pragma unroll
       for (int m = 0; m < NL; ++m)
         if ((m * KS) / NL == j) issue(m);
@@ -1127,44 +1179,26 @@ __device__ __forceinline__ void r128_compute(R128State<NRB>& st, const bf16x8 (&
   const uint8_t* kp[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) kp[b] = stage + lo.k[b];
-  // FP8: k-step kk (dims 16kk .. +15) is chunk kk of key row r, half h
-  const uint8_t* kp8 = stage + M16F8_ROW * r + 8 * h;
-  const int krot = f8_rot(r);
-  auto k8_at = [&](int kk) __attribute__((always_inline)) {
-    const int pos = kk < 32 ? (kk + krot) & 31 : 32 + ((kk + krot) & 3);
-    return *reinterpret_cast<const uint2*>(kp8 + 16 * pos);
-  };
   // K fragments (and the last k-steps of Q^T, from this wave's LDS copy laid
   // out [kk][lane]) are read three k-steps ahead of their MFMA
   bf16x8 kf[4], qt[4];
-  uint2 k8[4];
   auto q_at = [&](int kk) __attribute__((always_inline)) {
     return *reinterpret_cast<const bf16x8*>(q_tail + ((kk - R128_QREG) * 64 + lane) * 16);
   };
 #pragma unroll
   for (int kk = 0; kk < 3; ++kk) {
-    if constexpr (F8)
-      k8[kk] = k8_at(kk);
-    else
-      kf[kk] = *reinterpret_cast<const bf16x8*>(kp[kk & 3] + 128 * (kk >> 2));
+    kf[kk] = *reinterpret_cast<const bf16x8*>(kp[kk & 3] + 128 * (kk >> 2));
     if (kk >= R128_QREG) qt[kk % 4] = q_at(kk);
   }
 #pragma unroll
   for (int kk = 0; kk < 36; ++kk) {
     if (kk + 3 < 36) {
-      if constexpr (F8)
-        k8[(kk + 3) % 4] = k8_at(kk + 3);
-      else
-        kf[(kk + 3) % 4] = *reinterpret_cast<const bf16x8*>(kp[(kk + 3) & 3] + 128 * ((kk + 3) >> 2));
+      kf[(kk + 3) % 4] = *reinterpret_cast<const bf16x8*>(kp[(kk + 3) & 3] + 128 * ((kk + 3) >> 2));
       if (kk + 3 >= R128_QREG) qt[(kk + 3) % 4] = q_at(kk + 3);
     }
-    if constexpr (F8) {
-      if ((kk & 7) == 0) issue(kk >> 3);
-    } else {
-      if ((kk & 3) == 0) issue(kk >> 2);
-    }
+    if ((kk & 3) == 0) issue(kk >> 2);
     const bf16x8 qv = kk < R128_QREG ? qf[kk < R128_QREG ? kk : 0] : qt[kk % 4];
-    const bf16x8 kv = F8 ? f8x8_to_bf16(k8[kk % 4].x, k8[kk % 4].y) : kf[kk % 4];
+    const bf16x8 kv = kf[kk % 4];
     sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qv, sc, 0, 0, 0);
     // keep each step's reads three steps ahead of their MFMA (the scheduler
     // would otherwise sink them next to their use)
@@ -1244,9 +1278,9 @@ __device__ __forceinline__ void r128_compute(R128State<NRB>& st, const bf16x8 (&
         v[ks][d][rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_i16x4*)(vp[rd][d & 1] + 16 * ks * R128_ROWB + 128 * (d >> 1)));
   };
-  // bf16: the first k-step's operands are read before the rescale check,
-  // so their LDS latency overlaps it
-  if constexpr (!F8) pv_operands(0);
+  // the first k-step's operands are read before the rescale check, so their
+  // LDS latency overlaps it
+  pv_operands(0);
   // ---- this wave's value columns for all 128 rows.  The accumulator
   // column of lane l is row 32rb + l%32 in block rb: rescale the blocks whose
   // rows moved their reference (rare)
@@ -1270,34 +1304,6 @@ __device__ __forceinline__ void r128_compute(R128State<NRB>& st, const bf16x8 (&
           asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
                        : "+a"(st.o[NRB * d + rb][i]), "=&v"(tmp) : "v"(ab[rb]));
         }
-  }
-  if constexpr (F8) {
-    // an 8-bit transposed read per (ks, d): in 16-lane group q = lane/16,
-    // lanes 2e and 2e+1 address the halves of key 16ks + 8h + e, value chunk
-    // 2D + q%2 (D = 4w + d), and lane i16 receives value column
-    // 32D + 16(q%2) + i16 of the 8 keys: the A operand of the PV MFMA
-    const int i16 = lane & 15, qg = lane >> 4;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 bp[NRB];
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) bp[rb] = *reinterpret_cast<const bf16x8*>(pb + 32 * rb * R128_PROW + 32 * ks);
-      const int key = 16 * ks + 8 * h + (i16 >> 1);
-      const uint8_t* vrow = stage + M16F8_ROW * key + 8 * (i16 & 1);
-      const int vc = f8_rot(key) + 8 * wave + (qg & 1);
-      i32x2 v[4];
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-        v[d] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vrow + 16 * ((vc + 2 * d) & 31)));
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const bf16x8 av = f8x8_to_bf16((uint32_t)v[d].x, (uint32_t)v[d].y);
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-          st.o[NRB * d + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bp[rb], st.o[NRB * d + rb], 0, 0, 0);
-      }
-    }
-    return;
   }
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
@@ -1386,11 +1392,12 @@ __device__ __forceinline__ void r128_store_slot(const DecodeArgs& a, const R128S
 template <bool F8, int NRB>
 __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a) {
   constexpr int ROWS = 32 * NRB;
-  // FP8 cache: stages of 18 KiB (32 rows of 576 E4M3 bytes)
+  // FP8 cache: stages of 18 KiB (32 rows of 576 E4M3 bytes), each landed
+  // tile widened once into the bf16 tile `wide` that the compute reads
   constexpr int STAGE = F8 ? M16F8_RAW : R128_STAGE;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[R128_NS * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t wide[F8 ? R128_STAGE : 16];
   __shared__ int bt_lds[R128_BT_WIN];
-  constexpr int R128_QREG = r128_qreg<F8>, R128_QLDS = r128_qlds<F8>;
   // the 128-row tile keeps Q^T's last k-steps here; smaller tiles exchange
   // partial scores between the waves of a row block here instead
   __shared__ __attribute__((aligned(16)))
@@ -1519,9 +1526,14 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         if constexpr (F8) {
-          const F8Loads L = r128f8_loads(a, bt_lds, e0, ka + p * R128_TILE, kb, ring_lds + p * STAGE, wave, lane);
+          const F8Tile T = r128f8_tile(a, bt_lds, e0, ka + p * R128_TILE, kb, ring_lds + p * STAGE);
 #pragma unroll
-          for (int m = 0; m < 5; ++m) m16f8_issue(L, m, wave);
+          for (int m = 0; m < 5; ++m) {
+            if (T.rowwise)
+              r128f8_issue_rowwise(a, bt_lds, e0, T, m, wave);
+            else
+              r128f8_issue(T, m, wave, lane);
+          }
         } else {
           const RingRows rr = r128_tile_rows(a, bt_lds, e0, ka + p * R128_TILE, kb, ring_lds + p * STAGE, wave, lane);
           ring_issue_all(rr, wave, dma_sel_off);
@@ -1531,11 +1543,6 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
       // from it % 3 (which costs every LDS address extra instructions)
       uint32_t cur = 0, nxt_off = 2 * STAGE;
       for (int it = 0; it < nt; ++it) {
-        // FP8: the source addresses of tile it+2's loads need only the block
-        // table window, so they are resolved while the wait below runs
-        F8Loads nxt8;
-        if constexpr (F8)
-          nxt8 = r128f8_loads(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb, ring_lds + nxt_off, wave, lane);
         // tile it landed (only tile it+1 may still be in flight), then
         // every wave is also done with tile it-1 (its stage and the P tile) ...
         if constexpr (F8) {
@@ -1549,17 +1556,31 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
         __syncthreads();
         // ... so its stage can take tile it+2, loaded while tile it is computed
         if constexpr (F8) {
-          r128_compute<true, NRB>(st, qf, q_tail, ring + cur, p_lds, alpha_lds, a.scale_log2, ka + it * R128_TILE, kb,
-                             nrow, min(kb, nmin), lane, wave,
-                             [&](int m) __attribute__((always_inline)) { m16f8_issue(nxt8, m, wave); }, lane_off,
-                                  q_tail_lds);
+          // tile it widened into the bf16 tile (every wave is past its reads
+          // of tile it-1 there), then computed from it; tile it's E4M3 stage
+          // is free for tile it+2 from here on
+          r128f8_widen(ring + cur, wide, wave, lane);
+          __syncthreads();
+          // tile it+2's loads: spread over the score MFMAs, or (blocks under
+          // 32 keys, a row lookup per lane) issued together here
+          const F8Tile nxt8 = r128f8_tile(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb, ring_lds + nxt_off);
+          if (nxt8.rowwise) {
+#pragma unroll
+            for (int m = 0; m < 5; ++m) r128f8_issue_rowwise(a, bt_lds, e0, nxt8, m, wave);
+          }
+          r128_compute<NRB>(st, qf, q_tail, wide, p_lds, alpha_lds, a.scale_log2, ka + it * R128_TILE, kb, nrow,
+                            min(kb, nmin), lane, wave,
+                            [&](int m) __attribute__((always_inline)) {
+                              if (m < 5 && !nxt8.rowwise) r128f8_issue(nxt8, m, wave, lane);
+                            },
+                            lane_off, q_tail_lds);
         } else {
           const RingRows nxt = r128_tile_rows(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb, ring_lds + nxt_off, wave,
                                               lane);
-          r128_compute<false, NRB>(st, qf, q_tail, ring + cur, p_lds, alpha_lds, a.scale_log2, ka + it * R128_TILE, kb,
-                              nrow, min(kb, nmin), lane, wave,
-                              [&](int m) __attribute__((always_inline)) { ring_issue_one(nxt, m, wave, dma_sel_off); },
-                              lane_off, q_tail_lds);
+          r128_compute<NRB>(st, qf, q_tail, ring + cur, p_lds, alpha_lds, a.scale_log2, ka + it * R128_TILE, kb, nrow,
+                            min(kb, nmin), lane, wave,
+                            [&](int m) __attribute__((always_inline)) { ring_issue_one(nxt, m, wave, dma_sel_off); },
+                            lane_off, q_tail_lds);
         }
         nxt_off = cur;
         cur = __builtin_amdgcn_readfirstlane(cur == (R128_NS - 1) * STAGE ? 0u : cur + STAGE);

@@ -45,6 +45,9 @@ CASES = [
     spec("fp8_bs80_h16_q1", 3, 16, 1, True, [79, 800, 2500], global_is_null=True, bs=80),
     spec("fp8_rows24_h24_q1", 2, 24, 1, True, [40, 3000], global_is_null=True),
     spec("fp8_rows48_h16_q3_dcp2", 2, 16, 3, True, [500, 3000], W=2),
+    # blocks under 32 keys in the 128- and 64-row tiles (a row lookup per lane)
+    spec("fp8_bs1_h128_q4", 2, 128, 4, True, [17, 300], global_is_null=True, bs=1),
+    spec("fp8_bs16_h32_q2_dcp2", 2, 32, 2, True, [40, 900], W=2, bs=16),
 ]
 
 
