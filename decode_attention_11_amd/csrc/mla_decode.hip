@@ -1030,23 +1030,25 @@ __device__ __forceinline__ void r128f8_issue_rowwise(const DecodeArgs& a, const 
   dma16(src, T.lds + 1024 * g);
 }
 
-// The landed E4M3 tile (32 rows of 576 bytes, row-major) widened into a
-// bf16 tile in the ring's swizzled layout, once per workgroup: lane l of wave
-// w converts row 8w + l/8, bytes 72 (l%8) .. +71, nine 8-byte groups that
-// each become one 16-byte bf16 chunk (logical chunk c at physical chunk
-// (c & ~7) | ((c ^ f(r)) & 7)).  E4M3 values are exact in bf16, and the
-// zero row stays zero.
-__device__ __forceinline__ void r128f8_widen(const uint8_t* src, uint8_t* dst, int wave, int lane) {
-  const int r = 8 * wave + (lane >> 3), c0 = 9 * (lane & 7);
+// A landed E4M3 tile (32 rows of 576 bytes, row-major) widened into a bf16
+// tile in the ring's swizzled layout, once per workgroup: lane l of wave w
+// converts row 8w + l/8, bytes 72 (l%8) .. +71, nine 8-byte groups (item i:
+// bytes 72 (l%8) + 8i) that each become one 16-byte bf16 chunk (logical
+// chunk c at physical chunk (c & ~7) | ((c ^ f(r)) & 7)).  E4M3 values are
+// exact in bf16, and zero rows stay zero.  The read and the write of an item
+// are separate steps so that they can be spread over other work.
+__device__ __forceinline__ uint2 r128f8_widen_read(const uint8_t* src, int wave, int lane, int i) {
+  const int r = 8 * wave + (lane >> 3), c = 9 * (lane & 7) + i;
+  return *reinterpret_cast<const uint2*>(src + r * M16F8_ROW + 8 * c);
+}
+__device__ __forceinline__ void r128f8_widen_write(uint8_t* dst, int wave, int lane, int i, uint2 x) {
+  const int r = 8 * wave + (lane >> 3), c = 9 * (lane & 7) + i;
   const int fr = ring_swz(r);
-  const uint8_t* sp = src + r * M16F8_ROW + 8 * c0;
-  uint8_t* dp = dst + r * R128_ROWB;
+  *reinterpret_cast<bf16x8*>(dst + r * R128_ROWB + 16 * ((c & ~7) | ((c ^ fr) & 7))) = f8x8_to_bf16(x.x, x.y);
+}
+__device__ __forceinline__ void r128f8_widen(const uint8_t* src, uint8_t* dst, int wave, int lane) {
 #pragma unroll
-  for (int m = 0; m < 9; ++m) {
-    const uint2 x = *reinterpret_cast<const uint2*>(sp + 8 * m);
-    const int c = c0 + m;
-    *reinterpret_cast<bf16x8*>(dp + 16 * ((c & ~7) | ((c ^ fr) & 7))) = f8x8_to_bf16(x.x, x.y);
-  }
+  for (int i = 0; i < 9; ++i) r128f8_widen_write(dst, wave, lane, i, r128f8_widen_read(src, wave, lane, i));
 }
 
 // Per-lane LDS byte offsets inside a stage, fixed for the whole kernel (the
@@ -1098,13 +1100,14 @@ struct R128State {
 
 // One 32-key tile of bf16 rows in the ring's swizzled layout; the ring
 // loads of a later tile are issued one every four score MFMAs (issue(m),
-// m = 0..8).
-template <int NRB, class Issue>
+// m = 0..8), and side(step, steps) runs once before each of the wave's
+// `steps` score MFMAs (the FP8 instance widens the next tile there).
+template <int NRB, class Issue, class Side>
 __device__ __forceinline__ void r128_compute(R128State<NRB>& st, const bf16x8 (&qf)[R128_QREG],
                                              const uint8_t* q_tail, const uint8_t* stage, uint8_t* p_lds,
                                              float* alpha_lds, float scale_log2, int ts, int k1, int nrow, int kfull,
                                              int lane, int wave, Issue&& issue, const R128LaneOff& lo,
-                                             uint8_t* xchg) {
+                                             uint8_t* xchg, Side&& side) {
   const int r = lane & 31, h = lane >> 5;
   if constexpr (NRB < 4) {
     // 32- and 64-row tiles: the score MFMAs of row block rb are split across
@@ -1129,6 +1132,7 @@ __device__ __forceinline__ void r128_compute(R128State<NRB>& st, const bf16x8 (&
 #pragma unroll
       for (int m = 0; m < NL; ++m)
         if ((m * KS) / NL == j) issue(m);
+      side(j, KS);
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % 4], qf[j], sc, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1197,6 +1201,7 @@ __device__ __forceinline__ void r128_compute(R128State<NRB>& st, const bf16x8 (&
       if (kk + 3 >= R128_QREG) qt[(kk + 3) % 4] = q_at(kk + 3);
     }
     if ((kk & 3) == 0) issue(kk >> 2);
+    side(kk, 36);
     const bf16x8 qv = kk < R128_QREG ? qf[kk < R128_QREG ? kk : 0] : qt[kk % 4];
     const bf16x8 kv = kf[kk % 4];
     sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qv, sc, 0, 0, 0);
@@ -1392,11 +1397,13 @@ __device__ __forceinline__ void r128_store_slot(const DecodeArgs& a, const R128S
 template <bool F8, int NRB>
 __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a) {
   constexpr int ROWS = 32 * NRB;
-  // FP8 cache: stages of 18 KiB (32 rows of 576 E4M3 bytes), each landed
-  // tile widened once into the bf16 tile `wide` that the compute reads
+  // FP8 cache: two stages of 18 KiB (32 rows of 576 E4M3 bytes) and two
+  // bf16 tiles `wide` (as much LDS as the bf16 ring): while tile it is
+  // computed from one bf16 tile, tile it+1 is widened into the other and
+  // tile it+2 loads into the E4M3 stage tile it came from
   constexpr int STAGE = F8 ? M16F8_RAW : R128_STAGE;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[R128_NS * STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t wide[F8 ? R128_STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[(F8 ? 2 : R128_NS) * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t wide[F8 ? 2 * R128_STAGE : 16];
   __shared__ int bt_lds[R128_BT_WIN];
   // the 128-row tile keeps Q^T's last k-steps here; smaller tiles exchange
   // partial scores between the waves of a row block here instead
@@ -1522,11 +1529,11 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
       for (int e = e0 + tid; e <= e1; e += R128_THREADS) bt_lds[e - e0] = e < a.max_blocks ? gload_i32(btr + e) : -1;
       __syncthreads();
       const int nt = (kb - ka + R128_TILE - 1) / R128_TILE;
-      // prologue: tiles 0 and 1
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        if constexpr (F8) {
-          const F8Tile T = r128f8_tile(a, bt_lds, e0, ka + p * R128_TILE, kb, ring_lds + p * STAGE);
+      if constexpr (F8) {
+        // E4M3 tile t lands in stage t%2 and is widened into bf16 tile t%2
+        // while tile t-1 is computed.  Loads go out spread over the score
+        // MFMAs, or (blocks under 32 keys, a row lookup per lane) together.
+        auto issue_tile = [&](const F8Tile& T) __attribute__((always_inline)) {
 #pragma unroll
           for (int m = 0; m < 5; ++m) {
             if (T.rowwise)
@@ -1534,56 +1541,71 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
             else
               r128f8_issue(T, m, wave, lane);
           }
-        } else {
+        };
+        issue_tile(r128f8_tile(a, bt_lds, e0, ka, kb, ring_lds));
+        issue_tile(r128f8_tile(a, bt_lds, e0, ka + R128_TILE, kb, ring_lds + STAGE));
+        if (wave < 2)
+          WAIT_VMCNT(5);  // tile 0 landed; tile 1's five loads may stay in flight
+        else
+          WAIT_VMCNT(4);
+        __syncthreads();
+        r128f8_widen(ring, wide, wave, lane);
+        for (int it = 0; it < nt; ++it) {
+          const uint32_t par = it & 1;
+          // tile it+1 landed (its loads were the only ones in flight), and
+          // every wave is done with bf16 tile it-1 and with E4M3 tile it ...
+          WAIT_VMCNT(0);
+          __syncthreads();
+          // ... so bf16 tile it is whole, tile it+1 can be widened into
+          // bf16 tile it-1's place and tile it+2 loaded into E4M3 tile it's
+          const F8Tile nxt8 = r128f8_tile(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb, ring_lds + par * STAGE);
+          if (nxt8.rowwise) issue_tile(nxt8);
+          const uint8_t* s_nxt = ring + (par ^ 1) * STAGE;
+          uint8_t* w_nxt = wide + (par ^ 1) * R128_STAGE;
+          uint2 pend = {0u, 0u};
+          r128_compute<NRB>(
+              st, qf, q_tail, wide + par * R128_STAGE, p_lds, alpha_lds, a.scale_log2, ka + it * R128_TILE, kb, nrow,
+              min(kb, nmin), lane, wave,
+              [&](int m) __attribute__((always_inline)) {
+                if (m < 5 && !nxt8.rowwise) r128f8_issue(nxt8, m, wave, lane);
+              },
+              lane_off, q_tail_lds,
+              // item i read at step i*steps/9 and written steps/18 steps later
+              [&](int step, int steps) __attribute__((always_inline)) {
+#pragma unroll
+                for (int i = 0; i < 9; ++i) {
+                  const int rs = (i * steps) / 9, ws = rs + (steps >= 18 ? steps / 18 : 0);
+                  if (step == rs) pend = r128f8_widen_read(s_nxt, wave, lane, i);
+                  if (step == ws) r128f8_widen_write(w_nxt, wave, lane, i, pend);
+                }
+              });
+        }
+      } else {
+        // prologue: tiles 0 and 1
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
           const RingRows rr = r128_tile_rows(a, bt_lds, e0, ka + p * R128_TILE, kb, ring_lds + p * STAGE, wave, lane);
           ring_issue_all(rr, wave, dma_sel_off);
         }
-      }
-      // stage offsets of tiles it and it+2, rotated instead of computed
-      // from it % 3 (which costs every LDS address extra instructions)
-      uint32_t cur = 0, nxt_off = 2 * STAGE;
-      for (int it = 0; it < nt; ++it) {
-        // tile it landed (only tile it+1 may still be in flight), then
-        // every wave is also done with tile it-1 (its stage and the P tile) ...
-        if constexpr (F8) {
-          if (wave < 2)
-            WAIT_VMCNT(5);  // tile it+1's five loads may stay in flight
-          else
-            WAIT_VMCNT(4);
-        } else {
-          WAIT_VMCNT(R128_DMA_PER_WAVE);  // tile it+1's 9 loads may stay in flight
-        }
-        __syncthreads();
-        // ... so its stage can take tile it+2, loaded while tile it is computed
-        if constexpr (F8) {
-          // tile it widened into the bf16 tile (every wave is past its reads
-          // of tile it-1 there), then computed from it; tile it's E4M3 stage
-          // is free for tile it+2 from here on
-          r128f8_widen(ring + cur, wide, wave, lane);
+        // stage offsets of tiles it and it+2, rotated instead of computed
+        // from it % 3 (which costs every LDS address extra instructions)
+        uint32_t cur = 0, nxt_off = 2 * STAGE;
+        for (int it = 0; it < nt; ++it) {
+          // tile it landed (only tile it+1's 9 loads may still be in flight),
+          // then every wave is also done with tile it-1 (its stage and the P
+          // tile), so its stage can take tile it+2, loaded while tile it is
+          // computed
+          WAIT_VMCNT(R128_DMA_PER_WAVE);
           __syncthreads();
-          // tile it+2's loads: spread over the score MFMAs, or (blocks under
-          // 32 keys, a row lookup per lane) issued together here
-          const F8Tile nxt8 = r128f8_tile(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb, ring_lds + nxt_off);
-          if (nxt8.rowwise) {
-#pragma unroll
-            for (int m = 0; m < 5; ++m) r128f8_issue_rowwise(a, bt_lds, e0, nxt8, m, wave);
-          }
-          r128_compute<NRB>(st, qf, q_tail, wide, p_lds, alpha_lds, a.scale_log2, ka + it * R128_TILE, kb, nrow,
-                            min(kb, nmin), lane, wave,
-                            [&](int m) __attribute__((always_inline)) {
-                              if (m < 5 && !nxt8.rowwise) r128f8_issue(nxt8, m, wave, lane);
-                            },
-                            lane_off, q_tail_lds);
-        } else {
           const RingRows nxt = r128_tile_rows(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb, ring_lds + nxt_off, wave,
                                               lane);
           r128_compute<NRB>(st, qf, q_tail, ring + cur, p_lds, alpha_lds, a.scale_log2, ka + it * R128_TILE, kb, nrow,
                             min(kb, nmin), lane, wave,
                             [&](int m) __attribute__((always_inline)) { ring_issue_one(nxt, m, wave, dma_sel_off); },
-                            lane_off, q_tail_lds);
+                            lane_off, q_tail_lds, [](int, int) {});
+          nxt_off = cur;
+          cur = __builtin_amdgcn_readfirstlane(cur == (R128_NS - 1) * STAGE ? 0u : cur + STAGE);
         }
-        nxt_off = cur;
-        cur = __builtin_amdgcn_readfirstlane(cur == (R128_NS - 1) * STAGE ? 0u : cur + STAGE);
       }
       WAIT_VMCNT(0);
     }
