@@ -128,16 +128,31 @@ __device__ __forceinline__ int64_t shfl_i64(int64_t v, int src) {
   return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
-// Index of the balanced work range that holds unit u when T units are cut
-// into G ranges [floor(w*T/G), floor((w+1)*T/G)).
-__device__ __forceinline__ int range_owner(int64_t u, int64_t T, int G) {
-  return (int)floordiv((u + 1) * (int64_t)G - 1, T);
+// Work ranges: T units are cut into G ranges, the first G/2 of weight wa
+// and the rest of weight wb (wa = wb: equal ranges).  Range w starts at
+// floor(T * W(w) / Wt), with W(w) = wa min(w, G/2) + wb max(w - G/2, 0) and
+// Wt = W(G).  All in 64-bit integers: T * Wt stays far below 2^63.
+__device__ __forceinline__ int64_t range_weight(int64_t w, int G, int wa, int wb) {
+  const int64_t h = G / 2;
+  return w <= h ? wa * w : wa * h + wb * (w - h);
+}
+__device__ __forceinline__ int64_t range_start(int64_t w, int64_t T, int G, int wa, int wb) {
+  return floordiv(T * range_weight(w, G, wa, wb), range_weight(G, G, wa, wb));
+}
+
+// The range that holds unit u (0 <= u < T): the largest w whose start is at
+// most u.  start(w) <= u  <=>  T W(w) <= (u + 1) Wt - 1  <=>  W(w) <= Wmax.
+__device__ __forceinline__ int range_owner(int64_t u, int64_t T, int G, int wa, int wb) {
+  const int64_t wmax = floordiv((u + 1) * range_weight(G, G, wa, wb) - 1, T);
+  const int64_t h = G / 2;
+  const int64_t w = wmax <= wa * h ? wmax / wa : h + (wmax - wa * h) / wb;
+  return (int)(w < G - 1 ? w : G - 1);
 }
 
 // Whether range w holds any unit: with fewer units than ranges some are empty
 // (and can lie between the owners of two units).
-__device__ __forceinline__ bool range_nonempty(int w, int64_t T, int G) {
-  return floordiv((int64_t)w * T, G) < floordiv((int64_t)(w + 1) * T, G);
+__device__ __forceinline__ bool range_nonempty(int w, int64_t T, int G, int wa, int wb) {
+  return range_start(w, T, G, wa, wb) < range_start(w + 1, T, G, wa, wb);
 }
 
 // Launch a kernel that takes one argument struct and return the runtime's
