@@ -1,7 +1,7 @@
 """The float64 oracle over every element of a full-size workload, in a pool
 of worker processes (test infrastructure for the full-size GPU parity tests).
 
-python -m tests.oracle_full --config N --out DIR [--workers K] [--unsharded]
+python -m tests.oracle_full --config N --out DIR [--workers K] [--unsharded] [--fp8]
 
 Runs in a process of its own that never touches the GPU: it builds the
 workload from its seed (the same inputs the test uploads), forks single-
@@ -10,7 +10,8 @@ the workload DIR/out_r{r}.npy [B*Q, H, 512] and DIR/lse_r{r}.npy [B*Q, H]
 (float64, the oracle's own precision).  With --unsharded it also writes
 DIR/out_u.npy and DIR/lse_u.npy: the attention of every row over its whole
 global causal prefix (W = 1 over the contiguous global KV), which the
-LSE-merged shards must equal.
+LSE-merged shards must equal.  With --fp8 the workload's cache holds E4M3
+codes with the scale FP8_KV_SCALE, as bench.py --fp8 builds it.
 """
 from __future__ import annotations
 
@@ -22,6 +23,12 @@ import time
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 _JOB = {}
+FP8_KV_SCALE = 1.0 / 64  # codes of N(0,1) values / this scale, as in bench.py --fp8
+
+
+def spec_of(config, fp8=False):
+    import workloads as WL
+    return WL.config(config, kv_dtype="fp8", kv_scale=FP8_KV_SCALE) if fp8 else WL.config(config)
 
 
 def _item(it):
@@ -71,7 +78,7 @@ def default_workers():
     return max(1, min(16, n))
 
 
-def start(config, out_dir, unsharded=False):
+def start(config, out_dir, unsharded=False, fp8=False):
     """Start the oracle for workload `config` in a child process (single-
     threaded BLAS in every worker); returns the Popen."""
     import subprocess
@@ -83,6 +90,8 @@ def start(config, out_dir, unsharded=False):
            "--workers", str(default_workers())]
     if unsharded:
         cmd.append("--unsharded")
+    if fp8:
+        cmd.append("--fp8")
     return subprocess.Popen(cmd, cwd=ROOT, env=env)
 
 
@@ -98,11 +107,11 @@ def main():
     ap.add_argument("--out", required=True)
     ap.add_argument("--workers", type=int, default=0)
     ap.add_argument("--unsharded", action="store_true")
+    ap.add_argument("--fp8", action="store_true")
     args = ap.parse_args()
     sys.path.insert(0, ROOT)
-    import workloads as WL
     t0 = time.perf_counter()
-    run(WL.config(args.config), args.out, args.workers or default_workers(), args.unsharded)
+    run(spec_of(args.config, args.fp8), args.out, args.workers or default_workers(), args.unsharded)
     print(f"[oracle_full] workload {args.config}: {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
 
 

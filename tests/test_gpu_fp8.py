@@ -14,6 +14,7 @@ import torch
 import decode_attention_11_amd as mla
 import oracle
 import workloads as WL
+from tests import oracle_full
 from tests.gpu_util import Uploaded, compare, say, bf16_dev, u8_dev, i32_dev
 
 pytestmark = pytest.mark.gpu
@@ -160,34 +161,32 @@ def test_fp8_cache_scale_scales_scores_and_values():
     assert not torch.equal(l1, l2)
 
 
-def test_fp8_full_size_decode_on_sampled_rows():
-    sp = WL.config(2, kv_dtype="fp8", kv_scale=1.0 / 64)
-    say(f"{sp.name} fp8: generating")
-    wl = WL.build(sp)
-    up = Uploaded(wl)
-    out, lse = up.run(0, max_seq_len=int(wl.seq_lens[0].max()))
-    torch.cuda.synchronize()
-    o = out.float()
-    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
-    rng = np.random.default_rng(2002)
-    rows = sorted({(int(rng.integers(sp.B)), 0, int(rng.integers(sp.H))) for _ in range(24)}
-                  | {(int(np.argmax(wl.tot)), 0, sp.H - 1), (int(np.argmin(wl.tot)), 0, 0)})
-    ro, rl = oracle.mla_decode(wl.q_bits, wl.global_rows, wl.seq_lens[0], None, 1, 0, True, sp.scale, "e",
-                               rows=rows, kv_scale=sp.kv_scale)
-    compare(out, lse, ro, rl, f"{sp.name} fp8", rows=[(b, h) for (b, _, h) in rows])
-
-
-def test_fp8_full_size_spec_decode_on_sampled_rows():
-    sp = WL.config(3, kv_dtype="fp8", kv_scale=1.0 / 64)
-    say(f"{sp.name} fp8: generating")
-    wl = WL.build(sp)
-    up = Uploaded(wl)
-    out, lse = up.run(0, max_seq_len=int(wl.seq_lens[0].max()))
-    torch.cuda.synchronize()
-    assert bool(torch.isfinite(out.float()).all()) and bool(torch.isfinite(lse).all())
-    rng = np.random.default_rng(3003)
-    rows = sorted({(int(rng.integers(sp.B)), int(rng.integers(sp.Q)), int(rng.integers(sp.H))) for _ in range(20)}
-                  | {(int(np.argmax(wl.tot)), sp.Q - 1, sp.H - 1), (int(np.argmin(wl.tot)), 0, 0)})
-    ro, rl = oracle.mla_decode(wl.q_bits, wl.global_rows, wl.seq_lens[0], None, 1, 0, True, sp.scale, "e",
-                               rows=rows, kv_scale=sp.kv_scale)
-    compare(out, lse, ro, rl, f"{sp.name} fp8", rows=[(b * sp.Q + j, h) for (b, j, h) in rows])
+@pytest.mark.parametrize("cfg", [2, 6, 3, 5])
+def test_fp8_full_size_matches_oracle_on_every_element(cfg, tmp_path):
+    """The benchmark's workloads with the FP8 cache of bench.py --fp8, at full
+    size in the launch configuration bench.py times, every (row, head,
+    column) against the float64 oracle on the same E4M3 codes (computed in a
+    GPU-free worker pool while the GPU runs).  The single-token workload
+    uses the weighted ranges of the two workgroups per CU."""
+    sp = oracle_full.spec_of(cfg, fp8=True)
+    say(f"{sp.name} fp8: oracle started in a worker pool; generating")
+    proc = oracle_full.start(cfg, tmp_path, fp8=True)
+    try:
+        wl = WL.build(sp)
+        up = Uploaded(wl)
+        r = min(wl.pools)
+        say(f"{sp.name} fp8 rank {r}: GPU")
+        out, lse = up.run(r, sp.lse_base, max_seq_len=int(wl.seq_lens[r].max()))
+        torch.cuda.synchronize()
+        out, lse = out.cpu(), lse.cpu()
+        del up
+        say(f"{sp.name} fp8: waiting for the oracle")
+        rc = proc.wait(timeout=900)
+        assert rc == 0, f"{sp.name} fp8: the oracle process failed ({rc})"
+    finally:
+        if proc.poll() is None:
+            proc.kill()
+            proc.wait()
+    ro, rl = oracle_full.load(tmp_path, r)
+    assert not np.isnan(ro).any() and not np.isnan(rl).any(), "the oracle left rows uncomputed"
+    compare(out, lse, ro, rl, f"{sp.name} fp8, all {ro.size} outputs")
