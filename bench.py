@@ -449,6 +449,47 @@ class GpuRun:
         return out
 
 
+def graph_steps(torch, hip, stream, run, steps, warmup):
+    """The same steps replayed from HIP graphs (torch.cuda.CUDAGraph), one
+    captured per KV replica, as a serving loop replays its captured decode
+    step (PR #52188 page, risks: the captured step replayed every decode
+    step): ms per step, launch overheads excluded.  Nothing in a step
+    allocates, synchronises with the host or clears memory.  None if the
+    capture fails."""
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(run.replicas):
+                run.step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for i in range(run.replicas):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run.step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(max(warmup, run.replicas)):
+            graphs[i % run.replicas].replay()
+        torch.cuda.synchronize()
+        g_start, g_stop = hip.event(), hip.event()
+        hip.record(g_start, stream)
+        for i in range(steps):
+            graphs[i % run.replicas].replay()
+        hip.record(g_stop, stream)
+        torch.cuda.synchronize()
+        ms = hip.elapsed_ms(g_start, g_stop) / steps
+        hip.destroy(g_start)
+        hip.destroy(g_stop)
+        del graphs
+        return ms
+    except Exception as e:  # reported as null; the eager figures stand
+        log(f"graph replay not measured: {e}")
+        return None
+
+
 def measure(torch, hip, stream, run, n, args):
     """Warm-up, then exactly args.steps timed steps of one workload with the
     attention kernel's own events, then the same steps without those events;
@@ -488,6 +529,7 @@ def measure(torch, hip, stream, run, n, args):
     plain_ms_per_step = hip.elapsed_ms(u_start, u_stop) / args.steps
     hip.destroy(u_start)
     hip.destroy(u_stop)
+    graph_ms_per_step = graph_steps(torch, hip, stream, run, args.steps, args.warmup)
     ms_per_step = total_ms / args.steps
     avg_attn_ms = sum(attn_ms) / len(attn_ms)
     log(f"{s.name}: {ms_per_step:.4f} ms/step (wall {wall / args.steps * 1e3:.4f}), "
@@ -530,6 +572,7 @@ def measure(torch, hip, stream, run, n, args):
         "attention_kernel_ms_min": round(float(min(attn_ms)), 5),
         "attention_launches_per_step": len(ranks),
         "ms_per_step_without_kernel_events": round(plain_ms_per_step, 5),
+        "ms_per_step_graph": None if graph_ms_per_step is None else round(graph_ms_per_step, 5),
         "roofline": roof, "parts": parts,
         "shape": {"batch": s.B, "heads": s.H, "q_len": s.Q if s.q_lens is None else f"1..{s.Q} per request",
                   "causal": s.causal, "cp_world": s.W, "cp_interleave": s.interleave, "ranks": ranks,
@@ -663,6 +706,7 @@ def main():
         "attention_kernel_ms_median": h["attention_kernel_ms_median"],
         "attention_kernel_ms_min": h["attention_kernel_ms_min"],
         "ms_per_step_without_kernel_events": h["ms_per_step_without_kernel_events"],
+        "ms_per_step_graph": h["ms_per_step_graph"],
         "source_hash": source_hash(),
         "roofline": h["roofline"], "cpu_baseline": h["cpu_baseline"],
         "measured_peaks": peaks, "kv_write": kvw, "parts": h["parts"],
