@@ -61,12 +61,14 @@ struct DecodeArgs {
   float out_scale;         // output factor: the FP8 cache scale, 1 for bf16
   int kv_fp8;              // KV rows are 576 E4M3 bytes instead of 576 bf16
   int lse_base;
-  int n_rt;                // row tiles per request
+  int n_rt;                // row tiles per request (1 with per-tile ranges)
+  int vrt;                 // per-tile ranges: row tiles per request, else 0
+  int rows_tile;           // rows per row tile
   int ovh;                 // work units charged per piece on top of its keys
   int nbund;               // balanced key ranges (bundles)
   int wa, wb;              // weights of the first and second half of the ranges
   int G;                   // partial workgroups: nbund * n_rt, one per (bundle, row tile)
-  int64_t* prefix;         // [B+1] unit offsets of the requests
+  int64_t* prefix;         // [B+1] unit offsets of the requests ([B*vrt+1] of the (request, row tile) items)
   float* partials;         // [(nbund + B) * n_rt] slots
   uint16_t* out;           // bf16 [B*R, 512]
   float* lse;              // [B*R] or null
@@ -82,9 +84,15 @@ __device__ __forceinline__ int64_t request_units(const DecodeArgs& a, int nb) {
 
 // Partial slot of bundle j's piece of request bb, row tile rt.  For a fixed
 // row tile, the bundles cover the requests in order, so j + bb never repeats.
+// With per-tile ranges, range j's piece of item v = bb * vrt + rt: the ranges
+// cover the items in order, so j + v never repeats either.
 __device__ __forceinline__ int64_t piece_slot(const DecodeArgs& a, int j, int bb, int rt) {
-  return ((int64_t)j + bb) * a.n_rt + rt;
+  return a.vrt ? (int64_t)j + (int64_t)bb * a.vrt + rt : ((int64_t)j + bb) * a.n_rt + rt;
 }
+
+// Work items the ranges cut: the requests, or with per-tile ranges the
+// (request, row tile) pairs, request by request.
+__device__ __forceinline__ int work_items(const DecodeArgs& a) { return a.vrt ? a.B * a.vrt : a.B; }
 
 // Query tokens of request b and the index of its first one: Q each, or
 // from the token offsets of a varlen batch.
@@ -100,14 +108,20 @@ __device__ __forceinline__ void request_tokens(const DecodeArgs& a, int b, int& 
 
 // Key count of the largest row (the last query row sees the whole global
 // length, whatever the query length), local length and global length of
-// request b; zeros past B and for a request without query tokens.
-__device__ __forceinline__ void request_info(const DecodeArgs& a, int b, int& nb, int& seq, int& tot) {
+// work item v (request v, or with per-tile ranges request v / vrt); zeros
+// past the items, for a request without query tokens and for a row tile
+// past its request's rows.
+__device__ __forceinline__ void request_info(const DecodeArgs& a, int v, int& nb, int& seq, int& tot) {
   nb = seq = tot = 0;
-  if (b < a.B) {
+  const int b = a.vrt ? v / a.vrt : v;
+  if (v < work_items(a)) {
     seq = gload_i32(a.seq_lens + b);
     tot = a.glob ? gload_i32(a.glob + b) : seq;
     nb = row_bound(seq, tot, 1, 0, a.W, a.rank, a.I, a.causal);
-    if (a.qsl && gload_i32(a.qsl + b + 1) == gload_i32(a.qsl + b)) nb = 0;
+    if (a.qsl) {
+      const int ql = gload_i32(a.qsl + b + 1) - gload_i32(a.qsl + b);
+      if (ql == 0 || (a.vrt && (v - b * a.vrt) * a.rows_tile >= ql * a.H)) nb = 0;
+    }
   }
 }
 
@@ -174,7 +188,13 @@ __device__ __forceinline__ void request_piece(const DecodeArgs& a, int bb, int64
   const int k0 = __builtin_amdgcn_readfirstlane((int)(a0 > 0 ? a0 : 0));
   const int k1 = __builtin_amdgcn_readfirstlane((int)(a1 < nbb ? a1 : nbb));
   if (k1 <= k0) return;  // the range holds only the request's overhead units
-  piece(bb, rt, k0, k1, sq, tt);
+  if (a.vrt) {
+    // item bb is row tile bb % vrt of request bb / vrt
+    const int b = bb / a.vrt;
+    piece(b, bb - b * a.vrt, k0, k1, sq, tt);
+  } else {
+    piece(bb, rt, k0, k1, sq, tt);
+  }
 }
 
 // The requests' units are laid end to end and cut into nbund balanced
@@ -211,7 +231,7 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int j, int r
     pl.tot[tid] = tot;
     total0 = uniform_i64(t0);
     T = total0;
-    for (int base = NT; base < a.B; base += NT) {
+    for (int base = NT; base < work_items(a); base += NT) {
       int nb2, seq2, tot2;
       request_info(a, base + tid, nb2, seq2, tot2);
       T += uniform_i64(block_sum_i64<NT>(request_units(a, nb2), pl.red));
@@ -221,7 +241,7 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int j, int r
   const int64_t u1 = uniform_i64(range_start(j + 1, T, a.nbund, a.wa, a.wb));
 
   int64_t carry = 0;
-  for (int base = 0; base < a.B; base += NT) {
+  for (int base = 0; base < work_items(a); base += NT) {
     int64_t chunk_total = total0;
     if (base > 0) {
       int nb, seq, tot;
@@ -238,7 +258,7 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int j, int r
     const int64_t excl = pl.excl[tid];
     const int64_t x = request_units(a, pl.nb[tid]);
     const int64_t incl = excl + x;
-    if (j == 0 && rt == 0 && b < a.B) {
+    if (j == 0 && rt == 0 && b < work_items(a)) {
       a.prefix[b + 1] = incl;
       if (b == 0) a.prefix[0] = 0;
     }
@@ -1417,7 +1437,7 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // 128-row tiles keep a bundle's workgroups on one XCD; smaller tiles
   // (one per request) take ranges in launch order, as the 16-row kernel does
-  const int w = (NRB == 4 || a.n_rt > 1) ? xcd_range_index(blockIdx.x, a.G) : (int)blockIdx.x;
+  const int w = (NRB == 4 || a.n_rt > 1 || a.vrt) ? xcd_range_index(blockIdx.x, a.G) : (int)blockIdx.x;
   const int bund = w / a.n_rt, tile = w - bund * a.n_rt;
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
   int dma_sel_off[RING_DMA_PER_WAVE];  // per-lane constants of this wave's ring loads
@@ -1644,15 +1664,18 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   constexpr int64_t SLOT_BYTES = F16 ? r128_slot_bytes(ROWS) : (ROWS * D_V + 3 * ROWS) * 4;
   constexpr int O_BYTES = F16 ? r128_o_bytes(ROWS) : ROWS * D_V * 4;
   const int grp = blockIdx.x >> 3, slice = blockIdx.x & 7;
-  const int b = grp / a.n_rt, rt = grp - b * a.n_rt;
+  const int rpt = a.vrt ? a.vrt : a.n_rt;  // row tiles per request
+  const int b = grp / rpt, rt = grp - b * rpt;
   const int row = threadIdx.x % ROWS;
   const int col0 = slice * SLICE + (threadIdx.x / ROWS) * PER;
   const int row_idx = rt * ROWS + row;
   int q_len, q_base;
   request_tokens(a, b, q_len, q_base);
   if (row_idx >= q_len * a.H) return;
-  const int64_t T = a.prefix[a.B];
-  const int64_t pb = a.prefix[b], pb1 = a.prefix[b + 1];
+  // the group's units: its request's (bundles), or its own (per-tile ranges)
+  const int64_t T = a.prefix[work_items(a)];
+  const int pi = a.vrt ? grp : b;
+  const int64_t pb = a.prefix[pi], pb1 = a.prefix[pi + 1];
   const int nb = pb1 > pb ? (int)(pb1 - pb - a.ovh) : 0;
   int j0 = 0, j1 = -1;
   if (nb > 0) {
@@ -1663,7 +1686,8 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int64_t orow = (int64_t)q_base * a.H + row_idx;
   uint16_t* op = a.out + orow * D_V + col0;
   static_assert(PER % 4 == 0, "outputs are stored 4 columns at a time");
-  // bundle j's slot of this group is (j + b) * n_rt + rt = j * n_rt + grp; a
+  // bundle j's slot of this group is (j + b) * n_rt + rt = j * n_rt + grp
+  // (per-tile ranges: n_rt = 1 and grp is the item, so j + item); a
   // bundle with an empty range wrote nothing.  The slots are merged NMAX at
   // a time: all loads of a batch are issued before any is used.  With at
   // most NMAX slots this is the plain two-pass merge (weights relative to
@@ -1741,6 +1765,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 struct Plan {
   int rows_tile;
   int n_rt;
+  int vrt;
   int ovh;
   int nbund;
   int wa, wb;  // weights of the first and second half of the ranges
@@ -1767,11 +1792,23 @@ int device_cu_count() {
 
 // Requests of up to 16 rows run the 16-row kernel, larger ones the 128-row
 // kernel (any block size: a power of two takes shifts, others a division).
-Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool fp8 = false) {
+Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool fp8 = false, bool varlen = false) {
   Plan p{};
   const int64_t R = (int64_t)q_len * H;
   p.rows_tile = R <= M16_ROWS ? M16_ROWS : R <= 32 ? 32 : R <= 64 ? 64 : R128_ROWS;
   p.n_rt = (int)((R + p.rows_tile - 1) / p.rows_tile);
+  // Per-tile ranges (a query length per request and several row tiles): the
+  // (request, row tile) pairs of the requests' actual rows are the work
+  // items, laid end to end request by request and cut into one range per
+  // workgroup.  Bundles would leave the row-tile workgroups of a shorter
+  // request's missing rows idle over its keys.  A request's row tiles are
+  // adjacent items, so their ranges mostly fall on one XCD (consecutive
+  // workgroup indices) and still share its L2.
+  p.vrt = 0;
+  if (varlen && p.n_rt > 1 && p.rows_tile != M16_ROWS) {
+    p.vrt = p.n_rt;
+    p.n_rt = 1;
+  }
   // per-group overhead in key units, about what a group's start and end
   // cost in ring time: M16 5 tiles (the query item, a partial tile, the
   // 33 KB partial store and the pipeline refill behind them; 160 units ran
@@ -1793,7 +1830,7 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool fp8 = fal
   const int per_xcd = (p.rows_tile != M16_ROWS ? 1 : fp8 ? M16F8_WG_PER_CU : 1) * cus / 8;  // resident workgroups
   int64_t nbund = p.n_rt == 1 ? 8 * per_xcd : p.n_rt <= per_xcd ? 8 * (per_xcd / p.n_rt) : 8 * per_xcd / p.n_rt;
   if (nbund < 1) nbund = 1;
-  const int64_t units = (int64_t)B * ((max_seq_len > 0 ? max_seq_len : 1) + p.ovh);  // of one row tile
+  const int64_t units = (int64_t)B * (p.vrt ? p.vrt : 1) * ((max_seq_len > 0 ? max_seq_len : 1) + p.ovh);
   const int64_t by_work = (units + 255) / 256;  // at least 256 keys per workgroup
   if (nbund > by_work) nbund = by_work >= 8 ? by_work / 8 * 8 : by_work;
   if (nbund < 1) nbund = 1;
@@ -1813,9 +1850,10 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool fp8 = fal
   }
   const size_t slot = p.rows_tile != M16_ROWS ? (size_t)r128_slot_bytes(p.rows_tile)
                                                : (size_t)(p.rows_tile * D_V + 3 * p.rows_tile) * sizeof(float);
+  const size_t items = (size_t)B * (p.vrt ? p.vrt : p.n_rt);  // work items; groups of the combine
   p.prefix_off = 0;
-  p.partial_off = align_up((size_t)(B + 1) * sizeof(int64_t));
-  p.bytes = p.partial_off + align_up(((size_t)p.G + (size_t)B * p.n_rt) * slot);
+  p.partial_off = align_up((size_t)(B * (p.vrt ? p.vrt : 1) + 1) * sizeof(int64_t));
+  p.bytes = p.partial_off + align_up(((size_t)p.G + items) * slot);
   return p;
 }
 
@@ -1835,10 +1873,11 @@ extern "C" size_t mla_decode_workspace_size(int B, int q_len, int H, int max_seq
   if (B <= 0 || q_len < 1 || H < 1 || max_seq_len < 0) return 0;
   const int cus = device_cu_count();
   size_t m = 0;
-  for (const bool fp8 : {false, true}) {
-    const size_t x = make_plan(B, q_len, H, max_seq_len, cus, fp8).bytes;
-    m = x > m ? x : m;
-  }
+  for (const bool fp8 : {false, true})
+    for (const bool varlen : {false, true}) {
+      const size_t x = make_plan(B, q_len, H, max_seq_len, cus, fp8, varlen).bytes;
+      m = x > m ? x : m;
+    }
   return m;
 }
 
@@ -1860,7 +1899,7 @@ int decode(const void* q, const int32_t* query_start_loc, const void* kv_cache, 
   if (causal && cp_world > 1 && causal_seqlens_global == nullptr) return MLA_ERR_INVALID_ARG;
   if (B == 0) return MLA_OK;
   if (!q || !kv_cache || !block_table || !seq_lens || !out) return MLA_ERR_INVALID_ARG;
-  const Plan p = make_plan(B, q_len, H, max_seq_len, device_cu_count(), kv_fp8 != 0);
+  const Plan p = make_plan(B, q_len, H, max_seq_len, device_cu_count(), kv_fp8 != 0, query_start_loc != nullptr);
   if (workspace_bytes < p.bytes || workspace == nullptr) return MLA_ERR_INVALID_ARG;
 
   DecodeArgs a{};
@@ -1880,6 +1919,8 @@ int decode(const void* q, const int32_t* query_start_loc, const void* kv_cache, 
   a.kv_fp8 = kv_fp8;
   a.lse_base = lse_base;
   a.n_rt = p.n_rt;
+  a.vrt = p.vrt;
+  a.rows_tile = p.rows_tile;
   a.ovh = p.ovh;
   a.nbund = p.nbund;
   a.wa = p.wa;
@@ -1915,7 +1956,7 @@ int decode(const void* q, const int32_t* query_start_loc, const void* kv_cache, 
   const int threads = p.rows_tile == M16_ROWS ? M16_THREADS : R128_THREADS;
   if (launch(attn, dim3(p.G), dim3(threads), stream, a, tl_prof_start, tl_prof_stop) != hipSuccess)
     return MLA_ERR_HIP;
-  if (launch(comb, dim3(B * p.n_rt * 8), dim3(256), stream, a) != hipSuccess) return MLA_ERR_HIP;
+  if (launch(comb, dim3(B * (p.vrt ? p.vrt : p.n_rt) * 8), dim3(256), stream, a) != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }
 
