@@ -938,14 +938,13 @@ constexpr int R128_STAGE = RING_STAGE;        // 36 KiB
 constexpr int R128_NS = 3;                    // ring stages
 // The same kernel also runs tiles of 32 or 64 rows (requests of 17 to 64
 // rows: fewer heads, a few query tokens), with NRB = rows / 32 row blocks:
-// only waves 0 .. NRB-1 compute scores and softmax, every wave accumulates
-// its 128 value columns for the NRB row blocks.
+// the score MFMAs of a row block are split by dims over the 4/NRB waves that
+// share it, waves 0 .. NRB-1 add the slices and run the softmax, and every
+// wave accumulates its 128 value columns for the NRB row blocks.
 // Partial slot of a tile of `rows` rows: fp16 O, then m, l, lo per row and
 // a power-of-two factor per (value-column quarter, row), fp32.
 constexpr int r128_o_bytes(int rows) { return rows * D_V * 2; }
 constexpr int r128_slot_bytes(int rows) { return r128_o_bytes(rows) + 7 * rows * 4; }
-constexpr int R128_O_BYTES = r128_o_bytes(R128_ROWS);
-constexpr int R128_SLOT_BYTES = r128_slot_bytes(R128_ROWS);
 constexpr int R128_BT_WIN = 1024;             // block-table entries held in LDS per sub-piece
 // Q^T k-steps (of 16 dims) kept in registers; the rest in LDS.
 constexpr int R128_QREG = 28;

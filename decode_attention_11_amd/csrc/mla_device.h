@@ -63,10 +63,6 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
 typedef __attribute__((address_space(1))) const bf16x8 global_bf16x8;
 typedef __attribute__((address_space(1))) const int32_t global_i32;
 
-__device__ __forceinline__ bf16x8 load_bf16x8(const uint8_t* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
-}
-
 // 16-byte load through the global address space (global_load_dwordx4; a
 // generic pointer would become a flat load, which also counts against the
 // LDS wait counter).

@@ -56,7 +56,9 @@ const char* mla_status_string(int status);
 
 /*
  * Bytes of device workspace mla_decode needs for these sizes on the current
- * device (0 when none).  max_seq_len only sizes the work split; any upper
+ * device (0 when none): enough for every decode entry point (bf16 or FP8
+ * cache, and mla_decode_varlen with q_len the largest query length, whose
+ * work split can differ).  max_seq_len only sizes the work split; any upper
  * bound works.  Returns 0 for invalid sizes.
  */
 size_t mla_decode_workspace_size(int B, int q_len, int H, int max_seq_len);
@@ -225,9 +227,10 @@ int mla_decode_fp8(const void* q, const void* kv_cache, float kv_scale, const in
  * call's contents (nothing in it needs to start at zero): calls that overlap
  * on one GPU, on any streams, race and must be serialised by the caller.
  * Errors: those of mla_decode, and MLA_ERR_INVALID_ARG when the sizes need
- * more than MLA_NOALLOC_SCRATCH_BYTES (mla_decode_workspace_size(B, q_len,
- * H, max_seq_len) bytes; e.g. B = 16, q_len = 16, H = 128 and a 131072-key
- * bound need 69 MB); MLA_ERR_HIP if the array's address cannot be obtained.
+ * more than MLA_NOALLOC_SCRATCH_BYTES (at most mla_decode_workspace_size(B,
+ * q_len, H, max_seq_len) bytes; e.g. B = 16, q_len = 16, H = 128 and a
+ * 131072-key bound need 69 MB); MLA_ERR_HIP if the array's address cannot be
+ * obtained.
  */
 int mla_decode_noalloc(const void* q, const void* kv_cache, const int32_t* block_table,
                        const int32_t* seq_lens, const int32_t* causal_seqlens_global,
