@@ -21,6 +21,10 @@ CASES = [
     ("h16_noncausal_dcp2", 16, [16, 3, 0, 9], [100, 2500, 40, 800], 2, False, 1),
     ("h24_interleave2_dcp3", 24, [3, 1, 2, 3], [31, 400, 1111, 90], 3, True, 2),
     ("h16_rows64_tile", 16, [4, 1, 3, 0], [700, 30, 2500, 90], 1, True, 1),
+    # 70 requests of up to 4 row tiles: 280 (request, row tile) work items,
+    # more than one chunk of the in-kernel plan's scan
+    ("h128_280_items", 128, [1 + (3 * i) % 4 if i % 7 else 0 for i in range(70)],
+     [33 + (97 * i) % 600 for i in range(70)], 2, True, 1),
 ]
 
 
