@@ -1119,10 +1119,12 @@ struct R128State {
 };
 
 // One 32-key tile of bf16 rows in the ring's swizzled layout; the ring
-// loads of a later tile are issued one every four score MFMAs (issue(m),
-// m = 0..8), and side(step, steps) runs once before each of the wave's
-// `steps` score MFMAs (the FP8 instance widens the next tile there).
-template <int NRB, class Issue, class Side>
+// loads of a later tile are spread over the wave's score MFMAs (issue(m),
+// m = 0..8; with LATE, in the 32- and 64-row tiles, from the third one on),
+// and side(step, steps) runs once before each of the wave's `steps` score
+// MFMAs (the FP8 instance widens the next tile there; with LATE the bf16
+// instance resolves the later tile's row addresses in the first two).
+template <int NRB, bool LATE = false, class Issue, class Side>
 __device__ __forceinline__ void r128_compute(R128State<NRB>& st, const bf16x8 (&qf)[R128_QREG],
                                              const uint8_t* q_tail, const uint8_t* stage, uint8_t* p_lds,
                                              float* alpha_lds, float scale_log2, int ts, int k1, int nrow, int kfull,
@@ -1151,7 +1153,7 @@ __device__ __forceinline__ void r128_compute(R128State<NRB>& st, const bf16x8 (&
       constexpr int NL = RING_DMA_PER_WAVE;
 #pragma unroll
       for (int m = 0; m < NL; ++m)
-        if ((m * KS) / NL == j) issue(m);
+        if ((LATE ? (m * (KS - 2)) / NL + 2 : (m * KS) / NL) == j) issue(m);
       side(j, KS);
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % 4], qf[j], sc, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -1224,11 +1226,19 @@ __device__ __forceinline__ void r128_compute(R128State<NRB>& st, const bf16x8 (&
     side(kk, 36);
     const bf16x8 qv = kk < R128_QREG ? qf[kk < R128_QREG ? kk : 0] : qt[kk % 4];
     const bf16x8 kv = kf[kk % 4];
-    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qv, sc, 0, 0, 0);
+    // the score accumulator in VGPRs (the builtin puts it in AGPRs, where
+    // the allocator then moves a block of O out and back every tile)
+    if (kk == 0)
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(sc) : "v"(kv), "v"(qv));
+    else
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sc) : "v"(kv), "v"(qv));
     // keep each step's reads three steps ahead of their MFMA (the scheduler
     // would otherwise sink them next to their use)
     __builtin_amdgcn_sched_barrier(0);
   }
+  // the hazard checker does not see into the asm: wait states before VALU
+  // reads of the last MFMA's result (16 passes)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sc));
   // ---- online softmax of the wave's rows (keys past the piece or past a
   // row's bound masked; tiles below kfull, the wave's smallest bound, need
   // no mask)
@@ -1617,12 +1627,40 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
           // computed
           WAIT_VMCNT(R128_DMA_PER_WAVE);
           __syncthreads();
-          const RingRows nxt = r128_tile_rows(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb, ring_lds + nxt_off, wave,
-                                              lane);
-          r128_compute<NRB>(st, qf, q_tail, ring + cur, p_lds, alpha_lds, a.scale_log2, ka + it * R128_TILE, kb, nrow,
-                            min(kb, nmin), lane, wave,
-                            [&](int m) __attribute__((always_inline)) { ring_issue_one(nxt, m, wave, dma_sel_off); },
-                            lane_off, q_tail_lds, [](int, int) {});
+          if constexpr (NRB < 4) {
+            // tile it+2's row addresses: the block-table read is issued
+            // before the first score MFMA and used after it, so its latency
+            // and the address arithmetic run under the MFMAs; the tile's
+            // loads start at the third k-step.  (The 128-row tile, with four
+            // times the MFMAs per tile, gains nothing from this.)
+            RingRows nxt;
+            int nt_t = 0, nt_blk = -1;
+            r128_compute<NRB, true>(
+                st, qf, q_tail, ring + cur, p_lds, alpha_lds, a.scale_log2, ka + it * R128_TILE, kb, nrow,
+                min(kb, nmin), lane, wave,
+                [&](int m) __attribute__((always_inline)) { ring_issue_one(nxt, m, wave, dma_sel_off); }, lane_off,
+                q_tail_lds, [&](int step, int) __attribute__((always_inline)) {
+                  if (step == 0) {
+                    nt_t = ka + (it + 2) * R128_TILE + 8 * wave + (lane_id_fresh() & 7);
+                    if (nt_t < kb) nt_blk = bt_lds[block_of(a, nt_t) - e0];
+                  } else if (step == 1) {
+                    const uint8_t* rowp = reinterpret_cast<const uint8_t*>(kZeroRow);
+                    asm volatile("" : "+v"(rowp));
+                    if (nt_t < kb && (unsigned)nt_blk < (unsigned)a.num_blocks) {
+                      const int vb = block_of(a, nt_t);
+                      rowp = a.kv + ((int64_t)nt_blk * a.bs + (nt_t - vb * a.bs)) * ROW_BYTES;
+                    }
+                    nxt = ring_rows(rowp, ring_lds + nxt_off);
+                  }
+                });
+          } else {
+            const RingRows nxt = r128_tile_rows(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb, ring_lds + nxt_off,
+                                                wave, lane);
+            r128_compute<NRB>(st, qf, q_tail, ring + cur, p_lds, alpha_lds, a.scale_log2, ka + it * R128_TILE, kb,
+                              nrow, min(kb, nmin), lane, wave,
+                              [&](int m) __attribute__((always_inline)) { ring_issue_one(nxt, m, wave, dma_sel_off); },
+                              lane_off, q_tail_lds, [](int, int) {});
+          }
           nxt_off = cur;
           cur = __builtin_amdgcn_readfirstlane(cur == (R128_NS - 1) * STAGE ? 0u : cur + STAGE);
         }
