@@ -65,6 +65,7 @@ struct DecodeArgs {
   int vrt;                 // per-tile ranges: row tiles per request, else 0
   int rows_tile;           // rows per row tile
   int ovh;                 // work units charged per piece on top of its keys
+  int kalign;              // piece boundaries fall on multiples of this many keys (1 or 32)
   int nbund;               // balanced key ranges (bundles)
   int wa, wb;              // weights of the first and second half of the ranges
   int G;                   // partial workgroups: nbund * n_rt, one per (bundle, row tile)
@@ -178,16 +179,23 @@ struct PlanLds {
   int first_last[2][NT / 64];  // per wave: the first and last overlapping request (or sentinels)
 };
 
+// The key at which a range boundary x units past a request's overhead falls
+// (0 .. nb): rounded down to a multiple of kalign, so that with 32 every
+// 32-key tile of a piece lies in one block of a block size that 32 divides.
+// Both pieces beside a boundary round it the same way.
+__device__ __forceinline__ int piece_key(int64_t x, int nb, int kalign) {
+  return x <= 0 ? 0 : x >= nb ? nb : (int)x & -kalign;
+}
+
 // The piece of request bb (unit offset pb, nbb keys) inside [u0, u1): the
 // request's units are ovh overhead units, then one per key.
 template <class F>
 __device__ __forceinline__ void request_piece(const DecodeArgs& a, int bb, int64_t pb, int nbb, int sq, int tt,
                                               int64_t u0, int64_t u1, int rt, F&& piece) {
   if (nbb == 0) return;  // no keys: no units, no piece
-  const int64_t a0 = u0 - pb - a.ovh, a1 = u1 - pb - a.ovh;
-  const int k0 = __builtin_amdgcn_readfirstlane((int)(a0 > 0 ? a0 : 0));
-  const int k1 = __builtin_amdgcn_readfirstlane((int)(a1 < nbb ? a1 : nbb));
-  if (k1 <= k0) return;  // the range holds only the request's overhead units
+  const int k0 = __builtin_amdgcn_readfirstlane(piece_key(u0 - pb - a.ovh, nbb, a.kalign));
+  const int k1 = __builtin_amdgcn_readfirstlane(piece_key(u1 - pb - a.ovh, nbb, a.kalign));
+  if (k1 <= k0) return;  // the range holds only the request's overhead units (or under kalign keys)
   if (a.vrt) {
     // item bb is row tile bb % vrt of request bb / vrt
     const int b = bb / a.vrt;
@@ -302,8 +310,11 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int j, int r
 
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
   // 64 lanes x 16 bytes from per-lane global addresses to lds_base + 16*lane
+  // one wait state between the scalar write of M0 and the LDS-DMA load that
+  // reads it (the compiler's hazard checker does not look inside the asm)
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(base) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(base)
+               : "memory", "m0");
 }
 
 // A zero latent row: keys outside the piece (or with an invalid block id)
@@ -1620,6 +1631,10 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
         // stage offsets of tiles it and it+2, rotated instead of computed
         // from it % 3 (which costs every LDS address extra instructions)
         uint32_t cur = 0, nxt_off = 2 * STAGE;
+        // 128-row tile: the block-table entry of the tile loaded next, read
+        // one tile ahead (the same value in every lane)
+        int bt_ahead = -1;
+        if (NRB == 4 && a.kalign == 32 && ka + 2 * R128_TILE < kb) bt_ahead = bt_lds[block_of(a, ka + 2 * R128_TILE) - e0];
         for (int it = 0; it < nt; ++it) {
           // tile it landed (only tile it+1's 9 loads may still be in flight),
           // then every wave is also done with tile it-1 (its stage and the P
@@ -1654,8 +1669,25 @@ __global__ __launch_bounds__(R128_THREADS, 1) void attn_r128_kernel(DecodeArgs a
                   }
                 });
           } else {
-            const RingRows nxt = r128_tile_rows(a, bt_lds, e0, ka + (it + 2) * R128_TILE, kb, ring_lds + nxt_off,
-                                                wave, lane);
+            // tile it+2 on a 32-key boundary lies in one block when 32
+            // divides the block size: its 32 rows are contiguous, one
+            // block-table entry (read a tile ahead) gives all the wave's row
+            // addresses in scalar arithmetic.  Other tiles (a piece's last,
+            // or an invalid block id) resolve their rows lane by lane.
+            const int ts2 = ka + (it + 2) * R128_TILE;
+            const int blk2 = __builtin_amdgcn_readfirstlane(bt_ahead);
+            if (a.kalign == 32 && ts2 + R128_TILE < kb) bt_ahead = bt_lds[block_of(a, ts2 + R128_TILE) - e0];
+            RingRows nxt;
+            if (a.kalign == 32 && ts2 + R128_TILE <= kb && (ts2 & 31) == 0 && (unsigned)blk2 < (unsigned)a.num_blocks) {
+              const int vb = block_of(a, ts2);
+              const uint64_t r0 = reinterpret_cast<uint64_t>(a.kv) +
+                                  (uint64_t)((int64_t)blk2 * a.bs + (ts2 - vb * a.bs) + 8 * wave) * ROW_BYTES;
+#pragma unroll
+              for (int k = 0; k < 8; ++k) nxt.rows[k] = r0 + (uint64_t)k * ROW_BYTES;
+              nxt.stage_lds = ring_lds + nxt_off;
+            } else {
+              nxt = r128_tile_rows(a, bt_lds, e0, ts2, kb, ring_lds + nxt_off, wave, lane);
+            }
             r128_compute<NRB>(st, qf, q_tail, ring + cur, p_lds, alpha_lds, a.scale_log2, ka + it * R128_TILE, kb,
                               nrow, min(kb, nmin), lane, wave,
                               [&](int m) __attribute__((always_inline)) { ring_issue_one(nxt, m, wave, dma_sel_off); },
@@ -1748,7 +1780,11 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
       fac[t] = 1.f;
 #pragma unroll
       for (int c = 0; c < PER; ++c) v[t][c] = 0.f;
-      if (j <= j1 && (!some_empty || range_nonempty(j, T, a.nbund, a.wa, a.wb))) {
+      bool wrote = j <= j1 && (!some_empty || range_nonempty(j, T, a.nbund, a.wa, a.wb));
+      if (wrote && a.kalign > 1)  // the piece's keys as request_piece rounds them
+        wrote = piece_key(range_start(j + 1, T, a.nbund, a.wa, a.wb) - pb - a.ovh, nb, a.kalign) >
+                piece_key(range_start(j, T, a.nbund, a.wa, a.wb) - pb - a.ovh, nb, a.kalign);
+      if (wrote) {
         const uint8_t* slot = reinterpret_cast<const uint8_t*>(a.partials) + ((int64_t)j * a.n_rt + grp) * SLOT_BYTES;
         const float* pm = reinterpret_cast<const float*>(slot + O_BYTES);
         mw[t] = pm[row];
@@ -1804,6 +1840,7 @@ struct Plan {
   int n_rt;
   int vrt;
   int ovh;
+  int kalign;
   int nbund;
   int wa, wb;  // weights of the first and second half of the ranges
   int G;
@@ -1829,7 +1866,8 @@ int device_cu_count() {
 
 // Requests of up to 16 rows run the 16-row kernel, larger ones the 128-row
 // kernel (any block size: a power of two takes shifts, others a division).
-Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool fp8 = false, bool varlen = false) {
+Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool fp8 = false, bool varlen = false,
+               int block_size = 1) {
   Plan p{};
   const int64_t R = (int64_t)q_len * H;
   p.rows_tile = R <= M16_ROWS ? M16_ROWS : R <= 32 ? 32 : R <= 64 ? 64 : R128_ROWS;
@@ -1858,6 +1896,10 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int cus, bool fp8 = fal
   // on the DCP-8 shard and 5% on the 16-head spec-decode workload, and as
   // fast as 160 or 288 or faster)
   p.ovh = p.rows_tile == M16_ROWS ? (fp8 ? 144 : 160) : 224;
+  // the larger tiles' pieces start on 32-key boundaries when 32 divides the
+  // block size: each 32-key tile then lies in one block, and its rows are
+  // one contiguous 36 KiB span of the pool
+  p.kalign = p.rows_tile != M16_ROWS && block_size % 32 == 0 ? 32 : 1;
   // bundles: balanced key ranges, each processed by n_rt workgroups (one per
   // row tile).  The 128-row kernel keeps a bundle's workgroups on one XCD
   // (8 * k bundles, each XCD holding k whole bundles) so that they share the
@@ -1936,7 +1978,8 @@ int decode(const void* q, const int32_t* query_start_loc, const void* kv_cache, 
   if (causal && cp_world > 1 && causal_seqlens_global == nullptr) return MLA_ERR_INVALID_ARG;
   if (B == 0) return MLA_OK;
   if (!q || !kv_cache || !block_table || !seq_lens || !out) return MLA_ERR_INVALID_ARG;
-  const Plan p = make_plan(B, q_len, H, max_seq_len, device_cu_count(), kv_fp8 != 0, query_start_loc != nullptr);
+  const Plan p = make_plan(B, q_len, H, max_seq_len, device_cu_count(), kv_fp8 != 0, query_start_loc != nullptr,
+                           block_size);
   if (workspace_bytes < p.bytes || workspace == nullptr) return MLA_ERR_INVALID_ARG;
 
   DecodeArgs a{};
@@ -1959,6 +2002,7 @@ int decode(const void* q, const int32_t* query_start_loc, const void* kv_cache, 
   a.vrt = p.vrt;
   a.rows_tile = p.rows_tile;
   a.ovh = p.ovh;
+  a.kalign = p.kalign;
   a.nbund = p.nbund;
   a.wa = p.wa;
   a.wb = p.wb;

@@ -73,6 +73,11 @@ CASES = [
     # block sizes that are not powers of two: both kernel families divide
     # instead of shifting
     spec("bs48_h128_q4", 3, 128, 4, True, [47, 1000, 2401], global_is_null=True, bs=48),
+    # 128-row pieces start on 32-key boundaries when 32 divides the block
+    # size: ranges that hold under 32 keys of a request lose them to the next
+    # range, and the combine skips the emptied ones
+    spec("h128_q2_piece_bounds_bs64", 5, 128, 2, True, [31, 33, 95, 290, 1700], global_is_null=True),
+    spec("h128_q4_bs32_dcp2", 3, 128, 4, True, [40, 777, 2050], W=2, bs=32),
     spec("bs80_h128_q4_dcp2", 2, 128, 4, True, [161, 3000], W=2, bs=80),
     spec("bs48_h16_q1", 4, 16, 1, True, [1, 48, 49, 3000], global_is_null=True, bs=48),
     spec("bs80_h16_q1_dcp3", 3, 16, 1, True, [79, 800, 2500], W=3, bs=80),
