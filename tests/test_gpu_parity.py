@@ -357,3 +357,32 @@ def test_profiling_events_leave_results_unchanged(sp):
             hip.hipEventDestroy(e)
     assert torch.equal(o1, o2)
     assert torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("name,H,Q,bs,kv", [("h128_q4", 128, 4, 64, "bf16"), ("h16_q1", 16, 1, 64, "bf16"),
+                                            ("h16_q4", 16, 4, 32, "bf16"), ("h128_q4_bs48", 128, 4, 48, "bf16"),
+                                            ("h128_q4_fp8", 128, 4, 64, "fp8")])
+def test_unused_block_table_entries_are_never_read(name, H, Q, bs, kv):
+    """Block-table entries past a request's last block may hold anything (a
+    serving loop leaves them stale or -1): poisoning them with -1, huge ids
+    and ids past the pool changes no bit of the result."""
+    kw = dict(kv_dtype="fp8", kv_scale=1.0 / 64) if kv == "fp8" else {}
+    sp = spec(f"unused_bt_{name}", 4, H, Q, True, [40, 333, 1030, 2900], W=2, bs=bs, **kw)
+    wl = WL.build(sp)
+    up = Uploaded(wl)
+    for r in sorted(wl.pools):
+        say(f"{sp.name} rank {r}")
+        out0, lse0 = up.run(r)
+        bt = wl.block_table.copy()
+        nblocks = wl.pools[r].shape[0]
+        poison = np.array([-1, 2**31 - 1, nblocks, nblocks + 7], dtype=np.int32)
+        for b in range(sp.B):
+            used = -(-int(wl.seq_lens[r][b]) // bs)
+            if used < bt.shape[1]:
+                bt[b, used:] = poison[np.arange(bt.shape[1] - used) % poison.size]
+        saved = up.bt
+        up.bt = i32_dev(bt)
+        out1, lse1 = up.run(r)
+        up.bt = saved
+        torch.cuda.synchronize()
+        assert torch.equal(out0, out1) and torch.equal(lse0, lse1), f"{sp.name} rank {r}"
