@@ -1247,8 +1247,10 @@ __device__ __forceinline__ void r128_compute(R128State<NRB>& st, const bf16x8 (&
     // would otherwise sink them next to their use)
     __builtin_amdgcn_sched_barrier(0);
   }
-  // the hazard checker does not see into the asm: wait states before VALU
-  // reads of the last MFMA's result (16 passes)
+  // the compiler's hazard checker does not see into the asm: the wait states
+  // the ISA requires between an MFMA's write of VGPRs and VALU reads of
+  // them, with room to spare (24; chained MFMAs accumulating in place need
+  // none)
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sc));
   // ---- online softmax of the wave's rows (keys past the piece or past a
   // row's bound masked; tiles below kfull, the wave's smallest bound, need
