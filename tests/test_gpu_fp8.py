@@ -49,6 +49,7 @@ CASES = [
     # blocks under 32 keys in the 128- and 64-row tiles (a row lookup per lane)
     spec("fp8_bs1_h128_q4", 2, 128, 4, True, [17, 300], global_is_null=True, bs=1),
     spec("fp8_bs16_h32_q2_dcp2", 2, 32, 2, True, [40, 900], W=2, bs=16),
+    spec("fp8_rows160_h40_q4_partial_tile", 2, 40, 4, True, [50, 2500], global_is_null=True),
 ]
 
 

@@ -89,6 +89,11 @@ CASES = [
     spec("rows64_h16_q4_spec", 4, 16, 4, True, [3, 64, 1500, 5000], global_is_null=True),
     spec("rows48_h16_q3_dcp2_bs48", 2, 16, 3, True, [500, 3000], W=2, bs=48),
     spec("rows64_h16_q4_noncausal_dcp4_interleave2", 2, 16, 4, False, [100, 2100], W=4, interleave=2),
+    # more than 128 rows: a full 128-row tile and a partial one (its rows past
+    # the request's read the zero row and are never stored)
+    spec("rows160_h40_q4_partial_tile", 3, 40, 4, True, [50, 900, 2500], global_is_null=True),
+    spec("rows140_h20_q7_dcp2", 2, 20, 7, True, [300, 2049], W=2),
+    spec("rows200_h25_q8_noncausal_bs128", 2, 25, 8, False, [129, 1700], bs=128, global_is_null=True),
 ]
 
 
