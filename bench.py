@@ -262,8 +262,10 @@ def cpu_baseline_child(n, args, budget_s):
 # ------------------------------------------------------------------ achievable peaks
 def measured_peaks(torch, hip, stream, dev, reps=5):
     """Achievable HBM and bf16 matrix rates on this GPU, measured with torch
-    (not this library): a 1 GiB device copy (bytes read + written) and an
-    8192^3 bf16 GEMM (hipBLASLt).  Reported beside the published peaks."""
+    (not this library): a 1 GiB device copy (bytes read + written), row sums
+    over 1 GiB (bytes read: the memory-bound kernels' bytes are nearly all
+    reads) and an 8192^3 bf16 GEMM (hipBLASLt).  Reported beside the published
+    peaks."""
     out = {}
     x = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     y = torch.empty_like(x)
@@ -275,7 +277,18 @@ def measured_peaks(torch, hip, stream, dev, reps=5):
         y.copy_(x)
     hip.record(b_, stream)
     out["hbm_copy_GBps"] = round((2 << 30) * reps / (hip.elapsed_ms(a_, b_) * 1e-3) / 1e9, 1)
-    del x, y
+    # row sums of 4 KiB rows: 1 GiB read, 1 MiB written (a full reduction
+    # reads far slower in torch)
+    rows = x.view(-1, 1024)
+    acc = torch.empty(rows.shape[0], dtype=torch.float32, device=dev)
+    torch.sum(rows, 1, out=acc)
+    torch.cuda.synchronize()
+    hip.record(a_, stream)
+    for _ in range(reps):
+        torch.sum(rows, 1, out=acc)
+    hip.record(b_, stream)
+    out["hbm_read_GBps"] = round(((1 << 30) + acc.numel() * 4) * reps / (hip.elapsed_ms(a_, b_) * 1e-3) / 1e9, 1)
+    del x, y, rows, acc
     n = 8192
     g = torch.Generator(device=dev).manual_seed(0)
     m1 = torch.randn((n, n), dtype=torch.bfloat16, device=dev, generator=g).contiguous()
@@ -688,10 +701,10 @@ def main():
         wls[n] = None
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
-    log("achievable peaks: 1 GiB copy, 8192^3 bf16 GEMM (torch)")
+    log("achievable peaks: 1 GiB copy, 1 GiB of row sums, 8192^3 bf16 GEMM (torch)")
     peaks = measured_peaks(torch, hip, stream, dev)
     for n, res in results.items():
-        meas = peaks["hbm_copy_GBps"] if n in MEM_BOUND else peaks["bf16_gemm_TFLOPs"]
+        meas = peaks["hbm_read_GBps"] if n in MEM_BOUND else peaks["bf16_gemm_TFLOPs"]
         res["roofline"]["frac_of_measured_peak"] = round(res["roofline"]["achieved"] / meas, 4) if meas > 0 else None
 
     h = results[headline]
