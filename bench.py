@@ -27,7 +27,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import glob
 import hashlib
 import json
 import math
@@ -125,9 +124,11 @@ def rank_work(wl, r):
 
 
 def source_hash():
+    """Hash of the sources the attention kernels are built from (traffic
+    figures taken on other sources are not reported)."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "decode_attention_11_amd", "csrc", "*"))):
-        h.update(open(p, "rb").read())
+    for name in ("mla_decode.hip", "mla_device.h"):
+        h.update(open(os.path.join(ROOT, "decode_attention_11_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -260,12 +261,13 @@ def cpu_baseline_child(n, args, budget_s):
 
 
 # ------------------------------------------------------------------ achievable peaks
-def measured_peaks(torch, hip, stream, dev, reps=5):
+def measured_peaks(torch, mla, hip, stream, dev, reps=5):
     """Achievable HBM and bf16 matrix rates on this GPU, measured with torch
     (not this library): a 1 GiB device copy (bytes read + written), row sums
     over 1 GiB (bytes read: the memory-bound kernels' bytes are nearly all
-    reads) and an 8192^3 bf16 GEMM (hipBLASLt).  Reported beside the published
-    peaks."""
+    reads) and an 8192^3 bf16 GEMM (hipBLASLt); and the library's bare bf16
+    MFMA loop (mla_probe_mfma: 1024 workgroups, 2000 steps of four
+    32x32x16 MFMAs per wave).  Reported beside the published peaks."""
     out = {}
     x = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     y = torch.empty_like(x)
@@ -301,6 +303,15 @@ def measured_peaks(torch, hip, stream, dev, reps=5):
     hip.record(b_, stream)
     out["bf16_gemm_TFLOPs"] = round(2.0 * n ** 3 * reps / (hip.elapsed_ms(a_, b_) * 1e-3) / 1e12, 1)
     del m1, m2
+    wg, iters = 1024, 2000
+    probe = mla.probe_mfma(wg, iters)
+    torch.cuda.synchronize()
+    hip.record(a_, stream)
+    for _ in range(reps):
+        mla.probe_mfma(wg, iters, out=probe)
+    hip.record(b_, stream)
+    out["mfma_loop_TFLOPs"] = round(wg * 4 * iters * 4 * 32768.0 * reps / (hip.elapsed_ms(a_, b_) * 1e-3) / 1e12, 1)
+    del probe
     hip.destroy(a_)
     hip.destroy(b_)
     torch.cuda.synchronize()
@@ -701,10 +712,10 @@ def main():
         wls[n] = None
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
-    log("achievable peaks: 1 GiB copy, 1 GiB of row sums, 8192^3 bf16 GEMM (torch)")
-    peaks = measured_peaks(torch, hip, stream, dev)
+    log("achievable peaks: 1 GiB copy, 1 GiB of row sums, 8192^3 bf16 GEMM (torch), bare MFMA loop")
+    peaks = measured_peaks(torch, mla, hip, stream, dev)
     for n, res in results.items():
-        meas = peaks["hbm_read_GBps"] if n in MEM_BOUND else peaks["bf16_gemm_TFLOPs"]
+        meas = peaks["hbm_read_GBps"] if n in MEM_BOUND else peaks["mfma_loop_TFLOPs"]
         res["roofline"]["frac_of_measured_peak"] = round(res["roofline"]["achieved"] / meas, 4) if meas > 0 else None
 
     h = results[headline]

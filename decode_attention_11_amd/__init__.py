@@ -24,7 +24,7 @@ __all__ = [
     "D_QK", "D_V", "PAD_SLOT_ID", "LSE_BASE_E", "LSE_BASE_2", "MLAError",
     "library_path", "load_library", "exported_symbols",
     "mla_decode", "mla_decode_varlen", "mla_decode_workspace_size", "mla_merge_lse", "cp_local_slot", "kv_write",
-    "profile_attention_events", "mla_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "profile_attention_events", "mla_decode_noalloc", "NOALLOC_SCRATCH_BYTES", "probe_mfma",
 ]
 
 D_QK = 576
@@ -49,6 +49,7 @@ _SIGNATURES = [
     ("mla_merge_lse", _I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
     ("cp_local_slot", _I, [_P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, _P]),
     ("mla_profile_attention_events", _I, [_P, _P]),
+    ("mla_probe_mfma", _I, [_I, _I, _P, _P]),
     ("mla_kv_write", _I, [_P, _P, ctypes.c_int64, _P, _I, _I, _P]),
     ("mla_decode_interleaved", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                                     ctypes.c_float, _I, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -130,6 +131,21 @@ def profile_attention_events(start: Optional[int], stop: Optional[int]) -> None:
     """Record raw hipEvent_t handles around the attention kernel of following
     mla_decode calls of this thread (None, None to stop)."""
     _check(load_library().mla_profile_attention_events(start, stop))
+
+
+def probe_mfma(workgroups: int, iters: int, out: Optional[torch.Tensor] = None,
+               device: Optional[torch.device] = None) -> torch.Tensor:
+    """Enqueue the library's bare bf16 MFMA loop (a measurement helper, not
+    part of the decode path) on the current stream: workgroups * 4 waves *
+    iters * 4 * 32768 flop.  Returns out (float32 [workgroups * 256]), which
+    holds 64 * iters in every element once the launch has run."""
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    if out is None:
+        out = torch.empty((workgroups * 256,), dtype=torch.float32, device=dev)
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.numel() < workgroups * 256:
+        raise ValueError("out must be a contiguous float32 tensor of workgroups * 256 values")
+    _check(load_library().mla_probe_mfma(int(workgroups), int(iters), out.data_ptr(), _stream(out.device)))
+    return out
 
 
 def mla_decode_workspace_size(B: int, q_len: int, H: int, max_seq_len: int) -> int:

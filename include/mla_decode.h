@@ -251,6 +251,18 @@ int mla_decode_noalloc(const void* q, const void* kv_cache, const int32_t* block
 int mla_profile_attention_events(hipEvent_t start, hipEvent_t stop);
 
 /*
+ * A measurement helper, not part of the decode path: runs a bare bf16 MFMA
+ * loop (v_mfma_f32_32x32x16_bf16, four independent accumulation chains per
+ * wave, iters steps of four MFMAs) on `workgroups` workgroups of 256 threads,
+ * the achievable matrix rate beside the published peak.  Work per launch:
+ * workgroups * 4 waves * iters * 4 * 32768 flop.  out (device, float32,
+ * workgroups * 256 values, caller-owned) receives 64 * iters in every
+ * element.  Returns MLA_ERR_INVALID_ARG for workgroups or iters outside
+ * [1, 2^20] or a NULL out.
+ */
+int mla_probe_mfma(int workgroups, int iters, float* out, hipStream_t stream);
+
+/*
  * Merge partial attention results of disjoint key sets (the ranks' shards)
  * by their LSE (PR #54012 page, implementation breakdown: the CP path returns
  * a natural-log LSE and the bases must agree before the cross-rank merge;

@@ -23,7 +23,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["mla_status_string", "mla_decode_workspace_size", "mla_decode",
                                            "mla_merge_lse", "cp_local_slot", "mla_profile_attention_events",
                                            "mla_kv_write", "mla_decode_interleaved", "mla_decode_varlen",
-                                           "mla_decode_fp8", "mla_kv_write_fp8", "mla_decode_noalloc"])
+                                           "mla_decode_fp8", "mla_kv_write_fp8", "mla_decode_noalloc",
+                                           "mla_probe_mfma"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -227,3 +228,10 @@ def test_noalloc_array_size_is_the_documented_one():
     assert mla.NOALLOC_SCRATCH_BYTES == 96 * 1024 * 1024
     # the largest benchmark workload (B 16, q_len 16, H 128, 131072-key bound) fits
     assert mla.mla_decode_workspace_size(16, 16, 128, 131072) <= mla.NOALLOC_SCRATCH_BYTES
+
+
+def test_probe_refuses_bad_sizes_without_launching():
+    lib = mla.load_library()
+    assert lib.mla_probe_mfma(0, 10, None, None) == 1
+    assert lib.mla_probe_mfma(4, 0, None, None) == 1
+    assert lib.mla_probe_mfma(4, 10, None, None) == 1  # NULL out
